@@ -1,0 +1,246 @@
+"""CPU oracle for the wide-beam SID decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the GPU
+library (``wide_beam_sid_amd``) and never imports it; both read the same
+seeded inputs from ``synth``.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, compiled with gcc into
+``_oracle.so``); this module only marshals numpy arrays and walks the decode
+loop of GRACE Section 3.1 step by step (``decode.py``).
+
+Parity status per function (pins live in tests/test_oracle_*.py):
+  bloom_positions   pinned: SplitMix64 published test vector, eq 8 property
+  mask_row          pinned: toy example of eqs 6-7, brute force on tiny
+                    catalogs (catalog validity, no false negatives)
+  log_softmax       pinned: closed forms (uniform logits, normalisation)
+  topk              pinned: brute-force rank counting, two-level lemma
+  cross_attn        pinned: torch SDPA fp64 (Appendix B per-row broadcast),
+                    T_ctx = 1, q = 0, identical keys
+  self_attn         pinned: T_self = 1, coalesced block-diagonal tile of
+                    Section 5.2, torch SDPA fp64 per row
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, u64 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
+        L.orc_splitmix64_first.restype = u64
+        L.orc_splitmix64_first.argtypes = [u64]
+        L.orc_bloom_positions.argtypes = [i64, i32, i32, P]
+        L.orc_bloom_row.argtypes = [i64, i32, i32, P]
+        L.orc_bloom_contains.argtypes = [P, P, i32]
+        L.orc_bloom_contains.restype = i32
+        L.orc_bitmask_match.argtypes = [P, P, i32]
+        L.orc_bitmask_match.restype = i32
+        L.orc_index_create.restype = P
+        L.orc_index_create.argtypes = [i32, i32, i64, P, i32, i32, i32]
+        L.orc_index_add_ads.argtypes = [P, i64, P, P, P, P]
+        L.orc_index_finish.argtypes = [P]
+        L.orc_index_destroy.argtypes = [P]
+        L.orc_index_count.restype = i64
+        L.orc_index_count.argtypes = [P, i32]
+        L.orc_index_find.restype = i64
+        L.orc_index_find.argtypes = [P, P, i32]
+        L.orc_index_rows.argtypes = [P, i32, P, P, P]
+        L.orc_mask_row.restype = i32
+        L.orc_mask_row.argtypes = [P, P, i32, P, P, i32, P]
+        L.orc_log_softmax.argtypes = [P, i32, P]
+        L.orc_topk.restype = i64
+        L.orc_topk.argtypes = [P, i64, i64, P, P]
+        L.orc_cross_attn.argtypes = [P, P, P, i32, i32, i32, i32, i32, P]
+        L.orc_self_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# O1: Bloom hashing
+# ---------------------------------------------------------------------------
+
+def splitmix64_first(state: int) -> int:
+    return int(lib().orc_splitmix64_first(ctypes.c_uint64(state & (2**64 - 1))))
+
+
+def bloom_positions(geo_id: int, w_bits: int, k: int) -> np.ndarray:
+    out = np.zeros(k, dtype=np.uint32)
+    lib().orc_bloom_positions(int(geo_id), w_bits, k, _p(out))
+    return out
+
+
+def bloom_row(geo_id: int, w_bits: int, k: int) -> np.ndarray:
+    out = np.zeros(w_bits // 64, dtype=np.uint64)
+    lib().orc_bloom_row(int(geo_id), w_bits, k, _p(out))
+    return out
+
+
+def bloom_contains(B: np.ndarray, bloom_l: np.ndarray) -> bool:
+    B = _c(B, np.uint64)
+    bl = _c(bloom_l, np.uint64)
+    return bool(lib().orc_bloom_contains(_p(B), _p(bl), B.size))
+
+
+def bitmask_match(node_bm: np.ndarray, user_bm: np.ndarray) -> bool:
+    a = _c(node_bm, np.uint64)
+    u = _c(user_bm, np.uint64)
+    return bool(lib().orc_bitmask_match(_p(a), _p(u), a.size))
+
+
+# ---------------------------------------------------------------------------
+# O2-O5: prefix tables and masks
+# ---------------------------------------------------------------------------
+
+class Index:
+    """Per-level prefix tables with OR-union matchers (eqs 4, 9)."""
+
+    def __init__(self, L: int, V: int, sids: np.ndarray, w_bm: int,
+                 bloom_bits: int, bloom_k: int):
+        self.L, self.V, self.w_bm = L, V, w_bm
+        self.bloom_bits, self.bloom_k = bloom_bits, bloom_k
+        self.w_bl = bloom_bits // 64
+        s = _c(sids, np.int32)
+        self._keep = s
+        self.h = lib().orc_index_create(L, V, s.shape[0], _p(s), w_bm, bloom_bits, bloom_k)
+        if not self.h:
+            raise ValueError("bad index parameters")
+
+    def add_ads(self, ad_sid, rules, geo_off, geo_ids):
+        a = _c(ad_sid, np.int64)
+        r = _c(rules, np.uint64)
+        go = _c(geo_off, np.int64)
+        gi = _c(geo_ids, np.int32) if len(geo_ids) else np.zeros(1, np.int32)
+        lib().orc_index_add_ads(self.h, a.size, _p(a), _p(r), _p(go), _p(gi))
+
+    def finish(self):
+        lib().orc_index_finish(self.h)
+        return self
+
+    def count(self, level: int) -> int:
+        return int(lib().orc_index_count(self.h, level))
+
+    def find(self, prefix) -> int:
+        p = _c(prefix, np.int32)
+        if p.size == 0:
+            p = np.zeros(1, np.int32)
+            return int(lib().orc_index_find(self.h, _p(p), 0))
+        return int(lib().orc_index_find(self.h, _p(p), len(prefix)))
+
+    def rows(self, level: int):
+        n = self.count(level)
+        pfx = np.zeros((n, level), np.int32)
+        bm = np.zeros((n, max(self.w_bm, 1)), np.uint64)
+        bl = np.zeros((n, max(self.w_bl, 1)), np.uint64)
+        lib().orc_index_rows(self.h, level, _p(pfx), _p(bm), _p(bl))
+        return pfx, bm[:, : self.w_bm], bl[:, : self.w_bl]
+
+    def mask_row(self, prefix, t: int, user_bm, user_locs) -> np.ndarray:
+        """Mask words of one row; t < 0 marks a dead row."""
+        words = (self.V + 63) // 64
+        out = np.zeros(words, dtype=np.uint64)
+        p = _c(prefix if t > 0 else [0], np.int32)
+        ub = _c(user_bm, np.uint64)
+        ul = _c(user_locs if len(user_locs) else [0], np.int32)
+        lib().orc_mask_row(self.h, _p(p), t, _p(ub), _p(ul), len(user_locs), _p(out))
+        return out
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().orc_index_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+
+def build_index(w, sids, ads) -> Index:
+    ix = Index(w.L, w.V, sids, w.w_bm, w.bloom_bits, w.bloom_k)
+    ix.add_ads(ads.ad_sid, ads.rules, ads.geo_offsets, ads.geo_ids)
+    return ix.finish()
+
+
+def mask_bits_to_bool(words: np.ndarray, V: int) -> np.ndarray:
+    w = np.asarray(words, dtype=np.uint64)
+    bits = (w[..., :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
+    return bits.reshape(*w.shape[:-1], -1)[..., :V].astype(bool)
+
+
+# ---------------------------------------------------------------------------
+# O6, O8, O10
+# ---------------------------------------------------------------------------
+
+def log_softmax(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    lib().orc_log_softmax(_p(x), x.size, _p(out))
+    return out
+
+
+def topk(scores: np.ndarray, k: int):
+    """Top-k over flat candidates: (score desc, index asc), -inf excluded."""
+    s = _c(scores, np.float32)
+    f = np.zeros(max(k, 1), np.uint32)
+    v = np.zeros(max(k, 1), np.float32)
+    n = lib().orc_topk(_p(s), s.size, k, _p(f), _p(v))
+    return f[:n].copy(), v[:n].copy()
+
+
+def cross_attn(q, K, Vv, B: int, M: int) -> np.ndarray:
+    q = _c(q, np.float64)
+    K = _c(K, np.float64)
+    Vv = _c(Vv, np.float64)
+    R, H, d = q.shape
+    T = K.shape[2]
+    assert R == B * M and K.shape == (B, H, T, d) and Vv.shape == K.shape
+    out = np.empty_like(q)
+    lib().orc_cross_attn(_p(q), _p(K), _p(Vv), B, M, H, T, d, _p(out))
+    return out
+
+
+def self_attn(q, hk, hv, valid) -> np.ndarray:
+    q = _c(q, np.float64)
+    hk = _c(hk, np.float64)
+    hv = _c(hv, np.float64)
+    va = _c(valid, np.uint8)
+    R, H, d = q.shape
+    T = hk.shape[1]
+    assert hk.shape == (R, T, H, d) and va.shape == (R, T) and T <= 64
+    out = np.empty_like(q)
+    lib().orc_self_attn(_p(q), _p(hk), _p(hv), _p(va), R, T, H, d, _p(out))
+    return out

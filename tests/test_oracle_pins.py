@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks an oracle function against a published value, a closed form,
+a special case that a library routine computes, or brute force on tiny inputs
+written in a different formulation from the oracle's.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.decode import initial_state, step
+from synth import workload as W
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# O1: Bloom hashing
+# --------------------------------------------------------------------------
+
+def test_splitmix64_published_vectors(golden_dir):
+    g = _load(golden_dir, "splitmix64.json")
+    gamma = 0x9E3779B97F4A7C15
+    for seed, outs in g["sequences"].items():
+        for n, expect in enumerate(outs, start=1):
+            state = (int(seed) + (n - 1) * gamma) % 2**64
+            assert oracle.splitmix64_first(state) == int(expect, 0)
+
+
+def test_bloom_positions_hand_derived(golden_dir):
+    g = _load(golden_dir, "bloom_positions.json")
+    for c in g["cases"]:
+        got = oracle.bloom_positions(c["id"], c["w"], c["k"])
+        assert got.tolist() == c["positions"]
+
+
+def test_bloom_row_matches_positions_and_eq8():
+    """bloom(l) has exactly the probe bits; eq 8 containment equals 'every
+    probe bit of l is set in B' for random rows (dense and sparse)."""
+    r = np.random.default_rng(7)
+    for w_bits, k in [(256, 3), (4096, 4), (8192, 5)]:
+        for gid in r.integers(0, 10**6, size=40):
+            pos = oracle.bloom_positions(int(gid), w_bits, k)
+            row = oracle.bloom_row(int(gid), w_bits, k)
+            bits = {int(p) for p in pos}
+            got = {i for i in range(w_bits) if (int(row[i // 64]) >> (i % 64)) & 1}
+            assert got == bits
+            for density in (0.02, 0.5, 0.97):
+                B = np.zeros(w_bits // 64, np.uint64)
+                on = r.random(w_bits) < density
+                if r.random() < 0.3:
+                    on[list(bits)] = True
+                for i in np.nonzero(on)[0]:
+                    B[i // 64] |= np.uint64(1) << np.uint64(i % 64)
+                expect = all(on[p] for p in bits)
+                assert oracle.bloom_contains(B, row) == expect
+
+
+# --------------------------------------------------------------------------
+# O2-O5: toy example and brute force
+# --------------------------------------------------------------------------
+
+def _bits(s):
+    v = 0
+    for i, ch in enumerate(s):
+        if ch == "1":
+            v |= 1 << i
+    return np.array([v], np.uint64)
+
+
+def test_toy_bitmask_example_eqs_6_7(golden_dir):
+    g = _load(golden_dir, "toy_bitmask.json")
+    node, user = _bits(g["node_union"]), _bits(g["user"])
+    a, b = (_bits(s) for s in g["ads"].values())
+    assert (a | b)[0] == node[0]
+    assert oracle.bitmask_match(node, user) == g["expect"]["node_passes_eq5"]
+    assert oracle.bitmask_match(a, user) == g["expect"]["ad_A_passes_alone"]
+    assert oracle.bitmask_match(b, user) == g["expect"]["ad_B_passes_alone"]
+    # The same example through the index: one SID (1, 0) carrying ads A and B.
+    ix = oracle.Index(2, 4, np.array([[1, 0]], np.int32), 1, 0, 0)
+    ix.add_ads(np.array([0, 0]), np.stack([a, b]), np.zeros(3, np.int64), [])
+    ix.finish()
+    m = ix.mask_row([], 0, user, [])
+    assert int(m[0]) == 0b0010           # token 1 kept at the root (false positive)
+    m = ix.mask_row([1], 1, user, [])
+    assert int(m[0]) == 0b0001           # leaf (1, 0) kept as well
+    m = ix.mask_row([1], 1, _bits("00110"), [])   # UK user: neither ad allows UK
+    assert int(m[0]) == 0
+
+
+def _tiny_variants():
+    base = W.WORKLOADS["tiny_fp32"]
+    return [
+        ("tiny", base, 0),
+        ("tiny_s5", base, 5),
+        ("deep", base.scaled(L=4, V=6, n_sids=300, ads_per_sid=(1, 4),
+                             geo_pool=40, geo_per_ad=(1, 3), n_loc=3), 1),
+        ("sparse", base.scaled(bm_p=0.2, bloom_bits=128, bloom_k=2,
+                               geo_pool=500, geo_per_ad=(1, 2), n_loc=4), 2),
+        ("nobloom", base.scaled(bloom_bits=0, bloom_k=0, geo_pool=0,
+                                geo_per_ad=(0, 0), n_loc=0, B=3), 3),
+    ]
+
+
+@pytest.mark.parametrize("name,w,seed", _tiny_variants(), ids=[v[0] for v in _tiny_variants()])
+def test_mask_brute_force(name, w, seed):
+    """Mask of every catalog prefix (and a few non-catalog ones), checked by
+    exhaustive enumeration in a different formulation:
+      * catalog validity: kept tokens extend catalog prefixes (eq 1);
+      * no false negatives: a prefix holding an exactly eligible ad is kept;
+      * exactness of the OR-union tests: kept iff every user bit is allowed by
+        SOME ad under the prefix, and SOME user location has every probe bit
+        set by SOME geo id of SOME ad under the prefix.
+    """
+    sids = W.make_catalog(w, seed)
+    counts = W.ad_counts(w, seed)
+    ads = W.make_ads(w, seed, counts)
+    req = W.make_requests(w, seed)
+    ix = oracle.build_index(w, sids, ads)
+
+    ads_of_sid = [[] for _ in range(w.n_sids)]
+    for a, s in enumerate(ads.ad_sid):
+        ads_of_sid[s].append(a)
+    geo = [set(ads.geo_ids[ads.geo_offsets[a]:ads.geo_offsets[a + 1]].tolist())
+           for a in range(len(ads.ad_sid))]
+    rule = [int(ads.rules[a, 0]) for a in range(len(ads.ad_sid))]
+    probes = {}
+
+    def prb(g):
+        if g not in probes:
+            probes[g] = set(oracle.bloom_positions(g, w.bloom_bits, w.bloom_k).tolist())
+        return probes[g]
+
+    prefixes = {()}
+    for s in sids:
+        for l in range(1, w.L):
+            prefixes.add(tuple(s[:l].tolist()))
+    rr = np.random.default_rng(seed)
+    for _ in range(10):
+        l = int(rr.integers(1, w.L))
+        prefixes.add(tuple(rr.integers(0, w.V, size=l).tolist()))
+
+    n_fp = n_true = 0
+    for b in range(w.B):
+        ub = int(req.user_bm[b, 0])
+        user_bits = [i for i in range(64) if (ub >> i) & 1]
+        locs = req.locs[b].tolist()
+        for p in prefixes:
+            t = len(p)
+            m = oracle.mask_bits_to_bool(ix.mask_row(list(p), t, req.user_bm[b], req.locs[b]), w.V)
+            for v in range(w.V):
+                under = [i for i in range(w.n_sids) if tuple(sids[i, :t + 1].tolist()) == p + (v,)]
+                ad_list = [a for i in under for a in ads_of_sid[i]]
+                cd = len(under) > 0
+                exact = any(((rule[a] & ub) == ub) and (not w.bloom_bits or bool(set(locs) & geo[a]))
+                            for a in ad_list)
+                bm_union = all(any((rule[a] >> bit) & 1 for a in ad_list) for bit in user_bits)
+                if w.bloom_bits:
+                    cover = set()
+                    for a in ad_list:
+                        for g in geo[a]:
+                            cover |= prb(g)
+                    bl_union = any(prb(l) <= cover for l in locs)
+                else:
+                    bl_union = True
+                expect = cd and bm_union and bl_union
+                assert m[v] == expect, (b, p, v)
+                if m[v]:
+                    assert cd
+                if exact:
+                    assert m[v], "false negative"
+                    n_true += 1
+                elif m[v]:
+                    n_fp += 1
+    assert n_true > 0
+
+
+def test_dead_row_masks_everything():
+    w = W.WORKLOADS["tiny_fp32"]
+    sids = W.make_catalog(w, 0)
+    ads = W.make_ads(w, 0, W.ad_counts(w, 0))
+    req = W.make_requests(w, 0)
+    ix = oracle.build_index(w, sids, ads)
+    assert not oracle.mask_bits_to_bool(ix.mask_row([], -1, req.user_bm[0], req.locs[0]), w.V).any()
+
+
+# --------------------------------------------------------------------------
+# O6: log-softmax closed forms
+# --------------------------------------------------------------------------
+
+def test_log_softmax_closed_forms():
+    for V in (1, 2, 16, 256, 1024):
+        lp = oracle.log_softmax(np.full(V, 3.25))
+        assert np.allclose(lp, -math.log(V), atol=1e-15, rtol=0)
+    a, b = 0.7, -1.9
+    lp = oracle.log_softmax(np.array([a, b]))
+    assert abs(lp[0] + math.log1p(math.exp(b - a))) < 1e-15
+    assert abs(lp[1] + math.log1p(math.exp(a - b))) < 1e-15
+    r = np.random.default_rng(1)
+    for V in (16, 256, 1024):
+        x = r.standard_normal(V) * 3
+        lp = oracle.log_softmax(x)
+        assert abs(np.exp(lp).sum() - 1) < 1e-12
+        assert np.allclose(oracle.log_softmax(x + 11.5), lp, atol=1e-12, rtol=0)
+        assert (lp <= 0).all()
+        assert np.argmax(lp) == np.argmax(x)
+
+
+# --------------------------------------------------------------------------
+# O8: top-k
+# --------------------------------------------------------------------------
+
+def test_topk_brute_force_rank_counting():
+    r = np.random.default_rng(3)
+    for trial in range(60):
+        n = int(r.integers(1, 300))
+        s = r.integers(-6, 2, size=n).astype(np.float32) / 2      # many ties
+        s[r.random(n) < 0.3] = -np.inf
+        k = int(r.integers(1, 40))
+        f, v = oracle.topk(s, k)
+        rank = {}
+        for i in range(n):
+            if not np.isfinite(s[i]):
+                continue
+            rank[i] = sum(1 for j in range(n) if np.isfinite(s[j]) and
+                          (s[j] > s[i] or (s[j] == s[i] and j < i)))
+        expect = sorted([i for i in rank if rank[i] < k], key=lambda i: rank[i])
+        assert f.tolist() == expect
+        assert np.array_equal(v, s[expect])
+
+
+def test_topk_two_level_lemma():
+    """Per-row top-k followed by a merge selects the same set (a token ranked
+    below k inside its own row cannot make the global top-k)."""
+    r = np.random.default_rng(4)
+    for _ in range(20):
+        M, V, k = int(r.integers(1, 12)), int(r.integers(2, 40)), int(r.integers(1, 50))
+        s = (r.integers(-20, 0, size=(M, V)) / 4).astype(np.float32)
+        s[r.random((M, V)) < 0.2] = -np.inf
+        full_f, _ = oracle.topk(s.reshape(-1), k)
+        local = np.full((M, V), -np.inf, np.float32)
+        for m in range(M):
+            f, _ = oracle.topk(s[m], k)
+            local[m, f] = s[m, f]
+        two_f, _ = oracle.topk(local.reshape(-1), k)
+        assert full_f.tolist() == two_f.tolist()
+
+
+# --------------------------------------------------------------------------
+# O10: attention
+# --------------------------------------------------------------------------
+
+def _sdpa64(q, k, v):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+
+
+def test_cross_attn_vs_broadcast_sdpa_appendix_b():
+    """Beam-as-query (eqs 11-14) equals the per-row SDPA over K/V broadcast
+    to every beam row (the eq 10 layout), here computed by torch in fp64."""
+    r = np.random.default_rng(5)
+    B, M, H, T, d = 3, 5, 2, 7, 8
+    q = r.standard_normal((B * M, H, d))
+    K = r.standard_normal((B, H, T, d))
+    Vv = r.standard_normal((B, H, T, d))
+    out = oracle.cross_attn(q, K, Vv, B, M)
+    Kb = np.repeat(K, M, axis=0)              # [BM, H, T, d]
+    Vb = np.repeat(Vv, M, axis=0)
+    ref = _sdpa64(q[:, :, None, :], Kb, Vb)[:, :, 0, :]
+    assert np.abs(out - ref).max() < 1e-12
+    # and equals one SDPA per request with the beams as the query sequence
+    qv = q.reshape(B, M, H, d).transpose(0, 2, 1, 3)
+    ref2 = _sdpa64(np.ascontiguousarray(qv), K, Vv).transpose(0, 2, 1, 3).reshape(B * M, H, d)
+    assert np.abs(out - ref2).max() < 1e-12
+
+
+def test_cross_attn_special_cases():
+    r = np.random.default_rng(6)
+    B, M, H, d = 2, 3, 2, 4
+    q = r.standard_normal((B * M, H, d))
+    K1 = r.standard_normal((B, H, 1, d))
+    V1 = r.standard_normal((B, H, 1, d))
+    out = oracle.cross_attn(q, K1, V1, B, M)
+    assert np.array_equal(out, np.repeat(V1[:, :, 0], M, axis=0))     # T_ctx = 1
+    T = 9
+    K = r.standard_normal((B, H, T, d))
+    Vv = r.standard_normal((B, H, T, d))
+    out = oracle.cross_attn(np.zeros_like(q), K, Vv, B, M)
+    assert np.allclose(out, np.repeat(Vv.mean(axis=2), M, axis=0), atol=1e-14)
+    Ksame = np.repeat(K[:, :, :1], T, axis=2)                          # identical keys
+    out = oracle.cross_attn(q, Ksame, Vv, B, M)
+    assert np.allclose(out, np.repeat(Vv.mean(axis=2), M, axis=0), atol=1e-14)
+
+
+def test_self_attn_single_position_and_block_diagonal_tile():
+    r = np.random.default_rng(8)
+    R, H, d = 4, 2, 8
+    q = r.standard_normal((R, H, d))
+    hk = r.standard_normal((R, 1, H, d))
+    hv = r.standard_normal((R, 1, H, d))
+    out = oracle.self_attn(q, hk, hv, np.ones((R, 1), np.uint8))
+    assert np.array_equal(out, hv[:, 0])                                 # T_self = 1
+    # Section 5.2: G = 4 rows with T_self = 3 as one 4 x 12 tile under a
+    # block-diagonal mask equals four separate 1 x 3 attentions.
+    G, T = 4, 3
+    q = r.standard_normal((G, H, d))
+    hk = r.standard_normal((G, T, H, d))
+    hv = r.standard_normal((G, T, H, d))
+    out = oracle.self_attn(q, hk, hv, np.ones((G, T), np.uint8))
+    blockmask = np.kron(np.eye(G), np.ones((1, T))).astype(bool)        # 4 x 12
+    for h in range(H):
+        Kt = hk[:, :, h].reshape(G * T, d)
+        Vt = hv[:, :, h].reshape(G * T, d)
+        S = q[:, h] @ Kt.T / math.sqrt(d)
+        S[~blockmask] = -np.inf
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        assert np.abs(P @ Vt - out[:, h]).max() < 1e-12
+    # masked-out positions (a dead row's missing past) are excluded
+    valid = np.array([[1, 0, 1], [0, 0, 1], [1, 1, 1], [0, 1, 1]], np.uint8)
+    out = oracle.self_attn(q, hk, hv, valid)
+    for g in range(G):
+        keep = valid[g].astype(bool)
+        ref = _sdpa64(q[g][:, None, :], np.ascontiguousarray(hk[g][keep].transpose(1, 0, 2)),
+                      np.ascontiguousarray(hv[g][keep].transpose(1, 0, 2)))[:, 0]
+        assert np.abs(out[g] - ref).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
+# The decode walk end to end (tiny workload)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_oracle_decode_invariants(seed):
+    w = W.WORKLOADS["tiny_fp32"]
+    sids = W.make_catalog(w, seed)
+    ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+    req = W.make_requests(w, seed)
+    ctx = W.make_context(w, seed)
+    ix = oracle.build_index(w, sids, ads)
+    st = initial_state(w)
+    catalog = {tuple(s) for s in sids.tolist()}
+    lp_path = np.zeros(w.B)
+    for t in range(w.L):
+        inp = W.make_step(w, seed, t)
+        out = step(w, ix, req, ctx, t, st, inp, lambda a: W.as_float(w, a))
+        if t == 0:
+            root_kept = oracle.mask_bits_to_bool(out.mask, w.V).sum(axis=1)
+            live0 = (out.parent >= 0).reshape(w.B, -1).sum(axis=1)
+            assert (live0 == np.minimum(w.schedule[0], root_kept)).all()
+        for b in range(w.B):
+            s = out.sel_s[b]
+            assert (np.diff(s) <= 0).all()
+        nxt = out.next_state
+        # accumulated score = sum of the chosen tokens' log-probs along the path
+        live = out.parent >= 0
+        prev_acc = st.acc
+        assert np.allclose(nxt.acc[live], prev_acc[out.parent[live]] +
+                           out.lp[out.parent[live], out.token[live]], atol=1e-12)
+        st = nxt
+    final = {tuple(x) for x in st.tokens[st.live].tolist()}
+    assert final and final <= catalog
