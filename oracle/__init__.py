@@ -170,14 +170,23 @@ class Index:
         lib().orc_index_rows(self.h, level, _p(pfx), _p(bm), _p(bl))
         return pfx, bm[:, : self.w_bm], bl[:, : self.w_bl]
 
-    def mask_row(self, prefix, t: int, user_bm, user_locs) -> np.ndarray:
-        """Mask words of one row; t < 0 marks a dead row."""
+    def user_blooms(self, user_locs) -> np.ndarray:
+        """bloom(l) rows [n_loc, w_bl] of a request's locations (eq 8 operand)."""
+        rows = np.zeros((max(len(user_locs), 1), max(self.w_bl, 1)), np.uint64)
+        if self.w_bl:
+            for j, g in enumerate(user_locs):
+                lib().orc_bloom_row(int(g), self.bloom_bits, self.bloom_k, _p(rows[j]))
+        return rows
+
+    def mask_row(self, prefix, t: int, user_bm, user_locs, blooms=None) -> np.ndarray:
+        """Mask words of one row; t < 0 marks a dead row.  ``blooms`` may hold
+        the request's precomputed user_blooms(user_locs)."""
         words = (self.V + 63) // 64
         out = np.zeros(words, dtype=np.uint64)
         p = _c(prefix if t > 0 else [0], np.int32)
         ub = _c(user_bm, np.uint64)
-        ul = _c(user_locs if len(user_locs) else [0], np.int32)
-        lib().orc_mask_row(self.h, _p(p), t, _p(ub), _p(ul), len(user_locs), _p(out))
+        bl = self.user_blooms(user_locs) if blooms is None else _c(blooms, np.uint64)
+        lib().orc_mask_row(self.h, _p(p), t, _p(ub), _p(bl), len(user_locs), _p(out))
         return out
 
     def __del__(self):

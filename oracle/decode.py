@@ -114,10 +114,11 @@ def step(w, ix, req, ctx, t: int, st: OracleState, inp: dict, as_float,
     mask = np.zeros((R, words), np.uint64)
     logits = as_float(inp["logits"]).astype(np.float64)
     lp = np.empty((R, V))
+    blooms = [ix.user_blooms(req.locs[b]) for b in range(B)]
     for r in range(R):
         b = r // M
         mask[r] = ix.mask_row(st.tokens[r, :t], t if st.live[r] else -1,
-                              req.user_bm[b], req.locs[b])
+                              req.user_bm[b], req.locs[b], blooms[b])
         lp[r] = log_softmax(logits[r])
     keep = mask_bits_to_bool(mask, V)
     cand = np.where(keep, st.acc[:, None] + lp, -np.inf)

@@ -119,20 +119,20 @@ void orc_index_add_ads(orc_index *ix, int64_t n_ads, const int64_t *ad_sid,
                        const uint64_t *rules, const int64_t *geo_off,
                        const int32_t *geo_ids)
 {
-    uint64_t *tmp = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(ix->w_bl ? ix->w_bl : 1));
     for (int64_t a = 0; a < n_ads; a++) {
         int64_t s = ad_sid[a];
         for (int w = 0; w < ix->w_bm; w++)
             ix->leaf_bm[s * ix->w_bm + w] |= rules[a * ix->w_bm + w];
         if (ix->w_bl) {
+            /* bloom(a) = OR of bloom(g) over the ad's geo ids: set each id's bits */
+            uint32_t pos[64];
             for (int64_t j = geo_off[a]; j < geo_off[a + 1]; j++) {
-                orc_bloom_row(geo_ids[j], ix->bloom_bits, ix->bloom_k, tmp);
-                for (int w = 0; w < ix->w_bl; w++)
-                    ix->leaf_bl[s * ix->w_bl + w] |= tmp[w];
+                orc_bloom_positions(geo_ids[j], ix->bloom_bits, ix->bloom_k, pos);
+                for (int i = 0; i < ix->bloom_k; i++)
+                    ix->leaf_bl[s * ix->w_bl + pos[i] / 64] |= 1ULL << (pos[i] % 64);
             }
         }
     }
-    free(tmp);
 }
 
 static const orc_index *g_sort_ix;
@@ -225,11 +225,12 @@ void orc_index_rows(const orc_index *ix, int l, int32_t *pfx, uint64_t *bm, uint
 /* ------------------------------------------------------------------------ */
 /* O3-O5: the CD and TM masks of one beam row (eqs 1, 2, 5, 8).             */
 /* prefix: the row's t tokens; t < 0 marks a dead row (all tokens masked).  */
-/* user_bm [w_bm]; user_locs [n_loc] geo ids.  mask: ceil(V/64) words.      */
+/* user_bm [w_bm]; user_blooms [n_loc, w_bl]: bloom(l) of each user         */
+/* location (orc_bloom_row).  mask: ceil(V/64) words.                       */
 /* Returns the number of tokens kept.                                       */
 /* ------------------------------------------------------------------------ */
 int orc_mask_row(const orc_index *ix, const int32_t *prefix, int t,
-                 const uint64_t *user_bm, const int32_t *user_locs, int n_loc,
+                 const uint64_t *user_bm, const uint64_t *user_blooms, int n_loc,
                  uint64_t *mask)
 {
     int V = ix->V, words = (V + 63) / 64, kept = 0;
@@ -237,7 +238,6 @@ int orc_mask_row(const orc_index *ix, const int32_t *prefix, int t,
     if (t < 0 || t >= ix->L) return 0;
     int32_t child[17];
     for (int i = 0; i < t; i++) child[i] = prefix[i];
-    uint64_t *bl_l = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(ix->w_bl ? ix->w_bl : 1));
     for (int v = 0; v < V; v++) {
         child[t] = v;
         int64_t c = orc_index_find(ix, child, t + 1);
@@ -247,17 +247,15 @@ int orc_mask_row(const orc_index *ix, const int32_t *prefix, int t,
         int bl_ok = 1;
         if (ix->w_bl) {                                     /* eq 8, ANY of locations */
             bl_ok = 0;
-            for (int j = 0; j < n_loc && !bl_ok; j++) {
-                orc_bloom_row(user_locs[j], ix->bloom_bits, ix->bloom_k, bl_l);
-                bl_ok = orc_bloom_contains(ix->bl[t + 1] + c * ix->w_bl, bl_l, ix->w_bl);
-            }
+            for (int j = 0; j < n_loc && !bl_ok; j++)
+                bl_ok = orc_bloom_contains(ix->bl[t + 1] + c * ix->w_bl,
+                                           user_blooms + (size_t)j * ix->w_bl, ix->w_bl);
         }
         if (bm_ok && bl_ok) {                               /* CD * TM = 1 */
             mask[v / 64] |= 1ULL << (v % 64);
             kept++;
         }
     }
-    free(bl_l);
     return kept;
 }
 

@@ -1,0 +1,308 @@
+"""GPU parity of each hot-path kernel against the CPU oracle, through the C ABI.
+
+Sizes span several tiles with ragged tails; edge cases cover dead rows, ties,
+k larger than the survivors, the large-threshold-bin fallback of the top-k and
+single-row requests.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import workload as W
+from tests.helpers import attn_close, to_dev, to_np64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import wide_beam_sid_amd  # noqa: F401
+    yield
+
+
+def _gr():
+    import wide_beam_sid_amd as gr
+    return gr
+
+
+def _rand(shape, dtype, rng):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _as_f(a, dtype):
+    return W.bf16_bits_to_f32(a).astype(np.float64) if dtype == "bf16" else a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# A1: cross-attention
+# ---------------------------------------------------------------------------
+
+CROSS_CASES = [
+    # B, M, H, T, d, dtype
+    (1, 8, 2, 16, 32, "f32"),
+    (3, 5, 2, 7, 64, "f32"),
+    (2, 37, 2, 70, 64, "bf16"),      # ragged beams and keys
+    (3, 129, 4, 64, 32, "bf16"),     # two row tiles + 1
+    (1, 300, 2, 2048, 128, "bf16"),  # long context tiles
+    (16, 256, 4, 64, 64, "bf16"),
+    (2, 1, 8, 256, 64, "bf16"),      # one beam per request
+    (1, 20, 16, 1, 128, "bf16"),     # T_ctx = 1: output = V
+]
+
+
+@pytest.mark.parametrize("B,M,H,T,d,dt", CROSS_CASES)
+def test_cross_attn_parity(B, M, H, T, d, dt):
+    gr = _gr()
+    rng = np.random.default_rng(B * 1000 + M + T)
+    q = _rand((B * M, H, d), dt, rng)
+    K = _rand((B, H, T, d), dt, rng)
+    Vv = _rand((B, H, T, d), dt, rng)
+    out = torch.empty(to_dev(q, dt).shape, dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                      device="cuda")
+    gr.cross_attn(to_dev(q, dt), to_dev(K, dt), to_dev(Vv, dt), out, B, M)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attn(_as_f(q, dt), _as_f(K, dt), _as_f(Vv, dt), B, M)
+    attn_close(to_np64(out), ref, dt, f"cross {B}x{M}x{H}x{T}x{d}")
+    if T == 1:
+        got = to_np64(out)
+        assert np.array_equal(got, np.repeat(_as_f(Vv, dt)[:, :, 0], M, axis=0))
+
+
+# ---------------------------------------------------------------------------
+# A2: paged self-attention
+# ---------------------------------------------------------------------------
+
+SELF_CASES = [
+    # R, H, d, L, t, dtype
+    (8, 2, 32, 3, 0, "f32"),
+    (8, 2, 32, 3, 2, "f32"),
+    (37, 4, 64, 4, 3, "bf16"),
+    (1000, 4, 64, 4, 1, "bf16"),
+    (301, 16, 128, 3, 2, "bf16"),
+    (130, 8, 64, 4, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("R,H,d,L,t,dt", SELF_CASES)
+def test_self_attn_paged_parity(R, H, d, L, t, dt):
+    gr = _gr()
+    rng = np.random.default_rng(R + 7 * t)
+    old = 3 * R + 5                      # blocks already in the pool
+    pool_blocks = old + R
+    kp = _rand((pool_blocks, H, d), dt, rng)
+    vp = _rand((pool_blocks, H, d), dt, rng)
+    q, kn, vn = (_rand((R, H, d), dt, rng) for _ in range(3))
+    table = rng.integers(0, old, size=(R, L)).astype(np.int32)
+    table[rng.random((R, L)) < 0.15] = -1          # missing past (dead rows)
+    table[:, t:] = -1
+    fresh = old
+    dkp, dvp, dtab = to_dev(kp, dt), to_dev(vp, dt), to_dev(table)
+    out = torch.empty(to_dev(q, dt).shape, dtype=dkp.dtype, device="cuda")
+    gr.self_attn_paged(to_dev(q, dt), to_dev(kn, dt), to_dev(vn, dt), dkp, dvp, dtab, fresh, t, out)
+    torch.cuda.synchronize()
+    # oracle: dense per-row history gathered from the same (input) pool
+    hk = np.zeros((R, t + 1, H, d))
+    hv = np.zeros((R, t + 1, H, d))
+    ok = np.zeros((R, t + 1), np.uint8)
+    kpf, vpf = _as_f(kp, dt), _as_f(vp, dt)
+    for j in range(t):
+        live = table[:, j] >= 0
+        hk[live, j] = kpf[table[live, j]]
+        hv[live, j] = vpf[table[live, j]]
+        ok[live, j] = 1
+    hk[:, t], hv[:, t], ok[:, t] = _as_f(kn, dt), _as_f(vn, dt), 1
+    ref = oracle.self_attn(_as_f(q, dt), hk, hv, ok)
+    attn_close(to_np64(out), ref, dt, f"self R={R} t={t}")
+    # the current token went to block fresh + i and the table column t
+    gk = to_np64(dkp)
+    assert np.array_equal(gk[fresh:fresh + R], _as_f(kn, dt))
+    assert np.array_equal(to_np64(dvp)[fresh:fresh + R], _as_f(vn, dt))
+    assert np.array_equal(gk[:old], kpf[:old])
+    tab = dtab.cpu().numpy()
+    assert np.array_equal(tab[:, t], fresh + np.arange(R))
+    assert np.array_equal(np.delete(tab, t, axis=1), np.delete(table, t, axis=1))
+    if t == 0:
+        assert np.array_equal(to_np64(out), _as_f(vn, dt)) or dt == "f32"
+
+
+# ---------------------------------------------------------------------------
+# A3-A6: constrain / log-softmax / top-k / reorder
+# ---------------------------------------------------------------------------
+
+_TRIES = {}
+
+
+def _trie_case(w, seed):
+    key = (w, seed)
+    if key not in _TRIES:
+        gr = _gr()
+        sids = W.make_catalog(w, seed)
+        ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+        trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
+        view = trie.host_view()
+        ix = oracle.build_index(w, sids, ads)
+        n = view["num_nodes"]
+        prefix = [()] * n
+        for node in range(1, n):
+            prefix[node] = prefix[view["node_parent"][node]] + (int(view["node_token"][node]),)
+        _TRIES[key] = (trie, view, ix, prefix)
+    return _TRIES[key]
+
+
+def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mode="normal",
+             B=None):
+    """Run gr_constrain_topk on synthetic beam rows at depth t and check every
+    output against the oracle."""
+    gr = _gr()
+    B = B or w.B
+    trie, view, ix, prefix = _trie_case(w, seed)
+    rng = np.random.default_rng(seed * 31 + M_in + t)
+    R = B * M_in
+    depth_nodes = np.nonzero(view["node_depth"] == t)[0]
+    node_in = rng.choice(depth_nodes, size=R).astype(np.int32)
+    dead = rng.random(R) < dead_frac
+    node_in[dead] = -1
+    if acc_mode == "normal":
+        acc_in = (-rng.random(R) * 4).astype(np.float32)
+    else:
+        acc_in = np.full(R, -1.5, np.float32)
+    acc_in[dead] = -np.inf
+    if logit_mode == "normal":
+        logits = _rand((R, w.V), w.dtype, rng)
+    else:  # every logit equal: ties everywhere
+        logits = _rand((1, 1), w.dtype, rng).repeat(R * w.V).reshape(R, w.V)
+    req = W.make_requests(w.scaled(B=B), seed)
+    probes = gr.bloom_probes(req.locs.reshape(-1), w.bloom_bits, w.bloom_k) if w.bloom_bits else \
+        np.zeros((1, 1), np.uint32)
+    L = w.L
+    tokens_in = rng.integers(0, w.V, size=(R, L)).astype(np.int32)
+    table_in = rng.integers(0, 10**6, size=(R, L)).astype(np.int32)
+    dev = {k: to_dev(v) for k, v in dict(node_in=node_in, acc_in=acc_in, tokens_in=tokens_in,
+                                         table_in=table_in, user_bm=req.user_bm,
+                                         user_probes=probes).items()}
+    dev["logits"] = to_dev(logits, w.dtype)
+    Rn = B * k_out
+    out = dict(parent_out=torch.empty(Rn, dtype=torch.int32, device="cuda"),
+               token_out=torch.empty(Rn, dtype=torch.int32, device="cuda"),
+               node_out=torch.empty(Rn, dtype=torch.int32, device="cuda"),
+               acc_out=torch.empty(Rn, dtype=torch.float32, device="cuda"),
+               tokens_out=torch.empty((Rn, L), dtype=torch.int32, device="cuda"),
+               table_out=torch.empty((Rn, L), dtype=torch.int32, device="cuda"),
+               dbg_mask=torch.empty((R, (w.V + 63) // 64), dtype=torch.int64, device="cuda"),
+               dbg_scores=torch.empty((R, w.V), dtype=torch.float32, device="cuda"))
+    ws_bytes = gr.constrain_topk_workspace(B, M_in, w.V, k_out)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    args = gr.tail_args(B=B, M_in=M_in, V=w.V, k_out=k_out, t=t, L=L, n_loc=w.n_loc,
+                        dtype=gr.GR_BF16 if w.dtype == "bf16" else gr.GR_F32,
+                        user_bm=dev["user_bm"], user_probes=dev["user_probes"] if w.bloom_bits else None,
+                        logits=dev["logits"], node_in=dev["node_in"], acc_in=dev["acc_in"],
+                        tokens_in=dev["tokens_in"], table_in=dev["table_in"], ws=ws,
+                        ws_bytes=ws_bytes, **out)
+    gr.constrain_topk(trie, args)
+    torch.cuda.synchronize()
+    o = {k: v.cpu().numpy() for k, v in out.items()}
+    check_tail(w, ix, view, prefix, req, node_in, acc_in, W.as_float(w, logits).astype(np.float64),
+               M_in, k_out, t, o, tokens_in, table_in, B)
+    return o
+
+
+def check_tail(w, ix, view, prefix, req, node_in, acc_in, logits64, M_in, k_out, t, o,
+               tokens_in=None, table_in=None, B=None):
+    B = B or w.B
+    V, L = w.V, w.L
+    R = B * M_in
+    mask = o["dbg_mask"].view(np.uint64)
+    scores = o["dbg_scores"]
+    # A3: masks bit-exact
+    blooms = [ix.user_blooms(req.locs[b]) for b in range(B)]
+    exp_mask = np.zeros_like(mask)
+    for r in range(R):
+        b = r // M_in
+        live = node_in[r] >= 0
+        exp_mask[r] = ix.mask_row(list(prefix[node_in[r]]) if live else [], t if live else -1,
+                                  req.user_bm[b], req.locs[b], blooms[b])
+    assert np.array_equal(mask, exp_mask), "mask mismatch"
+    # A4: scores within tolerance of acc + fp64 log-softmax
+    keep = oracle.mask_bits_to_bool(mask, V)
+    assert np.array_equal(np.isfinite(scores), keep)
+    lp = np.stack([oracle.log_softmax(x) for x in logits64]) if R else np.zeros((0, V))
+    cand = np.where(keep, acc_in.astype(np.float64)[:, None] + lp, -np.inf)
+    if keep.any():
+        err = np.abs(scores[keep] - cand[keep])
+        bound = 2e-5 + 2e-7 * np.abs(cand[keep])
+        assert (err <= bound).all(), f"score err {err.max():.3g}"
+    # A5: top-k on the GPU's own scores, bit-exact
+    for b in range(B):
+        f, s = oracle.topk(scores[b * M_in:(b + 1) * M_in].reshape(-1), k_out)
+        n = f.size
+        sl = slice(b * k_out, b * k_out + n)
+        assert np.array_equal(o["parent_out"][sl], b * M_in + (f // V).astype(np.int32)), f"parent b={b}"
+        assert np.array_equal(o["token_out"][sl], (f % V).astype(np.int32)), f"token b={b}"
+        assert np.array_equal(o["acc_out"][sl].view(np.uint32), s.view(np.uint32))
+        dead = slice(b * k_out + n, (b + 1) * k_out)
+        assert (o["parent_out"][dead] == -1).all() and (o["node_out"][dead] == -1).all()
+        assert (o["token_out"][dead] == -1).all() and np.isneginf(o["acc_out"][dead]).all()
+    # A6: child node of (parent, token); token / table rows reordered
+    live = o["parent_out"] >= 0
+    par = o["parent_out"][live]
+    nodes = o["node_out"][live]
+    assert np.array_equal(view["node_parent"][nodes], node_in[par])
+    assert np.array_equal(view["node_token"][nodes], o["token_out"][live])
+    if tokens_in is not None:
+        tk = o["tokens_out"]
+        assert np.array_equal(tk[live, :t], tokens_in[par, :t])
+        assert np.array_equal(tk[live, t], o["token_out"][live])
+        assert (tk[live, t + 1:] == -1).all() and (tk[~live] == -1).all()
+        tb = o["table_out"]
+        assert np.array_equal(tb[live, :t + 1], table_in[par, :t + 1])
+        assert (tb[live, t + 1:] == -1).all() and (tb[~live] == -1).all()
+
+
+TAIL_WORKLOADS = {
+    "tiny": W.WORKLOADS["tiny_fp32"],
+    "main_50k": W.WORKLOADS["main_b16_m1024"].scaled(n_sids=50_000),
+    "long_50k": W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000),
+    "stress_20k": W.WORKLOADS["stress_b64"].scaled(n_sids=20_000, geo_per_ad=(1, 64)),
+}
+
+TAIL_CASES = [
+    # workload, seed, B, M_in, k_out, t, dead, logits, acc
+    ("tiny", 0, 1, 1, 8, 0, 0.0, "normal", "normal"),
+    ("tiny", 0, 1, 8, 8, 1, 0.2, "normal", "normal"),
+    ("tiny", 1, 1, 8, 8, 2, 0.0, "normal", "normal"),
+    ("main_50k", 1, 4, 1, 1024, 0, 0.0, "normal", "normal"),    # k > survivors: dead slots
+    ("main_50k", 1, 4, 300, 1000, 1, 0.1, "normal", "normal"),
+    ("main_50k", 1, 3, 1024, 1024, 2, 0.05, "normal", "normal"),
+    ("main_50k", 1, 2, 1024, 1024, 3, 0.0, "normal", "normal"),
+    ("main_50k", 1, 2, 700, 1024, 1, 0.0, "equal", "equal"),    # ties: huge threshold bin
+    ("main_50k", 1, 2, 64, 37, 1, 0.0, "equal", "normal"),
+    ("main_50k", 1, 2, 16, 5, 1, 1.0, "normal", "normal"),      # every row dead
+    ("long_50k", 3, 3, 300, 900, 1, 0.1, "normal", "normal"),
+    ("stress_20k", 4, 2, 1024, 1024, 1, 0.1, "normal", "normal"),
+    ("stress_20k", 4, 2, 1024, 1024, 2, 0.1, "normal", "normal"),
+]
+
+
+@pytest.mark.parametrize("name,seed,B,M_in,k_out,t,dead,lmode,amode", TAIL_CASES)
+def test_constrain_topk_parity(name, seed, B, M_in, k_out, t, dead, lmode, amode):
+    w = TAIL_WORKLOADS[name]
+    run_tail(w, seed, M_in, k_out, t, dead, lmode, amode, B=B)
+
+
+def test_constrain_topk_workspace_error():
+    gr = _gr()
+    w = TAIL_WORKLOADS["tiny"]
+    trie = _trie_case(w, 0)[0]
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    args = gr.tail_args(B=1, M_in=8, V=w.V, k_out=8, t=1, L=w.L, n_loc=1, dtype=gr.GR_F32,
+                        user_bm=small, user_probes=small, logits=small, node_in=small,
+                        acc_in=small, parent_out=small, token_out=small, node_out=small,
+                        acc_out=small, ws=small, ws_bytes=64)
+    with pytest.raises(gr.GrError) as e:
+        gr.constrain_topk(trie, args)
+    assert e.value.status == -4

@@ -1,0 +1,143 @@
+"""CPU-side checks of libgr.so: exports, argument validation, the host index
+builder and the request-side Bloom encoding (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import wide_beam_sid_amd as gr
+from synth import workload as W
+from wide_beam_sid_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gr_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gr.h but not exported"
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_bloom_probes_equal_oracle():
+    r = np.random.default_rng(0)
+    ids = r.integers(0, 2**31 - 1, size=500).astype(np.int32)
+    for w_bits, k in [(256, 3), (4096, 4), (8192, 5), (64, 1)]:
+        got = gr.bloom_probes(ids, w_bits, k)
+        for i in range(0, ids.size, 7):
+            assert got[i].tolist() == oracle.bloom_positions(int(ids[i]), w_bits, k).tolist()
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_argument_errors_return_codes_without_launch():
+    L = _lib.lib()
+    # null pointers / bad shapes are rejected before any HIP call
+    assert L.gr_cross_attn(None, None, None, None, 1, 1, 1, 1, 64, 1, None) == _lib.GR_E_INVALID
+    buf = ctypes.c_void_p(16)
+    assert L.gr_cross_attn(buf, buf, buf, buf, 1, 1, 1, 1, 48, 1, None) == _lib.GR_E_UNSUPPORTED
+    assert L.gr_cross_attn(buf, buf, buf, buf, 0, 1, 1, 1, 64, 1, None) == _lib.GR_E_INVALID
+    assert L.gr_cross_attn(buf, buf, buf, buf, 1, 1, 1, 1, 64, 7, None) == _lib.GR_E_INVALID
+    assert b"dtype" in L.gr_last_error()
+    # pool too small for the fresh blocks
+    assert L.gr_self_attn_paged(buf, buf, buf, buf, buf, 10, buf, 8, 4, 0, 4, 2, 64, 1, buf,
+                                None) == _lib.GR_E_INVALID
+    assert b"pool" in L.gr_last_error()
+    # t outside [0, L)
+    assert L.gr_self_attn_paged(buf, buf, buf, buf, buf, 100, buf, 0, 4, 4, 4, 2, 64, 1, buf,
+                                None) == _lib.GR_E_INVALID
+    assert L.gr_bloom_probes(None, 3, 4096, 4, None) == _lib.GR_E_INVALID
+    assert L.gr_bloom_probes(None, 0, 1000, 4, None) == _lib.GR_E_INVALID
+    assert gr.constrain_topk_workspace(16, 1024, 256, 1024) > 16 * 1024 * 256 * 12
+
+
+def test_builder_rejects_bad_input():
+    with pytest.raises(gr.GrError) as e:
+        gr.Trie.build(np.array([[0, 5]], np.int32), 4, 1, 0, 0, [], host_only=True)
+    assert e.value.status == _lib.GR_E_INVALID
+    ch = W.AdChunk(0, np.array([3]), np.zeros((1, 1), np.uint64), np.zeros(2, np.int64),
+                   np.zeros(0, np.int32))
+    with pytest.raises(gr.GrError) as e:
+        gr.Trie.build(np.array([[0, 1]], np.int32), 4, 1, 0, 0, [ch], host_only=True)
+    assert "ad_sid" in str(e.value)
+
+
+def test_host_only_trie_is_rejected_by_hot_path():
+    t = gr.Trie.build(np.array([[0, 1]], np.int32), 4, 1, 0, 0, [], host_only=True)
+    a = gr.tail_args(B=1, M_in=1, V=4, k_out=1, t=0, L=2, n_loc=0, dtype=0)
+    st = _lib.lib().gr_constrain_topk(t.h, ctypes.byref(a), None)
+    assert st == _lib.GR_E_INVALID
+
+
+def _check_trie_against_oracle(w, seed):
+    sids = W.make_catalog(w, seed)
+    counts = W.ad_counts(w, seed)
+    ads = W.make_ads(w, seed, counts)
+    trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], host_only=True)
+    v = trie.host_view()
+    ix = oracle.build_index(w, sids, ads)
+    n = v["num_nodes"]
+    assert n == 1 + sum(ix.count(l) for l in range(1, w.L + 1))
+    assert v["num_entries"] == n - 1
+    depth, par, ntok = v["node_depth"], v["node_parent"], v["node_token"]
+    off, child, tok = v["node_offsets"], v["child_nodes"], v["tokens"]
+    # prefix of every node from the parent / token chain
+    prefix = [()] * n
+    for node in range(1, n):
+        assert par[node] < node
+        prefix[node] = prefix[par[node]] + (int(ntok[node]),)
+        assert len(prefix[node]) == depth[node]
+    for l in range(1, w.L + 1):
+        pf, bm, bl = ix.rows(l)
+        lookup = {tuple(p): i for i, p in enumerate(pf.tolist())}
+        nodes = np.nonzero(depth == l)[0]
+        assert len(nodes) == len(lookup)
+        for node in nodes:
+            i = lookup[prefix[node]]
+            j = node - 1                          # the entry leading into the node
+            assert child[j] == node and tok[j] == ntok[node]
+            assert np.array_equal(v["bitmask_table"][v["bitmask_index"][j]], bm[i])
+            if w.bloom_bits:
+                assert np.array_equal(v["bloom_table"][v["bloom_index"][j]], bl[i])
+    # CSR: children of a node are exactly the catalog's next tokens, sorted
+    expect = {(): []}
+    for l in range(1, w.L + 1):
+        for p in ix.rows(l)[0].tolist():
+            expect.setdefault(tuple(p[:-1]), []).append(p[-1])
+    for node in range(n):
+        toks = tok[off[node]:off[node + 1]].tolist()
+        assert toks == sorted(expect.get(prefix[node], []))
+    # deduplicated tables hold distinct rows
+    for name in ("bitmask_table", "bloom_table"):
+        tab = v[name]
+        if tab.size:
+            assert len({r.tobytes() for r in tab}) == tab.shape[0]
+    return v
+
+
+@pytest.mark.parametrize("name,w,seed", [
+    ("tiny", W.WORKLOADS["tiny_fp32"], 0),
+    ("tiny_s3", W.WORKLOADS["tiny_fp32"], 3),
+    ("deep", W.WORKLOADS["tiny_fp32"].scaled(L=4, V=6, n_sids=400), 1),
+    ("main_20k", W.WORKLOADS["main_b16_m1024"].scaled(n_sids=20_000), 1),
+    ("longctx_20k", W.WORKLOADS["longctx_b8"].scaled(n_sids=20_000), 3),
+    ("stress_5k", W.WORKLOADS["stress_b64"].scaled(n_sids=5_000, geo_per_ad=(1, 40)), 4),
+], ids=lambda x: x if isinstance(x, str) else "")
+def test_trie_builder_matches_oracle_unions(name, w, seed):
+    v = _check_trie_against_oracle(w, seed)
+    if name == "main_20k":
+        # single-child chains share rows: fewer rows than non-root nodes
+        assert v["bl_rows"] < v["num_entries"]

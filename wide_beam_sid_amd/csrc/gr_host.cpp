@@ -1,0 +1,795 @@
+// Host side of libgr: argument validation, the GTM SID trie builder
+// (GRACE Section 4.4 and Appendix A: CSR trie, subtree-union matchers of
+// eqs 4 and 9, deduplicated matcher tables), trie upload, request-side Bloom
+// probe encoding (Section 4.3) and the dispatch of the hot-path kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "gr_internal.h"
+
+using namespace gr;
+
+namespace {
+
+thread_local std::string g_err;
+
+gr_status fail(gr_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+gr_status hip_fail(hipError_t e, const char *what) {
+    return fail(GR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int hw_threads(int req) {
+    if (req > 0) return req;
+    unsigned n = std::thread::hardware_concurrency();
+    return n ? (int)std::min(n, 64u) : 4;
+}
+
+template <typename F>
+void parallel_for(int64_t n, int threads, F f) {
+    if (n <= 0) return;
+    threads = (int)std::max<int64_t>(1, std::min<int64_t>(threads, n / 4096 + 1));
+    if (threads == 1) { f(0, n); return; }
+    std::vector<std::thread> th;
+    int64_t chunk = (n + threads - 1) / threads;
+    for (int i = 0; i < threads; ++i) {
+        int64_t a = i * chunk, b = std::min(n, a + chunk);
+        if (a >= b) break;
+        th.emplace_back([=] { f(a, b); });
+    }
+    for (auto &t : th) t.join();
+}
+
+// Bloom positions of one id: first SplitMix64 output from state `id`
+// (Steele, Lea and Flood 2014), split into h1 (low half) and h2 (high half
+// forced odd), position i = (h1 + i*h2) mod w (Kirsch and Mitzenmacher 2006).
+inline void bloom_pos(uint64_t id, uint32_t w_bits, int k, uint32_t *out) {
+    uint64_t z = id + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    uint32_t h1 = (uint32_t)z, h2 = (uint32_t)(z >> 32) | 1u;
+    for (int i = 0; i < k; ++i) out[i] = (h1 + (uint32_t)i * h2) & (w_bits - 1u);
+}
+
+inline uint64_t row_hash(const uint64_t *r, int w) {
+    uint64_t h = 0x2545F4914F6CDD1Dull ^ (uint64_t)w;
+    for (int i = 0; i < w; ++i) {
+        h ^= r[i] + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+        h *= 0xFF51AFD7ED558CCDull;
+    }
+    return h ^ (h >> 33);
+}
+
+// Deduplicated table of fixed-width rows (open addressing on a row hash,
+// collisions resolved by comparing whole rows).
+struct RowTable {
+    int w = 0;
+    std::vector<uint64_t> rows;   // [n, w]
+    int64_t n = 0;
+    std::vector<int32_t> slot;
+    uint64_t mask = 0;
+
+    void init(int width, int64_t expected) {
+        w = width;
+        n = 0;
+        uint64_t cap = 16;
+        while (cap < (uint64_t)(expected * 2 + 16)) cap <<= 1;
+        slot.assign(cap, -1);
+        mask = cap - 1;
+    }
+    void grow() {
+        std::vector<int32_t> old(slot.size() * 2, -1);
+        slot.swap(old);
+        mask = slot.size() - 1;
+        for (int64_t i = 0; i < n; ++i) place(i, row_hash(&rows[i * w], w));
+    }
+    void place(int64_t id, uint64_t h) {
+        uint64_t s = h & mask;
+        while (slot[s] >= 0) s = (s + 1) & mask;
+        slot[s] = (int32_t)id;
+    }
+    // Returns the id of `r` (inserting it if new).  `r` may alias the slot
+    // rows[n*w] (in-place compaction of an already filled buffer).
+    int32_t insert(const uint64_t *r) {
+        if ((uint64_t)(n * 2 + 2) > slot.size()) grow();
+        uint64_t h = row_hash(r, w), s = h & mask;
+        while (slot[s] >= 0) {
+            const uint64_t *o = &rows[(int64_t)slot[s] * w];
+            if (std::memcmp(o, r, sizeof(uint64_t) * w) == 0) return slot[s];
+            s = (s + 1) & mask;
+        }
+        int64_t id = n++;
+        uint64_t *dst = &rows[id * w];
+        if (dst != r) std::memmove(dst, r, sizeof(uint64_t) * w);
+        slot[s] = (int32_t)id;
+        return (int32_t)id;
+    }
+};
+
+template <typename T>
+hipError_t upload(T **dptr, const T *src, size_t n) {
+    *dptr = nullptr;
+    if (n == 0) return hipSuccess;
+    hipError_t e = hipMalloc((void **)dptr, n * sizeof(T));
+    if (e != hipSuccess) return e;
+    return hipMemcpy(*dptr, src, n * sizeof(T), hipMemcpyHostToDevice);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Opaque handles
+// ---------------------------------------------------------------------------
+
+struct gr_trie_builder {
+    gr_trie_params p{};
+    int w_bl = 0, bpt = 0, threads = 1;
+    int64_t n_in = 0, n_leaf = 0;
+    std::vector<int64_t> leaf_of_input;  // input row -> leaf index
+    std::vector<uint64_t> leaf_key;      // sorted distinct packed SIDs
+    std::vector<int64_t> n_level;        // nodes per level 0..L
+    std::vector<int64_t> n_multi;        // nodes with >= 2 children per level
+    std::vector<uint64_t> leaf_bm;       // [n_leaf (+ room), w_bm]
+    std::vector<uint64_t> leaf_bl;       // [n_leaf (+ room), w_bl]
+};
+
+struct gr_trie {
+    TrieDev d{};
+    int device = 0;
+    bool has_host = false;
+    std::vector<int32_t> h_off, h_child, h_bmi, h_bli, h_depth, h_parent;
+    std::vector<int16_t> h_tok, h_ntok;
+    std::vector<uint64_t> h_bm, h_bl;
+    bool host_only = false;
+};
+
+extern "C" {
+
+const char *gr_last_error(void) { return g_err.c_str(); }
+const char *gr_version(void) { return "libgr 0.1 (gfx950)"; }
+
+gr_status gr_bloom_probes(const int32_t *ids, int64_t n, int32_t bloom_bits,
+                          int32_t bloom_k, uint32_t *positions) {
+    if (n < 0 || (n > 0 && (!ids || !positions)))
+        return fail(GR_E_INVALID, "gr_bloom_probes: null array");
+    if (bloom_bits < 64 || bloom_bits > 65536 || (bloom_bits & (bloom_bits - 1)))
+        return fail(GR_E_INVALID, "gr_bloom_probes: bloom_bits %d is not a power of two in [64, 65536]", bloom_bits);
+    if (bloom_k < 1 || bloom_k > 16)
+        return fail(GR_E_INVALID, "gr_bloom_probes: bloom_k %d not in [1, 16]", bloom_k);
+    for (int64_t i = 0; i < n; ++i) {
+        if (ids[i] < 0) return fail(GR_E_INVALID, "gr_bloom_probes: id[%lld] < 0", (long long)i);
+        bloom_pos((uint64_t)ids[i], (uint32_t)bloom_bits, bloom_k, positions + i * bloom_k);
+    }
+    return GR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Trie builder
+// ---------------------------------------------------------------------------
+
+gr_status gr_trie_builder_create(const gr_trie_params *params, const int32_t *sids,
+                                 int64_t n_sids, gr_trie_builder **out) {
+    if (!params || !out || (n_sids > 0 && !sids))
+        return fail(GR_E_INVALID, "gr_trie_builder_create: null argument");
+    *out = nullptr;
+    const gr_trie_params &p = *params;
+    if (p.sid_length < 1 || p.sid_length > 16)
+        return fail(GR_E_INVALID, "sid_length %d not in [1, 16]", p.sid_length);
+    if (p.vocab_size < 2 || p.vocab_size > 32768)
+        return fail(GR_E_INVALID, "vocab_size %d not in [2, 32768]", p.vocab_size);
+    if (p.w_bm < 1 || p.w_bm > MAX_WBM)
+        return fail(GR_E_INVALID, "w_bm %d not in [1, %d]", p.w_bm, MAX_WBM);
+    if (p.bloom_bits != 0) {
+        if (p.bloom_bits < 64 || p.bloom_bits > 65536 || (p.bloom_bits & (p.bloom_bits - 1)))
+            return fail(GR_E_INVALID, "bloom_bits %d is not 0 or a power of two in [64, 65536]", p.bloom_bits);
+        if (p.bloom_k < 1 || p.bloom_k > 16)
+            return fail(GR_E_INVALID, "bloom_k %d not in [1, 16]", p.bloom_k);
+    }
+    if (n_sids < 1 || n_sids > (int64_t)1 << 30)
+        return fail(GR_E_INVALID, "n_sids %lld not in [1, 2^30]", (long long)n_sids);
+    int bpt = 1;
+    while ((1 << bpt) < p.vocab_size) ++bpt;
+    if (bpt * p.sid_length > 64)
+        return fail(GR_E_UNSUPPORTED, "L * ceil(log2 V) = %d exceeds 64", bpt * p.sid_length);
+
+    gr_trie_builder *b = new (std::nothrow) gr_trie_builder;
+    if (!b) return fail(GR_E_NOMEM, "out of host memory");
+    try {
+        b->p = p;
+        b->w_bl = p.bloom_bits / 64;
+        b->bpt = bpt;
+        b->threads = hw_threads(p.n_threads);
+        b->n_in = n_sids;
+        const int L = p.sid_length;
+        std::vector<std::pair<uint64_t, int64_t>> kv((size_t)n_sids);
+        for (int64_t i = 0; i < n_sids; ++i) {
+            uint64_t key = 0;
+            for (int l = 0; l < L; ++l) {
+                int32_t tok = sids[i * L + l];
+                if (tok < 0 || tok >= p.vocab_size) {
+                    delete b;
+                    return fail(GR_E_INVALID, "sids[%lld][%d] = %d out of [0, %d)",
+                                (long long)i, l, tok, p.vocab_size);
+                }
+                key = (key << bpt) | (uint64_t)tok;
+            }
+            kv[i] = {key, i};
+        }
+        std::sort(kv.begin(), kv.end());
+        b->leaf_of_input.assign(n_sids, -1);
+        for (int64_t i = 0; i < n_sids; ++i) {
+            if (i == 0 || kv[i].first != kv[i - 1].first) b->leaf_key.push_back(kv[i].first);
+            b->leaf_of_input[kv[i].second] = (int64_t)b->leaf_key.size() - 1;
+        }
+        b->n_leaf = (int64_t)b->leaf_key.size();
+        // Level sizes and multi-child counts (to reserve room for upper rows).
+        b->n_level.assign(L + 1, 0);
+        b->n_multi.assign(L + 1, 0);
+        b->n_level[0] = 1;
+        for (int l = 1; l <= L; ++l) {
+            int sh = (L - l) * bpt;
+            int64_t n = 0;
+            for (int64_t i = 0; i < b->n_leaf; ++i)
+                if (i == 0 || (b->leaf_key[i] >> sh) != (b->leaf_key[i - 1] >> sh)) ++n;
+            b->n_level[l] = n;
+        }
+        for (int l = 1; l < L; ++l) {
+            // level-l nodes with at least two distinct level-(l+1) children
+            int sh1 = (L - l - 1) * bpt;
+            int64_t multi = 0, run = 0;
+            uint64_t prev_c = 0, prev_p = 0;
+            for (int64_t i = 0; i < b->n_leaf; ++i) {
+                uint64_t c = b->leaf_key[i] >> sh1;
+                if (i > 0 && c == prev_c) continue;
+                uint64_t par = c >> bpt;
+                if (i > 0 && par == prev_p) {
+                    if (++run == 2) ++multi;
+                } else {
+                    run = 1;
+                    prev_p = par;
+                }
+                prev_c = c;
+            }
+            b->n_multi[l] = multi;
+        }
+        int64_t room = b->n_leaf;
+        for (int l = 1; l < L; ++l) room += b->n_multi[l];
+        b->leaf_bm.assign((size_t)room * p.w_bm, 0);
+        if (b->w_bl) b->leaf_bl.assign((size_t)room * b->w_bl, 0);
+    } catch (const std::bad_alloc &) {
+        delete b;
+        return fail(GR_E_NOMEM, "out of host memory building the catalog");
+    }
+    *out = b;
+    return GR_OK;
+}
+
+gr_status gr_trie_builder_add_ads(gr_trie_builder *b, int64_t n_ads, const int64_t *ad_sid,
+                                  const uint64_t *rules, const int64_t *geo_offsets,
+                                  const int32_t *geo_ids) {
+    if (!b) return fail(GR_E_INVALID, "gr_trie_builder_add_ads: null builder");
+    if (n_ads < 0) return fail(GR_E_INVALID, "n_ads < 0");
+    if (n_ads == 0) return GR_OK;
+    if (!ad_sid || !rules) return fail(GR_E_INVALID, "gr_trie_builder_add_ads: null array");
+    if (b->w_bl && !geo_offsets) return fail(GR_E_INVALID, "geo_offsets is NULL with a Bloom matcher");
+    for (int64_t a = 0; a < n_ads; ++a)
+        if (ad_sid[a] < 0 || ad_sid[a] >= b->n_in)
+            return fail(GR_E_INVALID, "ad_sid[%lld] = %lld out of [0, %lld)", (long long)a,
+                        (long long)ad_sid[a], (long long)b->n_in);
+    if (b->w_bl) {
+        if (geo_offsets[0] < 0) return fail(GR_E_INVALID, "geo_offsets[0] < 0");
+        for (int64_t a = 0; a < n_ads; ++a)
+            if (geo_offsets[a + 1] < geo_offsets[a])
+                return fail(GR_E_INVALID, "geo_offsets decreases at %lld", (long long)a);
+        if (geo_offsets[n_ads] > geo_offsets[0] && !geo_ids)
+            return fail(GR_E_INVALID, "geo_ids is NULL");
+        for (int64_t j = geo_offsets[0]; j < geo_offsets[n_ads]; ++j)
+            if (geo_ids[j] < 0) return fail(GR_E_INVALID, "geo_ids[%lld] < 0", (long long)j);
+    }
+    const int wbm = b->p.w_bm, wbl = b->w_bl, k = b->p.bloom_k;
+    const uint32_t wbits = (uint32_t)b->p.bloom_bits;
+    uint64_t *lbm = b->leaf_bm.data();
+    uint64_t *lbl = b->leaf_bl.data();
+    const int64_t *leaf_of = b->leaf_of_input.data();
+    parallel_for(n_ads, b->threads, [&](int64_t a0, int64_t a1) {
+        uint32_t pos[16];
+        for (int64_t a = a0; a < a1; ++a) {
+            int64_t leaf = leaf_of[ad_sid[a]];
+            for (int w = 0; w < wbm; ++w) {
+                uint64_t r = rules[a * wbm + w];
+                if (r) __atomic_fetch_or(&lbm[leaf * wbm + w], r, __ATOMIC_RELAXED);
+            }
+            if (!wbl) continue;
+            uint64_t *row = lbl + leaf * wbl;
+            for (int64_t j = geo_offsets[a]; j < geo_offsets[a + 1]; ++j) {
+                bloom_pos((uint64_t)geo_ids[j], wbits, k, pos);
+                for (int i = 0; i < k; ++i) {
+                    uint64_t bit = 1ull << (pos[i] & 63);
+                    uint64_t *wd = row + (pos[i] >> 6);
+                    if (!(__atomic_load_n(wd, __ATOMIC_RELAXED) & bit))
+                        __atomic_fetch_or(wd, bit, __ATOMIC_RELAXED);
+                }
+            }
+        }
+    });
+    return GR_OK;
+}
+
+void gr_trie_builder_destroy(gr_trie_builder *b) { delete b; }
+
+static void free_trie_dev(gr_trie *t) {
+    if (!t) return;
+    hipFree((void *)t->d.node_offsets);
+    hipFree((void *)t->d.child_nodes);
+    hipFree((void *)t->d.tokens);
+    hipFree((void *)t->d.bitmask_index);
+    hipFree((void *)t->d.bloom_index);
+    hipFree((void *)t->d.bitmask_table);
+    hipFree((void *)t->d.bloom_table);
+    t->d = TrieDev{};
+}
+
+static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *child,
+                             const int16_t *tok, const int32_t *bmi, const int32_t *bli,
+                             const uint64_t *bm, const uint64_t *bl) {
+    hipError_t e;
+    int32_t *d_off, *d_child, *d_bmi, *d_bli = nullptr;
+    int16_t *d_tok;
+    uint64_t *d_bm, *d_bl = nullptr;
+    TrieDev &d = t->d;
+    hipGetDevice(&t->device);
+    if ((e = upload(&d_off, off, (size_t)d.num_nodes + 1)) != hipSuccess) goto err;
+    d.node_offsets = d_off;
+    if ((e = upload(&d_child, child, (size_t)d.num_entries)) != hipSuccess) goto err;
+    d.child_nodes = d_child;
+    if ((e = upload(&d_tok, tok, (size_t)d.num_entries)) != hipSuccess) goto err;
+    d.tokens = d_tok;
+    if ((e = upload(&d_bmi, bmi, (size_t)d.num_entries)) != hipSuccess) goto err;
+    d.bitmask_index = d_bmi;
+    if ((e = upload(&d_bm, bm, (size_t)d.bm_rows * d.w_bm)) != hipSuccess) goto err;
+    d.bitmask_table = d_bm;
+    if (d.w_bl) {
+        if ((e = upload(&d_bli, bli, (size_t)d.num_entries)) != hipSuccess) goto err;
+        d.bloom_index = d_bli;
+        if ((e = upload(&d_bl, bl, (size_t)d.bl_rows * d.w_bl)) != hipSuccess) goto err;
+        d.bloom_table = d_bl;
+    }
+    return GR_OK;
+err:
+    free_trie_dev(t);
+    if (e == hipErrorOutOfMemory) return fail(GR_E_NOMEM, "device memory exhausted uploading the trie");
+    return hip_fail(e, "uploading the trie");
+}
+
+gr_status gr_trie_builder_finish(gr_trie_builder *b, gr_trie **out) {
+    if (!b || !out) {
+        delete b;
+        return fail(GR_E_INVALID, "gr_trie_builder_finish: null argument");
+    }
+    *out = nullptr;
+    gr_trie *t = new (std::nothrow) gr_trie;
+    if (!t) {
+        delete b;
+        return fail(GR_E_NOMEM, "out of host memory");
+    }
+    gr_status st = GR_OK;
+    try {
+        const int L = b->p.sid_length, bpt = b->bpt, wbm = b->p.w_bm, wbl = b->w_bl;
+        const uint64_t tokmask = (1ull << bpt) - 1;
+        // Node numbering: root 0, then level 1, 2, ..., L in sorted-prefix order
+        // (breadth first; a node's children are contiguous and sorted by token).
+        std::vector<int64_t> base(L + 2, 0);
+        base[0] = 0;
+        base[1] = 1;
+        for (int l = 1; l <= L; ++l) base[l + 1] = base[l] + b->n_level[l];
+        const int64_t num_nodes = base[L + 1];
+        const int64_t num_entries = num_nodes - 1;
+        if (num_nodes > INT32_MAX) {
+            delete b;
+            delete t;
+            return fail(GR_E_UNSUPPORTED, "trie with %lld nodes exceeds int32 ids", (long long)num_nodes);
+        }
+        // Per level: sorted prefix keys and, for each node, its first child.
+        std::vector<int32_t> off((size_t)num_nodes + 1, (int32_t)num_entries);
+        std::vector<int32_t> child((size_t)num_entries);
+        std::vector<int16_t> tok((size_t)num_entries);
+        std::vector<int32_t> depth((size_t)num_nodes), parent((size_t)num_nodes);
+        std::vector<int16_t> ntok((size_t)num_nodes);
+        depth[0] = 0;
+        parent[0] = -1;
+        ntok[0] = -1;
+        std::vector<std::vector<uint64_t>> pk(L + 1);
+        for (int l = 1; l <= L; ++l) {
+            int sh = (L - l) * bpt;
+            pk[l].reserve((size_t)b->n_level[l]);
+            for (int64_t i = 0; i < b->n_leaf; ++i) {
+                uint64_t k = b->leaf_key[i] >> sh;
+                if (pk[l].empty() || pk[l].back() != k) pk[l].push_back(k);
+            }
+        }
+        // children ranges
+        {
+            // root's children: all level-1 nodes
+            off[0] = 0;
+            for (int l = 1; l <= L; ++l) {
+                int64_t pi = -1;  // parent index within level l-1
+                for (int64_t i = 0; i < (int64_t)pk[l].size(); ++i) {
+                    int64_t id = base[l] + i;
+                    uint64_t pkey = pk[l][i] >> bpt;
+                    if (l == 1) {
+                        pi = 0;
+                    } else {
+                        if (pi < 0 || pk[l - 1][pi] != pkey) {
+                            ++pi;
+                            while (pk[l - 1][pi] != pkey) ++pi;  // keys are sorted
+                            off[base[l - 1] + pi] = (int32_t)(id - 1);
+                        }
+                    }
+                    int64_t pid = (l == 1) ? 0 : base[l - 1] + pi;
+                    depth[id] = l;
+                    parent[id] = (int32_t)pid;
+                    ntok[id] = (int16_t)(pk[l][i] & tokmask);
+                    child[id - 1] = (int32_t)id;
+                    tok[id - 1] = (int16_t)(pk[l][i] & tokmask);
+                }
+            }
+            // nodes with children got their first entry; leaves keep
+            // num_entries; make offsets non-decreasing by a backward pass.
+            for (int64_t n = num_nodes - 1; n >= 0; --n)
+                if (off[n] > off[n + 1]) off[n] = off[n + 1];
+        }
+        // Matcher rows: leaves from the ads, then each upper node = OR of its
+        // children (a single-child node reuses its child's row id).
+        auto build_rows = [&](std::vector<uint64_t> &store, int w, std::vector<int32_t> &idx) {
+            RowTable tab;
+            tab.rows.swap(store);
+            tab.init(w, b->n_leaf);
+            std::vector<int32_t> rid((size_t)num_nodes, -1);
+            for (int64_t i = 0; i < b->n_leaf; ++i)
+                rid[base[L] + i] = tab.insert(&tab.rows[(size_t)i * w]);
+            std::vector<uint64_t> tmp((size_t)w);
+            for (int l = L - 1; l >= 1; --l) {
+                for (int64_t i = 0; i < b->n_level[l]; ++i) {
+                    int64_t id = base[l] + i;
+                    int64_t c0 = off[id] + 1, c1 = off[id + 1] + 1;  // child node ids
+                    if (c1 - c0 == 1) {
+                        rid[id] = rid[c0];
+                        continue;
+                    }
+                    std::fill(tmp.begin(), tmp.end(), 0ull);
+                    for (int64_t c = c0; c < c1; ++c) {
+                        const uint64_t *r = &tab.rows[(size_t)rid[c] * w];
+                        for (int q = 0; q < w; ++q) tmp[q] |= r[q];
+                    }
+                    if ((size_t)(tab.n + 1) * w > tab.rows.size()) tab.rows.resize((size_t)(tab.n + 1) * w * 2);
+                    std::memcpy(&tab.rows[(size_t)tab.n * w], tmp.data(), sizeof(uint64_t) * w);
+                    rid[id] = tab.insert(&tab.rows[(size_t)tab.n * w]);
+                }
+            }
+            idx.resize((size_t)num_entries);
+            for (int64_t j = 0; j < num_entries; ++j) idx[j] = rid[j + 1];
+            tab.rows.resize((size_t)tab.n * w);
+            tab.rows.shrink_to_fit();
+            store.swap(tab.rows);
+            return tab.n;
+        };
+        std::vector<int32_t> bmi, bli;
+        int64_t bm_rows = build_rows(b->leaf_bm, wbm, bmi);
+        int64_t bl_rows = 0;
+        if (wbl) bl_rows = build_rows(b->leaf_bl, wbl, bli);
+
+        TrieDev &d = t->d;
+        d.V = b->p.vocab_size;
+        d.L = L;
+        d.w_bm = wbm;
+        d.w_bl = wbl;
+        d.bloom_bits = b->p.bloom_bits;
+        d.bloom_k = wbl ? b->p.bloom_k : 0;
+        d.num_nodes = num_nodes;
+        d.num_entries = num_entries;
+        d.bm_rows = bm_rows;
+        d.bl_rows = bl_rows;
+        t->host_only = b->p.host_only != 0;
+        if (!t->host_only)
+            st = upload_trie(t, off.data(), child.data(), tok.data(), bmi.data(),
+                             wbl ? bli.data() : nullptr, b->leaf_bm.data(),
+                             wbl ? b->leaf_bl.data() : nullptr);
+        if (st == GR_OK && (b->p.keep_host || t->host_only)) {
+            t->has_host = true;
+            t->h_off.swap(off);
+            t->h_child.swap(child);
+            t->h_tok.swap(tok);
+            t->h_bmi.swap(bmi);
+            t->h_bli.swap(bli);
+            t->h_bm.swap(b->leaf_bm);
+            t->h_bl.swap(b->leaf_bl);
+            t->h_depth.swap(depth);
+            t->h_parent.swap(parent);
+            t->h_ntok.swap(ntok);
+        }
+    } catch (const std::bad_alloc &) {
+        st = fail(GR_E_NOMEM, "out of host memory finishing the trie");
+    }
+    delete b;
+    if (st != GR_OK) {
+        free_trie_dev(t);
+        delete t;
+        return st;
+    }
+    *out = t;
+    return GR_OK;
+}
+
+gr_status gr_trie_create(const gr_trie_view *a, gr_trie **out) {
+    if (!a || !out) return fail(GR_E_INVALID, "gr_trie_create: null argument");
+    *out = nullptr;
+    if (a->vocab_size < 2 || a->vocab_size > 32768) return fail(GR_E_INVALID, "vocab_size %d not in [2, 32768]", a->vocab_size);
+    if (a->sid_length < 1 || a->sid_length > 16) return fail(GR_E_INVALID, "sid_length %d not in [1, 16]", a->sid_length);
+    if (a->w_bm < 1 || a->w_bm > MAX_WBM) return fail(GR_E_INVALID, "w_bm %d not in [1, %d]", a->w_bm, MAX_WBM);
+    if (a->bloom_bits && (a->bloom_bits < 64 || a->bloom_bits > 65536 || (a->bloom_bits & (a->bloom_bits - 1))))
+        return fail(GR_E_INVALID, "bloom_bits %d is not 0 or a power of two in [64, 65536]", a->bloom_bits);
+    if (a->bloom_bits && (a->bloom_k < 1 || a->bloom_k > 16)) return fail(GR_E_INVALID, "bloom_k %d not in [1, 16]", a->bloom_k);
+    if (a->num_nodes < 1 || a->num_nodes > INT32_MAX) return fail(GR_E_INVALID, "num_nodes %lld out of range", (long long)a->num_nodes);
+    if (a->num_entries < 0 || a->num_entries > INT32_MAX) return fail(GR_E_INVALID, "num_entries %lld out of range", (long long)a->num_entries);
+    if (!a->node_offsets || (a->num_entries && (!a->child_nodes || !a->tokens || !a->bitmask_index)))
+        return fail(GR_E_INVALID, "gr_trie_create: null array");
+    if (a->bm_rows < 1 || !a->bitmask_table) return fail(GR_E_INVALID, "bitmask table is empty");
+    const bool bloom = a->bloom_bits != 0;
+    if (bloom && (a->bl_rows < 1 || !a->bloom_table || (a->num_entries && !a->bloom_index)))
+        return fail(GR_E_INVALID, "bloom table or index missing");
+    if (a->node_offsets[0] != 0) return fail(GR_E_INVALID, "node_offsets[0] = %d, expected 0", a->node_offsets[0]);
+    if (a->node_offsets[a->num_nodes] != a->num_entries)
+        return fail(GR_E_INVALID, "node_offsets[num_nodes] = %d, expected num_entries", a->node_offsets[a->num_nodes]);
+    for (int64_t n = 0; n < a->num_nodes; ++n) {
+        int32_t s = a->node_offsets[n], e = a->node_offsets[n + 1];
+        if (e < s) return fail(GR_E_INVALID, "node_offsets decreases at node %lld", (long long)n);
+        for (int32_t j = s; j < e; ++j) {
+            if (a->child_nodes[j] < 1 || a->child_nodes[j] >= a->num_nodes)
+                return fail(GR_E_INVALID, "child_nodes[%d] = %d out of [1, %lld)", j, a->child_nodes[j], (long long)a->num_nodes);
+            if (a->tokens[j] < 0 || a->tokens[j] >= a->vocab_size)
+                return fail(GR_E_INVALID, "tokens[%d] = %d out of [0, %d)", j, a->tokens[j], a->vocab_size);
+            if (j > s && a->tokens[j] <= a->tokens[j - 1])
+                return fail(GR_E_INVALID, "tokens of node %lld not strictly increasing at entry %d", (long long)n, j);
+            if (a->bitmask_index[j] < 0 || a->bitmask_index[j] >= a->bm_rows)
+                return fail(GR_E_INVALID, "bitmask_index[%d] = %d out of range", j, a->bitmask_index[j]);
+            if (bloom && (a->bloom_index[j] < 0 || a->bloom_index[j] >= a->bl_rows))
+                return fail(GR_E_INVALID, "bloom_index[%d] = %d out of range", j, a->bloom_index[j]);
+        }
+    }
+    gr_trie *t = new (std::nothrow) gr_trie;
+    if (!t) return fail(GR_E_NOMEM, "out of host memory");
+    TrieDev &d = t->d;
+    d.V = a->vocab_size;
+    d.L = a->sid_length;
+    d.w_bm = a->w_bm;
+    d.w_bl = a->bloom_bits / 64;
+    d.bloom_bits = a->bloom_bits;
+    d.bloom_k = bloom ? a->bloom_k : 0;
+    d.num_nodes = a->num_nodes;
+    d.num_entries = a->num_entries;
+    d.bm_rows = a->bm_rows;
+    d.bl_rows = bloom ? a->bl_rows : 0;
+    gr_status st = upload_trie(t, a->node_offsets, a->child_nodes, a->tokens, a->bitmask_index,
+                               a->bloom_index, a->bitmask_table, a->bloom_table);
+    if (st != GR_OK) {
+        delete t;
+        return st;
+    }
+    *out = t;
+    return GR_OK;
+}
+
+static void fill_sizes(const gr_trie *t, gr_trie_view *o) {
+    std::memset(o, 0, sizeof *o);
+    o->vocab_size = t->d.V;
+    o->sid_length = t->d.L;
+    o->w_bm = t->d.w_bm;
+    o->bloom_bits = t->d.bloom_bits;
+    o->bloom_k = t->d.bloom_k;
+    o->num_nodes = t->d.num_nodes;
+    o->num_entries = t->d.num_entries;
+    o->bm_rows = t->d.bm_rows;
+    o->bl_rows = t->d.bl_rows;
+}
+
+gr_status gr_trie_info(const gr_trie *t, gr_trie_view *o) {
+    if (!t || !o) return fail(GR_E_INVALID, "gr_trie_info: null argument");
+    fill_sizes(t, o);
+    return GR_OK;
+}
+
+gr_status gr_trie_host_view(const gr_trie *t, gr_trie_view *o) {
+    if (!t || !o) return fail(GR_E_INVALID, "gr_trie_host_view: null argument");
+    if (!t->has_host) return fail(GR_E_INVALID, "trie was built without keep_host");
+    fill_sizes(t, o);
+    o->node_offsets = t->h_off.data();
+    o->child_nodes = t->h_child.data();
+    o->tokens = t->h_tok.data();
+    o->bitmask_index = t->h_bmi.data();
+    o->bloom_index = t->h_bli.empty() ? nullptr : t->h_bli.data();
+    o->bitmask_table = t->h_bm.data();
+    o->bloom_table = t->h_bl.empty() ? nullptr : t->h_bl.data();
+    o->node_depth = t->h_depth.data();
+    o->node_parent = t->h_parent.data();
+    o->node_token = t->h_ntok.data();
+    return GR_OK;
+}
+
+void gr_trie_destroy(gr_trie *t) {
+    if (!t) return;
+    free_trie_dev(t);
+    delete t;
+}
+
+// ---------------------------------------------------------------------------
+// Hot path entry points
+// ---------------------------------------------------------------------------
+
+static bool dtype_ok(gr_dtype d) { return d == GR_F32 || d == GR_BF16; }
+
+static gr_status check_attn_common(const char *fn, int B, int M, int H, int d, gr_dtype dt) {
+    if (!dtype_ok(dt)) return fail(GR_E_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+    if (B < 1 || M < 1 || H < 1 || d < 1) return fail(GR_E_INVALID, "%s: non-positive shape", fn);
+    return GR_OK;
+}
+
+gr_status gr_cross_attn(const void *q, const void *k_ctx, const void *v_ctx, void *out,
+                        int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
+                        gr_dtype dtype, void *stream) {
+    gr_status st = check_attn_common("gr_cross_attn", B, M, H, d_h, dtype);
+    if (st) return st;
+    if (!q || !k_ctx || !v_ctx || !out) return fail(GR_E_INVALID, "gr_cross_attn: null pointer");
+    if (T_ctx < 1) return fail(GR_E_INVALID, "gr_cross_attn: T_ctx %d < 1", T_ctx);
+    if ((int64_t)B * M * H > INT32_MAX) return fail(GR_E_INVALID, "gr_cross_attn: too many rows");
+    if (dtype == GR_BF16 && d_h != 32 && d_h != 64 && d_h != 128)
+        return fail(GR_E_UNSUPPORTED, "gr_cross_attn: bf16 d_h %d not in {32, 64, 128}", d_h);
+    if (dtype == GR_F32 && d_h > 64)
+        return fail(GR_E_UNSUPPORTED, "gr_cross_attn: f32 d_h %d > 64", d_h);
+    hipError_t e = launch_cross_attn(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_cross_attn launch");
+    return GR_OK;
+}
+
+gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new,
+                             void *k_pool, void *v_pool, int64_t pool_blocks,
+                             int32_t *table, int64_t fresh_base, int32_t R, int32_t t,
+                             int32_t L, int32_t H, int32_t d_h, gr_dtype dtype,
+                             void *out, void *stream) {
+    gr_status st = check_attn_common("gr_self_attn_paged", 1, R, H, d_h, dtype);
+    if (st) return st;
+    if (!q || !k_new || !v_new || !k_pool || !v_pool || !table || !out)
+        return fail(GR_E_INVALID, "gr_self_attn_paged: null pointer");
+    if (L < 1 || L > 16 || t < 0 || t >= L) return fail(GR_E_INVALID, "gr_self_attn_paged: t %d / L %d invalid", t, L);
+    if (fresh_base < 0 || pool_blocks < 0 || fresh_base + R > pool_blocks || fresh_base + R > INT32_MAX)
+        return fail(GR_E_INVALID, "gr_self_attn_paged: blocks [%lld, %lld) exceed pool of %lld",
+                    (long long)fresh_base, (long long)(fresh_base + R), (long long)pool_blocks);
+    const int vec = dtype == GR_BF16 ? 4 : 2;
+    if (d_h % vec || d_h / vec > 64 || (d_h / vec & (d_h / vec - 1)))
+        return fail(GR_E_UNSUPPORTED, "gr_self_attn_paged: d_h %d unsupported for this dtype", d_h);
+    if ((int64_t)H * d_h > 64 * vec * 16)
+        return fail(GR_E_UNSUPPORTED, "gr_self_attn_paged: H*d_h %d too large", H * d_h);
+    hipError_t e = launch_self_attn(q, k_new, v_new, k_pool, v_pool, pool_blocks, table, fresh_base, R, t, L, H, d_h,
+                                    dtype, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_self_attn_paged launch");
+    return GR_OK;
+}
+
+}  // extern "C"
+
+namespace gr {
+TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    TailWsLayout l{};
+    l.cap = (int64_t)M_in * V;
+    size_t o = 0;
+    l.ubound = o; o = al(o + sizeof(float) * B);
+    l.ctr = o;    o = al(o + sizeof(uint32_t) * 4 * B);
+    l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * B);
+    l.skey = o;   o = al(o + sizeof(uint64_t) * (size_t)l.cap * B);
+    l.schild = o; o = al(o + sizeof(int32_t) * (size_t)l.cap * B);
+    l.total = o;
+    return l;
+}
+}  // namespace gr
+
+extern "C" {
+
+size_t gr_constrain_topk_workspace(int32_t B, int32_t M_in, int32_t V, int32_t k_out) {
+    (void)k_out;
+    if (B < 1 || M_in < 1 || V < 1) return 0;
+    return tail_ws_layout(B, M_in, V).total;
+}
+
+static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const char *fn) {
+    if (!trie || !a) return fail(GR_E_INVALID, "%s: null argument", fn);
+    if (trie->host_only) return fail(GR_E_INVALID, "%s: trie was built host_only", fn);
+    const TrieDev &d = trie->d;
+    if (!dtype_ok(a->dtype)) return fail(GR_E_INVALID, "%s: unknown dtype %d", fn, (int)a->dtype);
+    if (a->B < 1 || a->M_in < 1 || a->k_out < 1) return fail(GR_E_INVALID, "%s: B, M_in, k_out must be >= 1", fn);
+    if (a->V != d.V) return fail(GR_E_INVALID, "%s: V %d differs from the trie's %d", fn, a->V, d.V);
+    if (a->V > MAX_V) return fail(GR_E_UNSUPPORTED, "%s: V %d > %d", fn, a->V, MAX_V);
+    if (a->k_out > MAX_K) return fail(GR_E_UNSUPPORTED, "%s: k_out %d > %d", fn, a->k_out, MAX_K);
+    if (a->L != d.L || a->t < 0 || a->t >= a->L) return fail(GR_E_INVALID, "%s: t %d / L %d invalid for the trie", fn, a->t, a->L);
+    if ((int64_t)a->M_in * a->V > INT32_MAX) return fail(GR_E_UNSUPPORTED, "%s: M_in * V exceeds 2^31", fn);
+    if ((int64_t)a->B * a->M_in > INT32_MAX || (int64_t)a->B * a->k_out > INT32_MAX)
+        return fail(GR_E_INVALID, "%s: too many rows", fn);
+    if (!a->user_bm || !a->logits || !a->node_in || !a->acc_in || !a->parent_out || !a->token_out ||
+        !a->node_out || !a->acc_out)
+        return fail(GR_E_INVALID, "%s: null pointer", fn);
+    if (d.w_bl) {
+        if (a->n_loc < 0 || (int64_t)a->n_loc * d.bloom_k > MAX_PROBES)
+            return fail(GR_E_UNSUPPORTED, "%s: n_loc %d * bloom_k %d exceeds %d", fn, a->n_loc, d.bloom_k, MAX_PROBES);
+        if (a->n_loc > 0 && !a->user_probes) return fail(GR_E_INVALID, "%s: user_probes is NULL", fn);
+    }
+    if (a->tokens_out && a->t > 0 && !a->tokens_in) return fail(GR_E_INVALID, "%s: tokens_in is NULL", fn);
+    if (a->table_out && !a->table_in) return fail(GR_E_INVALID, "%s: table_in is NULL", fn);
+    size_t need = tail_ws_layout(a->B, a->M_in, a->V).total;
+    if (!a->ws || a->ws_bytes < need)
+        return fail(GR_E_WORKSPACE, "%s: workspace %zu bytes < %zu required", fn, a->ws_bytes, need);
+    if (((uintptr_t)a->ws & 255) != 0) return fail(GR_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+    return GR_OK;
+}
+
+gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *stream) {
+    gr_status st = check_tail(trie, a, "gr_constrain_topk");
+    if (st) return st;
+    hipError_t e = launch_constrain_topk(trie->d, *a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk launch");
+    return GR_OK;
+}
+
+gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
+    if (!trie || !s) return fail(GR_E_INVALID, "gr_decode_step: null argument");
+    const gr_tail_args &a = s->tail;
+    gr_status st = check_tail(trie, &a, "gr_decode_step");
+    if (st) return st;
+    if (!a.table_in) return fail(GR_E_INVALID, "gr_decode_step: tail.table_in is NULL");
+    // Validate everything before the first launch.
+    st = check_attn_common("gr_decode_step", a.B, a.M_in, s->H, s->d_h, a.dtype);
+    if (st) return st;
+    if (!s->k_ctx || !s->v_ctx || !s->qx || !s->q || !s->k_new || !s->v_new || !s->k_pool ||
+        !s->v_pool || !s->cross_out || !s->self_out)
+        return fail(GR_E_INVALID, "gr_decode_step: null pointer");
+    const int R = a.B * a.M_in;
+    if (s->T_ctx < 1) return fail(GR_E_INVALID, "gr_decode_step: T_ctx < 1");
+    if (a.dtype == GR_BF16 && s->d_h != 32 && s->d_h != 64 && s->d_h != 128)
+        return fail(GR_E_UNSUPPORTED, "gr_decode_step: bf16 d_h %d not in {32, 64, 128}", s->d_h);
+    if (a.dtype == GR_F32 && s->d_h > 64) return fail(GR_E_UNSUPPORTED, "gr_decode_step: f32 d_h > 64");
+    if (s->fresh_base < 0 || s->fresh_base + R > s->pool_blocks || s->fresh_base + R > INT32_MAX)
+        return fail(GR_E_INVALID, "gr_decode_step: pool of %lld blocks too small", (long long)s->pool_blocks);
+    const int vec = a.dtype == GR_BF16 ? 4 : 2;
+    if (s->d_h % vec || (int64_t)s->H * s->d_h > 64 * vec * 16)
+        return fail(GR_E_UNSUPPORTED, "gr_decode_step: H*d_h unsupported for self-attention");
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = launch_cross_attn(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
+                                     s->d_h, a.dtype, hs);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_step cross-attention launch");
+    e = launch_self_attn(s->q, s->k_new, s->v_new, s->k_pool, s->v_pool, s->pool_blocks,
+                         const_cast<int32_t *>(a.table_in),
+                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_step self-attention launch");
+    e = launch_constrain_topk(trie->d, a, hs);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");
+    return GR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// Paged short-prefix self-attention on gfx950.
+//
+// GRACE Section 5.2 (each beam row attends only to its own cached prefix:
+// the block-diagonal mask, not a causal one), Section 5.2 "kernel fusion"
+// (the kernel consumes q/k/v, writes the current token's k, v into the cache,
+// gathers the prefix and returns the output) and Section 5.3 / Section 3.3
+// (flat KV pool of one-token blocks addressed through the block table P;
+// reorder copies block ids only).  GR-Inference's CUDA-core beam attention
+// (K2) makes the same choice of plain FMA over matrix units for such short,
+// gathered sequences.
+//
+// One wavefront per beam row.  A row's H*d_h elements are spread over the 64
+// lanes in 8-byte chunks (4 bf16 or 2 fp32 per lane per chunk), so every load
+// and store of q, k, v, out and of a gathered pool block is one fully
+// coalesced wavefront access; the d_h/VEC lanes of a head reduce their dot
+// products with xor shuffles.  Positions are consumed with an online softmax,
+// so at most L <= 16 blocks are gathered once each.
+#include "gr_device.h"
+#include "gr_internal.h"
+
+namespace gr {
+namespace {
+
+struct SelfParams {
+    const void *q, *k_new, *v_new;
+    void *k_pool, *v_pool;
+    int32_t *table;
+    void *out;
+    int64_t fresh_base, pool_blocks;
+    int R, t, L, H, d, E, G;
+    float scale;
+};
+
+template <bool BF16>
+struct Chunk;
+template <>
+struct Chunk<true> {  // 4 x bf16 in 8 bytes
+    static constexpr int VEC = 4;
+    __device__ static void unpack(uint2 u, float *f) {
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    }
+    __device__ static uint2 pack(const float *f) {
+        return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    }
+};
+template <>
+struct Chunk<false> {  // 2 x fp32 in 8 bytes
+    static constexpr int VEC = 2;
+    __device__ static void unpack(uint2 u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+    }
+    __device__ static uint2 pack(const float *f) {
+        return make_uint2(__float_as_uint(f[0]), __float_as_uint(f[1]));
+    }
+};
+
+template <bool BF16, int NCH>
+__global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
+    using C = Chunk<BF16>;
+    constexpr int VEC = C::VEC;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + wave;
+    if (i >= p.R) return;
+    const int E2 = p.E / VEC;  // 8-byte chunks per row
+    const int64_t f = p.fresh_base + i;
+    const uint2 *q = (const uint2 *)p.q + (size_t)i * E2;
+    const uint2 *kn = (const uint2 *)p.k_new + (size_t)i * E2;
+    const uint2 *vn = (const uint2 *)p.v_new + (size_t)i * E2;
+    uint2 *kp = (uint2 *)p.k_pool;
+    uint2 *vp = (uint2 *)p.v_pool;
+
+    float qf[NCH][VEC], kc[NCH][VEC], vc[NCH][VEC];
+    float o[NCH][VEC], mrun[NCH], lrun[NCH];
+    bool act[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = c * 64 + lane;
+        act[c] = e < E2;
+        uint2 uq = make_uint2(0, 0), uk = uq, uv = uq;
+        if (act[c]) {
+            uq = q[e];
+            uk = kn[e];
+            uv = vn[e];
+            kp[(size_t)f * E2 + e] = uk;   // current token -> fresh block
+            vp[(size_t)f * E2 + e] = uv;
+        }
+        C::unpack(uq, qf[c]);
+        C::unpack(uk, kc[c]);
+        C::unpack(uv, vc[c]);
+        mrun[c] = -INFINITY;
+        lrun[c] = 0.0f;
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) o[c][x] = 0.0f;
+    }
+    if (lane == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
+
+    for (int j = 0; j <= p.t; ++j) {
+        float kj[NCH][VEC], vj[NCH][VEC];
+        if (j < p.t) {
+            const int32_t blk = p.table[(size_t)i * p.L + j];
+            if (blk < 0 || blk >= p.pool_blocks) continue;  // a dead row's missing past
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int e = c * 64 + lane;
+                uint2 uk = make_uint2(0, 0), uv = uk;
+                if (act[c]) {
+                    uk = kp[(size_t)blk * E2 + e];
+                    uv = vp[(size_t)blk * E2 + e];
+                }
+                C::unpack(uk, kj[c]);
+                C::unpack(uv, vj[c]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) {
+                    kj[c][x] = kc[c][x];
+                    vj[c][x] = vc[c][x];
+                }
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int x = 0; x < VEC; ++x) dot += qf[c][x] * kj[c][x];
+            for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
+            const float s = dot * p.scale;
+            const float mn = fmaxf(mrun[c], s);
+            const float alpha = __expf(mrun[c] - mn);
+            const float pe = __expf(s - mn);
+            lrun[c] = lrun[c] * alpha + pe;
+#pragma unroll
+            for (int x = 0; x < VEC; ++x) o[c][x] = o[c][x] * alpha + pe * vj[c][x];
+            mrun[c] = mn;
+        }
+    }
+    uint2 *out = (uint2 *)p.out + (size_t)i * E2;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int e = c * 64 + lane;
+        if (!act[c]) continue;
+        const float inv = 1.0f / lrun[c];
+        float r[VEC];
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) r[x] = o[c][x] * inv;
+        out[e] = C::pack(r);
+    }
+}
+
+template <bool BF16>
+hipError_t dispatch(const SelfParams &p, hipStream_t s) {
+    constexpr int VEC = Chunk<BF16>::VEC;
+    const int nch = (p.E / VEC + 63) / 64;
+    dim3 grid((p.R + 3) / 4);
+    if (nch <= 1) k_self_attn<BF16, 1><<<grid, 256, 0, s>>>(p);
+    else if (nch <= 2) k_self_attn<BF16, 2><<<grid, 256, 0, s>>>(p);
+    else if (nch <= 4) k_self_attn<BF16, 4><<<grid, 256, 0, s>>>(p);
+    else if (nch <= 8) k_self_attn<BF16, 8><<<grid, 256, 0, s>>>(p);
+    else k_self_attn<BF16, 16><<<grid, 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                            void *v_pool, int64_t pool_blocks, int32_t *table,
+                            int64_t fresh_base, int R, int t, int L, int H, int d, gr_dtype dt,
+                            void *out, hipStream_t s) {
+    SelfParams p{};
+    p.pool_blocks = pool_blocks;
+    p.q = q;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.table = table;
+    p.out = out;
+    p.fresh_base = fresh_base;
+    p.R = R;
+    p.t = t;
+    p.L = L;
+    p.H = H;
+    p.d = d;
+    p.E = H * d;
+    p.scale = 1.0f / sqrtf((float)d);
+    if (dt == GR_BF16) {
+        p.G = d / 4;
+        return dispatch<true>(p, s);
+    }
+    p.G = d / 2;
+    return dispatch<false>(p, s);
+}
+
+}  // namespace gr
