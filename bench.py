@@ -1,0 +1,438 @@
+#!/usr/bin/env python3
+"""Throughput of the wide-beam SID decode step on one MI355X.
+
+One benchmark step is one whole decode of a batch: L SID steps, each running
+beam-as-query cross-attention, paged self-attention and the CD + GTM
+constrain / log-softmax / top-k / reorder tail (GRACE Sections 3.1, 3.3, 4
+and 5), chained with the per-step beam widths of the workload.  The metric is
+beam rows per second: the beam rows of all L SID steps (R_t = B * M_t, dead
+rows included) divided by the wall time of the decode, with every input
+already resident in device memory.
+
+Inputs are seeded and synthetic (the pages' data is not public): the SID
+catalog, ads, targeting rules and requests come from ``synth.workload``; the
+per-step decoder outputs (cross-attention queries, self-attention q/k/v and
+logits) are N(0, 1) draws made on the device.  Several independent input sets
+are rotated so that the working set (well above the 256 MB MALL) is re-read
+from HBM on every decode.
+
+Output: one JSON line on stdout (logs go to stderr), with the per-step
+latency distribution, each entry point's mean duration measured with HIP
+events on the stream the kernels run on, the roofline of the dominant kernel
+and, on request, the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "beam-rows/s per decode step at B16×M1024×L4; p99 step latency; % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Setup
+# ---------------------------------------------------------------------------
+
+class Bench:
+    def __init__(self, w, seed: int, n_sets: int, stream):
+        import torch
+
+        import wide_beam_sid_amd as gr
+        from synth import workload as W
+        from wide_beam_sid_amd.runner import Decoder
+
+        self.torch, self.gr, self.W = torch, gr, W
+        self.w, self.seed, self.stream = w, seed, stream
+        dev = torch.device("cuda")
+        t0 = time.time()
+        sids = W.make_catalog(w, seed)
+        ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+        self.req = W.make_requests(w, seed)
+        log(f"[bench] workload {w.name}: {w.n_sids} SIDs, {ads.ad_sid.size} ads "
+            f"({time.time() - t0:.1f} s)")
+        t0 = time.time()
+        self.trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads],
+                                  keep_host=True)
+        self.view = self.trie.host_view()
+        log(f"[bench] trie {self.trie.info()} ({time.time() - t0:.1f} s)")
+        self.sids, self.ads = sids, ads
+        probes = (gr.bloom_probes(self.req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
+                  if w.bloom_bits else np.zeros((1, 1), np.uint32))
+        self.ubm = torch.from_numpy(self.req.user_bm.view(np.int64)).to(dev)
+        self.upr = torch.from_numpy(probes.view(np.int32)).to(dev)
+        self.dec = Decoder(self.trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype,
+                           debug=False)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.tdt = tdt
+        # Independent input sets, drawn on the device from seeded generators.
+        self.sets = []
+        for s in range(n_sets):
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed * 1000 + s)
+            ctx = [torch.randn((w.B, w.H, w.T_ctx, w.d_h), generator=g, device=dev).to(tdt)
+                   for _ in range(2)]
+            steps = []
+            for t in range(w.L):
+                R = w.rows(t)
+                inp = {k: torch.randn((R, w.H, w.d_h), generator=g, device=dev).to(tdt)
+                       for k in ("qx", "q", "k", "v")}
+                inp["logits"] = torch.randn((R, w.V), generator=g, device=dev).to(tdt)
+                steps.append(inp)
+            self.sets.append((ctx, steps))
+        torch.cuda.synchronize()
+        self.set_bytes = sum(x.numel() * x.element_size() for c, st in self.sets
+                             for x in (*c, *[v for inp in st for v in inp.values()]))
+        # Pre-built argument blocks: the timed loop is one C call per SID step.
+        self.args = [[self.dec.step_args(t, self.ubm, self.upr if w.bloom_bits else None,
+                                         w.n_loc, ctx[0], ctx[1], steps[t])
+                      for t in range(w.L)] for ctx, steps in self.sets]
+        L = gr._lib.lib()
+        self.L = L
+        self.h = self.trie.h
+        self.sp = ctypes.c_void_p(stream.cuda_stream)
+
+    # -- one whole decode (L SID steps) of input set s -----------------------
+    def decode(self, s: int):
+        for a in self.args[s]:
+            st = self.L.gr_decode_step(self.h, ctypes.byref(a), self.sp)
+            if st != 0:
+                raise RuntimeError(f"gr_decode_step: {self.L.gr_last_error().decode()}")
+
+    # -- the same decode issued entry point by entry point, with events -------
+    def decode_split(self, s: int, ev):
+        w, d = self.w, self.dec
+        ctx, steps = self.sets[s]
+        gdt = d.gr_dtype
+        out = []
+        for t in range(w.L):
+            a = self.args[s][t]
+            R = w.rows(t)
+            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(self.stream)
+            st = self.L.gr_cross_attn(a.qx, a.k_ctx, a.v_ctx, a.cross_out, w.B, d.M[t], w.H,
+                                      w.T_ctx, w.d_h, gdt, self.sp)
+            e[1].record(self.stream)
+            st |= self.L.gr_self_attn_paged(a.q, a.k_new, a.v_new, a.k_pool, a.v_pool,
+                                            a.pool_blocks, a.tail.table_in, a.fresh_base, R, t,
+                                            w.L, w.H, w.d_h, gdt, a.self_out, self.sp)
+            e[2].record(self.stream)
+            st |= self.L.gr_constrain_topk(self.h, ctypes.byref(a.tail), self.sp)
+            e[3].record(self.stream)
+            if st != 0:
+                raise RuntimeError(self.L.gr_last_error().decode())
+            out.append(e)
+        ev.append(out)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes / flops per launch (the units each kernel must touch)
+# ---------------------------------------------------------------------------
+
+def algorithmic_units(b: Bench):
+    """Per SID step t: the bytes (and flops) each entry point must move at
+    least once, from the beam state of a finished decode of input set 0."""
+    w, d, v = b.w, b.dec, b.view
+    torch = b.torch
+    es = 2 if w.dtype == "bf16" else 4
+    E = w.H * w.d_h
+    off = v["node_offsets"].astype(np.int64)
+    bmi, bli = v["bitmask_index"], v["bloom_index"]
+    bm_tab = v["bitmask_table"]
+    ubm = b.req.user_bm
+    b.decode(0)
+    torch.cuda.synchronize()
+    res = []
+    for t in range(w.L):
+        R, M, k = w.rows(t), d.M[t], w.schedule[t]
+        node = d.node[t].cpu().numpy().astype(np.int64)
+        live = node >= 0
+        # A1: q and out per row, the request's K and V once.
+        cross_b = (2 * R * E + 2 * w.B * w.H * w.T_ctx * w.d_h) * es
+        cross_f = 4 * R * w.H * w.T_ctx * w.d_h
+        # A2: q, k, v in; k, v to the pool; out; distinct prefix blocks; table.
+        tab = d.table[t].cpu().numpy()[:, :t]
+        uniq_blk = np.unique(tab[tab >= 0]).size if t else 0
+        self_b = 6 * R * E * es + 2 * uniq_blk * E * es + R * (t + 1) * 4
+        # A3-A6: logits, node/acc, user rows, CSR entries of live rows
+        # (token 2 + child 4 + two matcher ids 8 bytes), distinct matcher rows
+        # read (Bloom rows only behind a passing bitmask), the outputs and the
+        # parents' token / table rows.
+        rows = np.nonzero(live)[0]
+        s0, s1 = off[node[rows]], off[node[rows] + 1]
+        cnt = s1 - s0
+        n_ent = int(cnt.sum())
+        ent = np.repeat(s0 - np.concatenate([[0], np.cumsum(cnt)[:-1]]), cnt) + np.arange(n_ent)
+        req_of = np.repeat(rows // M, cnt)
+        bmr = bmi[ent]
+        ok = np.all((bm_tab[bmr] & ubm[req_of]) == ubm[req_of], axis=1)
+        n_bm = np.unique(bmr).size
+        n_bl = np.unique(bli[ent[ok]]).size if w.bloom_bits else 0
+        ent_bytes = 10 + (4 if w.bloom_bits else 0)
+        n_sel = int((d.parent[t].cpu().numpy() >= 0).sum())
+        tail_b = (R * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
+                  + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl
+                  + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4)
+        res.append(dict(t=t, R=R, live_in=int(live.sum()), cross_bytes=int(cross_b),
+                        cross_flops=int(cross_f), self_bytes=int(self_b),
+                        uniq_prefix_blocks=int(uniq_blk), tail_bytes=int(tail_b),
+                        csr_entries=n_ent, bitmask_pass=int(ok.sum()),
+                        bm_rows_read=int(n_bm), bloom_rows_read=int(n_bl),
+                        live_out=n_sel))
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def cpu_baseline(b: Bench, n_req: int):
+    """The oracle's decode of the first n_req requests (all L SID steps,
+    attention, masks, top-k, reorder), timed on the host; index build
+    excluded."""
+    import oracle
+    from oracle.decode import initial_state, step as oracle_step
+    W, w = b.W, b.w
+    threads = min(16, len(os.sched_getaffinity(0)))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    t0 = time.time()
+    ix = oracle.build_index(w, b.sids, b.ads)
+    log(f"[cpu] oracle index built ({time.time() - t0:.1f} s)")
+    w1 = w.scaled(B=n_req)
+    req = W.Requests(b.req.attrs[:n_req], b.req.user_bm[:n_req], b.req.locs[:n_req])
+    kc, vc = W.make_context(w, b.seed)
+    ctx = (kc[:n_req], vc[:n_req])
+    st = initial_state(w1)
+    rows = 0
+    spent = 0.0
+    for t in range(w.L):
+        full = W.make_step(w, b.seed, t)
+        R1 = w1.rows(t)
+        inp = {k: v[:R1] for k, v in full.items()}
+        t0 = time.perf_counter()
+        ref = oracle_step(w1, ix, req, ctx, t, st, inp, lambda a: W.as_float(w, a))
+        spent += time.perf_counter() - t0
+        rows += R1
+        st = ref.next_state
+        log(f"[cpu] t={t} rows={R1} cumulative {spent:.2f} s")
+    return dict(value=rows / spent, unit="beam-rows/s", cores=threads, kind="oracle",
+                sample=(f"first {n_req} of {w.B} requests, all {w.L} SID steps "
+                        f"({rows} beam rows): cross/self attention in fp64, CD+GTM masks, "
+                        f"log-softmax, top-k, reorder; index build excluded; "
+                        f"{spent:.1f} s on {cpu_model()}"),
+                seconds=spent)
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500, help="timed decodes")
+    ap.add_argument("--warmup", type=int, default=50, help="untimed decodes")
+    ap.add_argument("--workload", default="main_b16_m1024")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--sets", type=int, default=6, help="rotated input sets")
+    ap.add_argument("--split-iters", type=int, default=100,
+                    help="decodes issued per entry point for the event breakdown")
+    ap.add_argument("--cpu-requests", type=int, default=-1,
+                    help="requests in the oracle's sample (-1: the whole batch, 0: skip)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode step shards by request with no "
+              "exchange between GPUs, and this build measures one GPU's share. "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import workload as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    stream = torch.cuda.Stream()
+    b = Bench(w, args.seed, args.sets, stream)
+    rows_per_decode = w.total_rows
+    log(f"[bench] rows per decode {rows_per_decode}, {args.sets} input sets "
+        f"({b.set_bytes / 2**20:.0f} MiB)")
+
+    with torch.cuda.stream(stream):
+        units = algorithmic_units(b)
+        for u in units:
+            log(f"[bench] units {u}")
+
+        # Untimed warm-up.
+        for i in range(args.warmup):
+            b.decode(i % args.sets)
+        torch.cuda.synchronize()
+
+        # Timed region: exactly K decodes, synchronised on both sides.
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            b.decode(i % args.sets)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        log(f"[bench] timed {args.steps} decodes in {elapsed:.4f} s")
+
+        # Per-SID-step latency (events between steps, on the launch stream).
+        lat = [[] for _ in range(w.L)]
+        n_lat = max(args.steps, 1)
+        evs = []
+        for i in range(n_lat):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(w.L + 1)]
+            e[0].record(stream)
+            s = i % args.sets
+            for t in range(w.L):
+                a = b.args[s][t]
+                st = b.L.gr_decode_step(b.h, ctypes.byref(a), b.sp)
+                assert st == 0
+                e[t + 1].record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        dec_ms = []
+        for e in evs:
+            for t in range(w.L):
+                lat[t].append(e[t].elapsed_time(e[t + 1]))
+            dec_ms.append(e[0].elapsed_time(e[w.L]))
+        # Warm numbers: one input set only (its working set stays in the MALL).
+        t0w = time.perf_counter()
+        for i in range(args.steps):
+            b.decode(0)
+        torch.cuda.synchronize()
+        warm_elapsed = time.perf_counter() - t0w
+
+        # Entry-point breakdown: the same decodes issued call by call with
+        # events around each call; a spin kernel first lets the host queue
+        # run ahead so that no gap of host time sits inside an event pair.
+        split = []
+        torch.cuda._sleep(100_000_000)
+        for i in range(args.split_iters):
+            b.decode_split(i % args.sets, split)
+        torch.cuda.synchronize()
+
+        if args.copy_calib_mib:
+            n = args.copy_calib_mib * 2**20
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+
+    names = ["gr_cross_attn", "gr_self_attn_paged", "gr_constrain_topk"]
+    per = {n: [[] for _ in range(w.L)] for n in names}
+    for dec in split:
+        for t, e in enumerate(dec):
+            for j, n in enumerate(names):
+                per[n][t].append(e[j].elapsed_time(e[j + 1]))
+    mean_us = {n: [float(np.mean(per[n][t])) * 1e3 for t in range(w.L)] for n in names}
+
+    steps_tab = []
+    for t in range(w.L):
+        u = units[t]
+        x = np.array(lat[t]) * 1e3
+        steps_tab.append(dict(
+            t=t, R=u["R"], live_in=u["live_in"], p50_us=float(np.percentile(x, 50)),
+            p99_us=float(np.percentile(x, 99)),
+            rows_per_s=u["R"] / (float(np.mean(x)) * 1e-6),
+            cross_us=mean_us["gr_cross_attn"][t], self_us=mean_us["gr_self_attn_paged"][t],
+            tail_us=mean_us["gr_constrain_topk"][t],
+            cross_tflops=u["cross_flops"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e12,
+            cross_gbs=u["cross_bytes"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e9,
+            self_gbs=u["self_bytes"] / (mean_us["gr_self_attn_paged"][t] * 1e-6) / 1e9,
+            tail_gbs=u["tail_bytes"] / (mean_us["gr_constrain_topk"][t] * 1e-6) / 1e9))
+
+    # Dominant entry point: largest total time over the decode.
+    tot = {n: sum(mean_us[n]) for n in names}
+    dom = max(tot, key=tot.get)
+    wide = [t for t in range(w.L) if w.rows(t) == max(w.rows(s) for s in range(w.L))]
+    if dom == "gr_cross_attn":
+        fl = sum(units[t]["cross_flops"] for t in wide) / len(wide)
+        dur = sum(mean_us[dom][t] for t in wide) / len(wide)
+        ach = fl / (dur * 1e-6) / 1e12
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s", frac=ach / peak)
+        algo = fl
+    else:
+        key = "self_bytes" if dom == "gr_self_attn_paged" else "tail_bytes"
+        by = sum(units[t][key] for t in wide) / len(wide)
+        dur = sum(mean_us[dom][t] for t in wide) / len(wide)
+        ach = by / (dur * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS)
+        algo = by
+    roof.update(kernel=dom, steps=wide, mean_us=dur, algorithmic_per_launch=algo,
+                traffic=None)
+
+    all_steps = np.concatenate([np.array(lat[t]) for t in range(w.L)]) * 1e3
+    wide_steps = np.concatenate([np.array(lat[t]) for t in wide]) * 1e3
+    value = rows_per_decode * args.steps / elapsed
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "beam-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "beams": list(w.schedule), "L_SID": w.L,
+                   "V": w.V, "T_ctx": w.T_ctx, "heads": w.H, "head_dim": w.d_h,
+                   "n_sids": w.n_sids, "bloom_bits": w.bloom_bits, "bloom_k": w.bloom_k,
+                   "n_loc": w.n_loc, "rows_per_decode": rows_per_decode,
+                   "input_sets": args.sets, "input_set_mib": round(b.set_bytes / 2**20)},
+        "step_latency_us": {"p50": float(np.percentile(wide_steps, 50)),
+                            "p99": float(np.percentile(wide_steps, 99)),
+                            "p50_all": float(np.percentile(all_steps, 50)),
+                            "p99_all": float(np.percentile(all_steps, 99)),
+                            "decode_p50_us": float(np.percentile(dec_ms, 50)) * 1e3,
+                            "decode_p99_us": float(np.percentile(dec_ms, 99)) * 1e3},
+        "warm_value": rows_per_decode * args.steps / warm_elapsed,
+        "per_step": steps_tab,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.cpu_requests != 0:
+        n_req = w.B if args.cpu_requests < 0 else min(args.cpu_requests, w.B)
+        res["cpu_baseline"] = cpu_baseline(b, n_req)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
