@@ -75,6 +75,11 @@ typedef struct {
     int32_t keep_host;   /* 1: keep host copies of the arrays (gr_trie_view)     */
     int32_t host_only;   /* 1: keep host arrays only, no device copy (for         */
                          /* inspection; hot-path calls reject such a trie)       */
+    int32_t bloom_slice_min; /* nodes with at least this many children also get */
+                         /* a bit-sliced (column-major) copy of their children's */
+                         /* Bloom and bitmask rows, which answers eqs 5 and 8   */
+                         /* for all children at once (0: 16, -1: none); see      */
+                         /* gr_trie_view.slice_words                             */
 } gr_trie_params;
 
 /*
@@ -133,6 +138,8 @@ typedef struct {
     const int32_t *node_depth;     /* [num_nodes] (view only)                    */
     const int32_t *node_parent;    /* [num_nodes] (view only)                    */
     const int16_t *node_token;     /* [num_nodes] (view only)                    */
+    int64_t slice_words;           /* 8-byte words of bit-sliced matcher blocks   */
+                                   /* on the device (info only)                   */
 } gr_trie_view;
 
 /*
@@ -140,6 +147,8 @@ typedef struct {
  * Validates: offsets non-decreasing from 0 to num_entries, child ids in
  * [1, num_nodes), tokens in [0, V), matcher ids in range, tokens of one node
  * strictly increasing.  GR_E_INVALID names the first violation.
+ * Nodes with at least 16 children also get the bit-sliced copy described at
+ * gr_trie_params.bloom_slice_min.
  */
 gr_status gr_trie_create(const gr_trie_view *arrays, gr_trie **out);
 
@@ -226,9 +235,10 @@ gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new
  *   table_out[s, 0..t] = table_in[parent, 0..t]; other entries -1.
  * Rows with node_in < 0 (or not a node of the trie) are dead: no candidates.
  * Probe positions are taken modulo bloom_bits.
- * Limits: V <= 4096, k_out <= 1024, M_in * V < 2^31, n_loc * bloom_k <= 2048,
- * w_bm <= 64 (GR_E_UNSUPPORTED beyond).  The workspace must be 256-byte
- * aligned and at least gr_constrain_topk_workspace(B, M_in, V, k_out) bytes
+ * Limits: V <= 4096, k_out <= 1024, M_in <= 65536, M_in * V < 2^31,
+ * n_loc * (bloom_k rounded up to a multiple of 4) <= 2048, w_bm <= 64, Bloom
+ * filters of at most 32768 bits (GR_E_UNSUPPORTED beyond).
+ * The workspace must be 256-byte aligned and at least gr_constrain_topk_workspace(B, M_in, V, k_out) bytes
  * (GR_E_WORKSPACE); its contents need no initialisation.  Calls sharing a
  * workspace must be ordered (same stream).
  */

@@ -137,13 +137,14 @@ def test_self_attn_paged_parity(R, H, d, L, t, dt):
 _TRIES = {}
 
 
-def _trie_case(w, seed):
-    key = (w, seed)
+def _trie_case(w, seed, slice_min=0):
+    key = (w, seed, slice_min)
     if key not in _TRIES:
         gr = _gr()
         sids = W.make_catalog(w, seed)
         ads = W.make_ads(w, seed, W.ad_counts(w, seed))
-        trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
+        trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True,
+                             bloom_slice_min=slice_min)
         view = trie.host_view()
         ix = oracle.build_index(w, sids, ads)
         n = view["num_nodes"]
@@ -155,12 +156,12 @@ def _trie_case(w, seed):
 
 
 def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mode="normal",
-             B=None):
+             B=None, slice_min=0):
     """Run gr_constrain_topk on synthetic beam rows at depth t and check every
     output against the oracle."""
     gr = _gr()
     B = B or w.B
-    trie, view, ix, prefix = _trie_case(w, seed)
+    trie, view, ix, prefix = _trie_case(w, seed, slice_min)
     rng = np.random.default_rng(seed * 31 + M_in + t)
     R = B * M_in
     depth_nodes = np.nonzero(view["node_depth"] == t)[0]
@@ -306,3 +307,30 @@ def test_constrain_topk_workspace_error():
     with pytest.raises(gr.GrError) as e:
         gr.constrain_topk(trie, args)
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("name,seed,M_in,t", [("tiny", 0, 8, 1), ("main_50k", 1, 64, 2),
+                                              ("stress_20k", 4, 200, 1), ("long_50k", 3, 300, 2)])
+def test_constrain_topk_k_at_survivor_count(name, seed, M_in, t):
+    """k equal to the number of finite candidates, and one either side: the
+    boundary between 'every survivor is selected' and a threshold bin."""
+    w = TAIL_WORKLOADS[name]
+    o = run_tail(w, seed, M_in, 1024, t, 0.0, B=1)
+    n = int((o["parent_out"] >= 0).sum())
+    assert 2 <= n < 1024, n
+    for k in (n, n - 1, n + 1):
+        run_tail(w, seed, M_in, k, t, 0.0, B=1)
+
+
+@pytest.mark.parametrize("slice_min", [-1, 1])
+@pytest.mark.parametrize("name,seed,M_in,k_out,t", [("tiny", 1, 8, 8, 1), ("main_50k", 1, 300, 1000, 1),
+                                                   ("main_50k", 1, 700, 1024, 2),
+                                                   ("stress_20k", 4, 512, 1024, 1)])
+def test_constrain_topk_bloom_layouts(slice_min, name, seed, M_in, k_out, t):
+    """The Bloom test through staged rows only (no bit-sliced blocks) and
+    through bit-sliced blocks for every node with a child: same oracle."""
+    w = TAIL_WORKLOADS[name]
+    trie = _trie_case(w, seed, slice_min)[0]
+    info = trie.info()
+    assert (info["slice_words"] == 0) == (slice_min == -1)
+    run_tail(w, seed, M_in, k_out, t, 0.1, B=2, slice_min=slice_min)

@@ -71,14 +71,15 @@ class Trie:
     @classmethod
     def build(cls, sids: np.ndarray, vocab_size: int, w_bm: int, bloom_bits: int,
               bloom_k: int, ad_chunks, keep_host: bool = False, n_threads: int = 0,
-              host_only: bool = False) -> "Trie":
+              host_only: bool = False, bloom_slice_min: int = 0) -> "Trie":
         """Build from the catalog and an iterable of ad chunks (objects with
         ad_sid, rules, geo_offsets, geo_ids)."""
         L = _lib.lib()
         sids = np.ascontiguousarray(sids, dtype=np.int32)
         p = TrieParams(sid_length=sids.shape[1], vocab_size=vocab_size, w_bm=w_bm,
                        bloom_bits=bloom_bits, bloom_k=bloom_k, n_threads=n_threads,
-                       keep_host=int(keep_host), host_only=int(host_only))
+                       keep_host=int(keep_host), host_only=int(host_only),
+                       bloom_slice_min=bloom_slice_min)
         b = ctypes.c_void_p()
         check(L.gr_trie_builder_create(ctypes.byref(p), _ptr(sids), sids.shape[0], ctypes.byref(b)))
         try:
@@ -121,7 +122,7 @@ class Trie:
         check(_lib.lib().gr_trie_info(self.h, ctypes.byref(v)))
         return {k: getattr(v, k) for k in ("vocab_size", "sid_length", "w_bm", "bloom_bits",
                                            "bloom_k", "num_nodes", "num_entries", "bm_rows",
-                                           "bl_rows")}
+                                           "bl_rows", "slice_words")}
 
     def host_view(self) -> dict:
         """Copies of the host arrays (trie built with keep_host=True)."""

@@ -35,7 +35,7 @@ class GrError(RuntimeError):
 class TrieParams(ctypes.Structure):
     _fields_ = [("sid_length", i32), ("vocab_size", i32), ("w_bm", i32),
                 ("bloom_bits", i32), ("bloom_k", i32), ("n_threads", i32),
-                ("keep_host", i32), ("host_only", i32)]
+                ("keep_host", i32), ("host_only", i32), ("bloom_slice_min", i32)]
 
 
 class TrieView(ctypes.Structure):
@@ -45,7 +45,8 @@ class TrieView(ctypes.Structure):
                 ("node_offsets", P), ("child_nodes", P), ("tokens", P),
                 ("bitmask_index", P), ("bloom_index", P),
                 ("bitmask_table", P), ("bloom_table", P),
-                ("node_depth", P), ("node_parent", P), ("node_token", P)]
+                ("node_depth", P), ("node_parent", P), ("node_token", P),
+                ("slice_words", i64)]
 
 
 class TailArgs(ctypes.Structure):

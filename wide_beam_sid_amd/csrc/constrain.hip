@@ -23,6 +23,8 @@
 //                the k winners are sorted by (score desc, flat index asc) and
 //                the reorder writes parent / token / child node / score and
 //                the token and block-table rows of the new beams.
+#include <algorithm>
+
 #include "gr_device.h"
 #include "gr_internal.h"
 
@@ -31,9 +33,11 @@ namespace {
 
 constexpr int EXP_WAVES = 4;
 constexpr int EXP_THREADS = 64 * EXP_WAVES;
-constexpr int EXP_ROWS = 16;          // beam rows per expand workgroup
+constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 4096 bits)
+constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
+constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
-constexpr int BND_CAP = 4096;         // threshold-bin entries resolved in LDS
+constexpr int BND_CAP = 2048;         // threshold-bin entries buffered in LDS
 
 struct TailParams {
     const int32_t *off;
@@ -43,6 +47,8 @@ struct TailParams {
     const int32_t *bli;
     const uint64_t *bm_tab;
     const uint64_t *bl_tab;
+    const int64_t *nslice;      // bit-sliced Bloom block of each node (-1: none)
+    const uint64_t *slice_tab;
     int w_bm, w_bl, bloom_k, bloom_bits;
     int64_t num_nodes;
     int B, M_in, V, k_out, t, L, n_loc;
@@ -59,12 +65,20 @@ struct TailParams {
     uint64_t *dbg_mask;
     float *dbg_scores;
     float *ubound;
-    uint32_t *ctr;   // per request: [0] survivors, [1] finished workgroups,
-                     // [2] threshold bin, [3] survivors in better bins
+    uint32_t *segcnt;   // survivors of each expand workgroup [B, gx]
     uint32_t *hist;
-    uint64_t *skey;
+    uint64_t *skey;     // survivor segments [B, gx, seg_cap]
     int32_t *schild;
-    int64_t cap;
+    int64_t seg_cap;
+    int gx;
+    // expand launch shape
+    int rows_wg;        // beam rows per workgroup
+    int G, S, log2_s;   // Bloom rows staged per sub-round, lanes per row
+    int log2_wq;        // log2 of the 8-byte words per Bloom row
+    int stage_dw;       // staging dwords per wavefront
+    int mask_words;     // per-row mask words kept in LDS (debug outputs), else 0
+    int tpr, log2_tpr;  // threads per row of the log-sum-exp
+    int wmax;           // pass-vector words per row (bit-sliced rows), else 0
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -86,7 +100,6 @@ __global__ __launch_bounds__(256) void k_tail_prep(TailParams p) {
     const int b = blockIdx.x, tid = threadIdx.x;
     uint32_t *h = p.hist + (size_t)b * NBINS;
     for (int i = tid; i < NBINS; i += 256) h[i] = 0u;
-    if (tid < 4) p.ctr[b * 4 + tid] = 0u;
     float mx = -INFINITY;
     for (int m = tid; m < p.M_in; m += 256) {
         const int r = b * p.M_in + m;
@@ -100,176 +113,483 @@ __global__ __launch_bounds__(256) void k_tail_prep(TailParams p) {
 }
 
 template <bool BF16>
+__device__ __forceinline__ float logit_at(const void *logits, size_t idx) {
+    if (BF16) return bf16_to_f32(((const uint16_t *)logits)[idx]);
+    return ((const float *)logits)[idx];
+}
+
+// Running (max, sum of exp(x - max)) of one more logit.
+__device__ __forceinline__ void lse_push(float x, float &m, float &s) {
+    if (x > m) {
+        s = s * __expf(m - x) + 1.0f;
+        m = x;
+    } else {
+        s += __expf(x - m);
+    }
+}
+
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v &= __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Words w0 .. w0 + n - 1 (n <= 4) of a bit-sliced column, 16 bytes at a time
+// when the column width wc is even (the block base is 512-byte aligned).
+__device__ __forceinline__ void col_words(const uint64_t *col, int n, bool even, uint64_t w[4]) {
+    if (even) {
+        const uint4 u = *(const uint4 *)col;
+        w[0] = (uint64_t)u.x | ((uint64_t)u.y << 32);
+        w[1] = (uint64_t)u.z | ((uint64_t)u.w << 32);
+        if (n > 2) {
+            const uint4 u2 = *(const uint4 *)(col + 2);
+            w[2] = (uint64_t)u2.x | ((uint64_t)u2.y << 32);
+            w[3] = (uint64_t)u2.z | ((uint64_t)u2.w << 32);
+        }
+    } else {
+        w[0] = col[0];
+        if (n > 1) w[1] = col[1];
+        if (n > 2) w[2] = col[2];
+        if (n > 3) w[3] = col[3];
+    }
+}
+
+// Bloom test of G staged matcher rows (eq 8).  Lanes (g, s) with
+// g = lane / S: entry g's row is at stage + g * row_dw; lane s tries the
+// locations s, s + S, ...; the entry passes once any of them has all its
+// probe bits set, and its S lanes stop together.  probes holds kp positions
+// per location (a multiple of 4, padded with the location's first probe).  Returns the ballot: bit
+// g * S is set for every passing entry.
+__device__ __forceinline__ uint64_t bloom_test(const uint32_t *stage, int row_dw,
+                                               const int32_t *rowid, const uint32_t *probes,
+                                               int n_loc, int kp, int S, int sh_s,
+                                               int lane) {
+    const int g = lane >> sh_s, s = lane & (S - 1);
+    const bool act = rowid[g] >= 0;
+    const uint32_t *row = stage + g * row_dw;
+    const uint64_t gm = S == 64 ? ~0ull : ((1ull << S) - 1ull);
+    bool found = false;
+    for (int l0 = 0; l0 < n_loc; l0 += S) {
+        const int l = l0 + s;
+        if (act && !found && l < n_loc) {
+            // probes are padded to a multiple of 4 (pad = probe 0): one
+            // 16-byte read brings 4 positions, the 4 row reads are independent
+            const uint4 *pr = (const uint4 *)(probes + l * kp);
+            uint32_t all = 1u;
+            for (int q = 0; q < kp; q += 4) {
+                const uint4 pp = pr[q >> 2];
+                all &= (row[pp.x >> 5] >> (pp.x & 31u)) & (row[pp.y >> 5] >> (pp.y & 31u)) &
+                       (row[pp.z >> 5] >> (pp.z & 31u)) & (row[pp.w >> 5] >> (pp.w & 31u));
+            }
+            found = (all & 1u) != 0u;
+        }
+        const uint64_t fb = __ballot(found);
+        found = ((fb >> (g * S)) & gm) != 0ull;  // any lane of the entry
+        if (__ballot(act && !found) == 0ull) break;
+    }
+    return __ballot(found);
+}
+
+// One workgroup = up to rows_wg beam rows of one request, taken with a stride
+// of gridDim.x (row m = blockIdx.x + i * gridDim.x) so that the live rows,
+// which sit at the front of a request after a top-k, spread over the grid.
+// The CSR child entries of those rows are flattened and processed 64 at a
+// time, one entry per lane: token, child, bitmask test (eq 5); then the Bloom
+// test (eq 8) for the entries that passed.  WIDE (rows of >= 64 words): the
+// rows of up to 64 * NQ / w_bl entries are loaded into registers in one
+// round, then moved to LDS G rows at a time for the test; otherwise G rows
+// are loaded straight into LDS per sub-round.
+template <bool BF16, bool WIDE>
 __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
-    extern __shared__ float s_x[];                 // [EXP_WAVES][V] logits of the row
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];  // [mask][probes][staging]
     __shared__ uint32_t s_hist[NBINS];
     __shared__ uint64_t s_ubm[MAX_WBM];
-    __shared__ uint32_t s_probe[MAX_PROBES];
-    __shared__ uint64_t s_mask[EXP_WAVES][MAX_V / 64];
-    __shared__ int s_last;
-    __shared__ uint32_t s_scan[EXP_THREADS];
+    __shared__ int32_t s_rstart[MAX_ROWS_WG + 1];  // prefix sums of child counts
+    __shared__ int32_t s_roff[MAX_ROWS_WG];        // first CSR entry of the row's node
+    __shared__ int32_t s_rm[MAX_ROWS_WG];          // beam index m of the row
+    __shared__ float s_lse[MAX_ROWS_WG];
+    __shared__ float s_acc[MAX_ROWS_WG];
+    __shared__ int64_t s_rblk[MAX_ROWS_WG];        // bit-sliced block of the row's node
+    __shared__ uint32_t s_nsurv;                   // survivors written to the segment
+    __shared__ int s_nub;
+    __shared__ int32_t s_rowid[EXP_WAVES][64];     // Bloom row of each staged entry
 
     const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m0 = blockIdx.x * EXP_ROWS;
-    const int m1 = min(p.M_in, m0 + EXP_ROWS);
+    const int gx = gridDim.x, x = blockIdx.x;
+    const int nrows = x < p.M_in ? min(p.rows_wg, (p.M_in - x + gx - 1) / gx) : 0;
     const int V = p.V, words = (V + 63) >> 6;
-    const int nprobe = p.w_bl ? p.n_loc * p.bloom_k : 0;
+    const int kp = (p.bloom_k + 3) & ~3;   // probes per location, padded
+    const int nprobe = p.w_bl ? p.n_loc * kp : 0;
+    uint64_t *s_mask = s_dyn;
+    uint64_t *s_pass = s_dyn + (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1);
+    uint32_t *s_probe = (uint32_t *)(s_pass + (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1));
+    int16_t *s_ubit = (int16_t *)(s_probe + nprobe);   // positions of the user's bitmask bits
+    uint32_t *s_stage = s_probe + nprobe + (p.wmax ? 32 * p.w_bm : 0) + wave * p.stage_dw;
+    int32_t *rowid = s_rowid[wave];
+
     for (int i = tid; i < NBINS; i += EXP_THREADS) s_hist[i] = 0u;
     for (int i = tid; i < p.w_bm; i += EXP_THREADS) s_ubm[i] = p.user_bm[(size_t)b * p.w_bm + i];
-    for (int i = tid; i < nprobe; i += EXP_THREADS)
-        s_probe[i] = p.user_probes[(size_t)b * nprobe + i] & (uint32_t)(p.bloom_bits - 1);
+    for (int i = tid; i < nprobe; i += EXP_THREADS) {
+        const int l = i / kp, q = i - l * kp;
+        const int qs = q < p.bloom_k ? q : 0;   // pad with the location's first probe
+        s_probe[i] = p.user_probes[((size_t)b * p.n_loc + l) * p.bloom_k + qs] & (uint32_t)(p.bloom_bits - 1);
+    }
+    for (int i = tid; i < p.rows_wg * p.mask_words; i += EXP_THREADS) s_mask[i] = 0ull;
+    if (tid == 0) s_nsurv = 0u;
     const float U = p.ubound[b];
-    __syncthreads();
-
-    float *sx = s_x + wave * V;
-    uint64_t *smask = s_mask[wave];
-    const uint64_t lanemask_lt = (1ull << lane) - 1ull;
-    uint64_t *skey = p.skey + (size_t)b * p.cap;
-    int32_t *schild = p.schild + (size_t)b * p.cap;
-
-    for (int m = m0 + wave; m < m1; m += EXP_WAVES) {
-        const int r = b * p.M_in + m;
-        int node = p.node_in[r];
-        if (node >= p.num_nodes) node = -1;   // not a node of this trie: dead
-        const size_t rowoff = (size_t)r * V;
-        // Full-vocabulary log-sum-exp (the mask is applied after, eq 3).
-        float mx = -INFINITY;
-        if (BF16) {
-            const uint16_t *x = (const uint16_t *)p.logits + rowoff;
-            for (int v = lane; v < V; v += 64) {
-                float xv = bf16_to_f32(x[v]);
-                sx[v] = xv;
-                mx = fmaxf(mx, xv);
-            }
-        } else {
-            const float *x = (const float *)p.logits + rowoff;
-            for (int v = lane; v < V; v += 64) {
-                float xv = x[v];
-                sx[v] = xv;
-                mx = fmaxf(mx, xv);
-            }
+    if (p.wmax && wave == 1) {  // list the user's attribute bits (eq 5 columns)
+        const uint64_t u = lane < p.w_bm ? p.user_bm[(size_t)b * p.w_bm + lane] : 0ull;
+        const int n = __popcll(u);
+        int inc = n;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
         }
-        for (int w = lane; w < words; w += 64) smask[w] = 0ull;
-        mx = wave_max(mx);
-        wave_lds_sync();
-        float se = 0.0f;
-        for (int v = lane; v < V; v += 64) se += __expf(sx[v] - mx);
-        se = wave_sum(se);
-        const float lse = mx + __logf(se);
-        const float acc = node >= 0 ? p.acc_in[r] : -INFINITY;
-
-        if (node >= 0) {
-            const int j0 = p.off[node], j1 = p.off[node + 1];
-            for (int jb = j0; jb < j1; jb += 64) {
-                const int j = jb + lane;
-                bool pass = false;
-                uint64_t key = 0;
-                int child = 0;
-                if (j < j1) {
-                    const int v = p.tok[j];
-                    // eq 5: every user attribute bit present in the node row
-                    const uint64_t *bmr = p.bm_tab + (size_t)p.bmi[j] * p.w_bm;
-                    pass = true;
-                    for (int w = 0; w < p.w_bm; ++w) {
-                        const uint64_t u = s_ubm[w];
-                        if ((bmr[w] & u) != u) { pass = false; break; }
-                    }
-                    // eq 8: ANY user location whose probe bits are all set
-                    if (pass && p.w_bl) {
-                        const uint32_t *blr = (const uint32_t *)(p.bl_tab + (size_t)p.bli[j] * p.w_bl);
-                        bool any = false;
-                        for (int l = 0; l < p.n_loc && !any; ++l) {
-                            const uint32_t *pr = s_probe + l * p.bloom_k;
-                            bool all = true;
-                            for (int i = 0; i < p.bloom_k; ++i) {
-                                const uint32_t pos = pr[i];
-                                if (!((blr[pos >> 5] >> (pos & 31u)) & 1u)) { all = false; break; }
-                            }
-                            any = all;
-                        }
-                        pass = any;
-                    }
-                    if (pass) {
-                        const float s = acc + (sx[v] - lse);
-                        child = p.child[j];
-                        atomicOr((unsigned long long *)&smask[v >> 6], 1ull << (v & 63));
-                        atomicAdd(&s_hist[score_bin(s, U)], 1u);
-                        key = make_key(s, (uint32_t)(m * V + v));
-                    }
-                }
-                const uint64_t bal = __ballot(pass);
-                if (bal) {
-                    uint32_t base = 0;
-                    if (lane == 0) base = atomicAdd(&p.ctr[b * 4 + 0], (uint32_t)__popcll(bal));
-                    base = __shfl(base, 0, 64);
-                    if (pass) {
-                        const uint32_t idx = base + (uint32_t)__popcll(bal & lanemask_lt);
-                        skey[idx] = key;
-                        schild[idx] = child;
-                    }
-                }
-            }
+        uint64_t x = u;
+        for (int q = inc - n; x; ++q) {
+            s_ubit[q] = (int16_t)(lane * 64 + __builtin_ctzll(x));
+            x &= x - 1;
         }
-        wave_lds_sync();
-        if (p.dbg_mask)
-            for (int w = lane; w < words; w += 64) p.dbg_mask[(size_t)r * words + w] = smask[w];
-        if (p.dbg_scores)
-            for (int v = lane; v < V; v += 64) {
-                const bool kept = (smask[v >> 6] >> (v & 63)) & 1ull;
-                p.dbg_scores[rowoff + v] = kept ? acc + (sx[v] - lse) : -INFINITY;
-            }
-        wave_lds_sync();
+        if (lane == 63) s_nub = inc;
     }
 
-    // Merge this workgroup's histogram into the request's.
+    // Rows of this workgroup, their child ranges and the prefix sum of counts.
+    if (wave == 0) {
+        int cnt = 0;
+        if (lane < nrows) {
+            const int m = x + lane * gx;
+            const int r = b * p.M_in + m;
+            const int node = p.node_in[r];
+            int off0 = 0;
+            float acc = -INFINITY;
+            int64_t blk = -1;
+            if (node >= 0 && node < p.num_nodes) {  // otherwise a dead row
+                off0 = p.off[node];
+                cnt = p.off[node + 1] - off0;
+                acc = p.acc_in[r];
+                if (p.nslice) blk = p.nslice[node];
+            }
+            s_rblk[lane] = blk;
+            s_roff[lane] = off0;
+            s_rm[lane] = m;
+            s_acc[lane] = acc;
+        }
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane < nrows) s_rstart[lane + 1] = inc;
+        if (lane == 0) s_rstart[0] = 0;
+    }
     __syncthreads();
+
+    // Full-vocabulary log-sum-exp of every row with candidates (eq 3 masks
+    // log-probabilities, so the normaliser runs over all V tokens): TPR
+    // threads per row, each with a running (max, sum) over its share.
+    {
+        const int tpr = p.tpr, sh_tpr = p.log2_tpr;
+        const int i = tid >> sh_tpr, part = tid & (tpr - 1);
+        float m = -INFINITY, s = 0.0f;
+        const bool has = i < nrows && s_rstart[i + 1] > s_rstart[i];
+        if (has) {
+            const size_t rowoff = (size_t)(b * p.M_in + s_rm[i]) * V;
+            if (BF16 && (V & 3) == 0) {
+                const uint2 *x4 = (const uint2 *)((const uint16_t *)p.logits + rowoff);
+                for (int c = part; c < (V >> 2); c += tpr) {
+                    const uint2 u = x4[c];
+                    lse_push(__uint_as_float(u.x << 16), m, s);
+                    lse_push(__uint_as_float(u.x & 0xFFFF0000u), m, s);
+                    lse_push(__uint_as_float(u.y << 16), m, s);
+                    lse_push(__uint_as_float(u.y & 0xFFFF0000u), m, s);
+                }
+            } else {
+                for (int v = part; v < V; v += tpr) lse_push(logit_at<BF16>(p.logits, rowoff + v), m, s);
+            }
+        }
+        for (int o = 1; o < tpr; o <<= 1) {
+            const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+            const float mm = fmaxf(m, m2);
+            s = (m == -INFINITY ? 0.0f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.0f : s2 * __expf(m2 - mm));
+            m = mm;
+        }
+        if (i < nrows && part == 0) s_lse[i] = has ? m + __logf(s) : 0.0f;
+    }
+
+    // eqs 5 and 8 for every child of a node with a bit-sliced block, one
+    // wavefront per row.  Eq 5: AND of the columns of the user's attribute
+    // bits.  Eq 8: lane l ANDs the columns of location l's probe positions
+    // (bit j set = child j has all of them), then the lanes OR (ANY location).
+    if (p.wmax) {
+        const int nub = s_nub;
+        const int bl_pos = p.w_bl ? p.bloom_bits : 0;
+        for (int i = wave; i < nrows; i += EXP_WAVES) {
+            const int64_t blk = s_rblk[i];
+            const int c = s_rstart[i + 1] - s_rstart[i];
+            if (blk < 0 || c == 0) continue;
+            const int wc = (c + 63) >> 6;
+            const bool even = (wc & 1) == 0;
+            const uint64_t *tab = p.slice_tab + blk;
+            for (int w0 = 0; w0 < wc; w0 += 4) {
+                const int n = min(4, wc - w0);
+                uint64_t bm[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+                for (int qg = 0; qg < nub; qg += 64) {
+                    const int q = qg + lane;
+                    if (q < nub) {
+                        uint64_t cw[4];
+                        col_words(tab + (size_t)(bl_pos + s_ubit[q]) * wc + w0, n, even, cw);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (u < n) bm[u] &= cw[u];
+                    }
+                }
+                uint64_t pass[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) pass[u] = wave_and64(bm[u]);
+                if (p.w_bl) {
+                    uint64_t acc[4] = {0ull, 0ull, 0ull, 0ull};
+                    for (int lg = 0; lg < p.n_loc; lg += 64) {
+                        const int l = lg + lane;
+                        if (l < p.n_loc) {
+                            uint64_t a[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+                            const uint4 *pr = (const uint4 *)(s_probe + l * kp);
+                            for (int q = 0; q < kp; q += 4) {
+                                const uint4 pp = pr[q >> 2];
+                                const uint32_t pos[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+                                for (int t4 = 0; t4 < 4; ++t4) {
+                                    uint64_t cw[4];
+                                    col_words(tab + (size_t)pos[t4] * wc + w0, n, even, cw);
+#pragma unroll
+                                    for (int u = 0; u < 4; ++u)
+                                        if (u < n) a[u] &= cw[u];
+                                }
+                            }
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[u] |= a[u];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) pass[u] &= wave_or64(acc[u]);
+                }
+                if (lane < n) {
+                    uint64_t x = pass[0];
+#pragma unroll
+                    for (int u = 1; u < 4; ++u)
+                        if (lane == u) x = pass[u];
+                    s_pass[(size_t)i * p.wmax + w0 + lane] = x;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int n_ent = s_rstart[nrows];
+    const uint64_t lanemask_lt = (1ull << lane) - 1ull;
+    // this workgroup's survivor segment: slots come from an LDS counter
+    uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
+    int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
+    const int G = p.G, S = p.S, sh_s = p.log2_s, wq = p.w_bl, sh_wq = p.log2_wq;
+    const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
+
+    for (int c0 = wave * 64; c0 < n_ent; c0 += EXP_THREADS) {
+        const int e = c0 + lane;
+        const bool valid = e < n_ent;
+        int i = 0;
+        if (valid) {  // row of entry e: the largest i with s_rstart[i] <= e
+            int lo = 0, hi = nrows;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_rstart[mid] <= e) lo = mid;
+                else hi = mid;
+            }
+            i = lo;
+        }
+        // One round of loads for the entry, then one for what it points at.
+        int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
+        const bool sliced = valid && s_rblk[i] >= 0;
+        if (valid) {
+            j = s_roff[i] + (e - s_rstart[i]);
+            v = p.tok[j];
+            child = p.child[j];
+            if (!sliced) {
+                bmi = p.bmi[j];
+                if (wq) bli = p.bli[j];
+            }
+            m = s_rm[i];
+        }
+        bool ok = false;
+        float xv = 0.0f;
+        if (valid) {
+            xv = logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
+            if (sliced) {  // eqs 5 and 8 came from the node's bit-sliced block
+                const int jj = e - s_rstart[i];
+                ok = (s_pass[(size_t)i * p.wmax + (jj >> 6)] >> (jj & 63)) & 1ull;
+            } else {
+                // eq 5: every user attribute bit present in the node's row
+                const uint64_t *bmr = p.bm_tab + (size_t)bmi * p.w_bm;
+                ok = true;
+                for (int w = 0; w < p.w_bm; ++w) {
+                    const uint64_t u = s_ubm[w];
+                    if ((bmr[w] & u) != u) {
+                        ok = false;
+                        break;
+                    }
+                }
+            }
+        }
+        if (wq) {
+            // eq 8: ANY user location whose probe bits are all set in the row
+            // (children of a bit-sliced node already have it in ok).
+            bool bl_ok = sliced;
+            const uint64_t need = __ballot(ok && !sliced);
+            if (!need) {
+            } else if (WIDE) {
+                const int CH = (64 * NQ) >> sh_wq;   // entries per register batch
+                const int bli_m = ((need >> lane) & 1ull) ? bli : -1;
+                const uint64_t chm = CH >= 64 ? ~0ull : ((1ull << CH) - 1ull);
+                for (int b0 = 0; b0 < 64; b0 += CH) {
+                    const uint64_t grp = (need >> b0) & chm;
+                    if (!grp) continue;
+                    const int src = __shfl(bli, (b0 + lane) & 63, 64);
+                    if (lane < CH) rowid[lane] = ((grp >> lane) & 1ull) ? src : -1;
+                    wave_lds_sync();
+                    // register q holds 8-byte word ((q * 64) mod w_bl) + lane
+                    // of entry b0 + (q * 64) / w_bl
+                    uint2 r[NQ];
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        // the row id is uniform: a scalar buffer descriptor per row,
+                        // empty (loads return 0, no memory access) for a skipped entry
+                        const int g = (q << 6) >> sh_wq;
+                        const int rid = __builtin_amdgcn_readlane(bli_m, b0 + g);
+                        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                            (void *)(p.bl_tab + (size_t)(rid < 0 ? 0 : rid) * wq), (short)0,
+                            rid < 0 ? 0 : wq * 8, BUF_DWORD3);
+                        const auto u = __builtin_amdgcn_raw_buffer_load_b64(
+                            rs, lane * 8, ((q << 6) & (wq - 1)) * 8, 0);
+                        r[q] = make_uint2(u[0], u[1]);
+                    }
+                    for (int s0 = 0; s0 < CH; s0 += G) {
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) {
+                            const int g = (q << 6) >> sh_wq;
+                            if (g >= s0 && g < s0 + G) {   // zeros for a skipped entry
+                                uint32_t *dst = s_stage + 2 * lane +
+                                                ((g - s0) * row_dw + 2 * ((q << 6) & (wq - 1)));
+                                dst[0] = r[q].x;
+                                dst[1] = r[q].y;
+                            }
+                        }
+                        wave_lds_sync();
+                        const uint64_t fb = bloom_test(s_stage, row_dw, rowid + s0, s_probe, p.n_loc,
+                                                       kp, S, sh_s, lane);
+                        const int q = lane - b0 - s0;
+                        if (q >= 0 && q < G && ((fb >> (q * S)) & 1ull)) bl_ok = true;
+                        wave_lds_sync();
+                    }
+                }
+            } else {
+                for (int sr = 0; sr < 64; sr += G) {
+                    const uint64_t grp = G == 64 ? need : (need >> sr) & ((1ull << G) - 1ull);
+                    if (!grp) continue;
+                    const int src = __shfl(bli, (sr + lane) & 63, 64);
+                    if (lane < G) rowid[lane] = ((grp >> lane) & 1ull) ? src : -1;
+                    wave_lds_sync();
+                    const int nld = G << sh_wq;   // 8-byte words to stage
+                    for (int base = 0; base < nld; base += 4 * 64) {
+                        uint2 u[4];
+                        int dsto[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int idx = base + q * 64 + lane;
+                            dsto[q] = -1;
+                            if (idx < nld) {
+                                const int g = idx >> sh_wq, cw = idx & (wq - 1);
+                                const int rid = rowid[g];
+                                if (rid >= 0) {
+                                    u[q] = *(const uint2 *)(p.bl_tab + (size_t)rid * wq + cw);
+                                    dsto[q] = g * row_dw + 2 * cw;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (dsto[q] >= 0) {
+                                s_stage[dsto[q]] = u[q].x;
+                                s_stage[dsto[q] + 1] = u[q].y;
+                            }
+                    }
+                    wave_lds_sync();
+                    const uint64_t fb = bloom_test(s_stage, row_dw, rowid, s_probe, p.n_loc,
+                                                   kp, S, sh_s, lane);
+                    const int q = lane - sr;
+                    if (q >= 0 && q < G && ((fb >> (q * S)) & 1ull)) bl_ok = true;
+                    wave_lds_sync();
+                }
+            }
+            ok = ok && bl_ok;
+        }
+        float score = -INFINITY;
+        if (ok) {
+            score = s_acc[i] + (xv - s_lse[i]);
+            if (p.mask_words)
+                atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
+        }
+        const bool sel = ok && score > -INFINITY;
+        uint64_t key = 0;
+        if (sel) {
+            key = make_key(score, (uint32_t)(m * V + v));
+            atomicAdd(&s_hist[score_bin(score, U)], 1u);
+        }
+        const uint64_t bal = __ballot(sel);
+        if (bal) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
+            base = __shfl(base, 0, 64);
+            if (sel) {
+                const uint32_t idx = base + (uint32_t)__popcll(bal & lanemask_lt);
+                if (idx < (uint32_t)p.seg_cap) {
+                    skey[idx] = key;
+                    schild[idx] = child;
+                }
+            }
+        }
+    }
+
+    if (p.mask_words) {  // debug outputs: kept tokens and their scores, per row
+        __syncthreads();
+        for (int i = wave; i < nrows; i += EXP_WAVES) {
+            const size_t r = (size_t)b * p.M_in + s_rm[i];
+            const uint64_t *mk = s_mask + i * p.mask_words;
+            if (p.dbg_mask)
+                for (int w = lane; w < words; w += 64) p.dbg_mask[r * words + w] = mk[w];
+            if (p.dbg_scores)
+                for (int v = lane; v < V; v += 64) {
+                    const bool kept = (mk[v >> 6] >> (v & 63)) & 1ull;
+                    p.dbg_scores[r * V + v] =
+                        kept ? s_acc[i] + (logit_at<BF16>(p.logits, r * V + v) - s_lse[i]) : -INFINITY;
+                }
+        }
+    }
+
+    // Merge this workgroup's histogram into the request's and publish the
+    // segment's count; k_select reads both after the kernel boundary, so no
+    // device-scope fence is needed here.
+    __syncthreads();
+    if (tid == 0) p.segcnt[(size_t)b * gx + x] = min(s_nsurv, (uint32_t)p.seg_cap);
     uint32_t *gh = p.hist + (size_t)b * NBINS;
     for (int i = tid; i < NBINS; i += EXP_THREADS) {
         const uint32_t c = s_hist[i];
         if (c) atomicAdd(&gh[i], c);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&p.ctr[b * 4 + 1], 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Last workgroup of request b: threshold bin of the k_out-th best score.
-    constexpr int PER = NBINS / EXP_THREADS;
-    uint32_t c[PER];
-    uint32_t part = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = __hip_atomic_load(&gh[tid * PER + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        part += c[i];
-    }
-    s_scan[tid] = part;
-    __syncthreads();
-    for (int o = 1; o < EXP_THREADS; o <<= 1) {
-        const uint32_t v = tid >= o ? s_scan[tid - o] : 0u;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    const uint32_t total = s_scan[EXP_THREADS - 1];
-    const uint32_t excl = s_scan[tid] - part;
-    const uint32_t k = (uint32_t)p.k_out;
-    if (total <= k) {
-        if (tid == 0) {
-            p.ctr[b * 4 + 2] = NBINS;
-            p.ctr[b * 4 + 3] = total;
-        }
-    } else if (excl < k && k <= excl + part) {
-        uint32_t cum = excl;
-        for (int i = 0; i < PER; ++i) {
-            if (cum + c[i] >= k) {
-                p.ctr[b * 4 + 2] = (uint32_t)(tid * PER + i);
-                p.ctr[b * 4 + 3] = cum;
-                break;
-            }
-            cum += c[i];
-        }
     }
 }
 
@@ -303,78 +623,160 @@ __device__ __forceinline__ int next_pow2(int n) {
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
-    __shared__ uint64_t s_key[MAX_K];
-    __shared__ int32_t s_idx[MAX_K];
-    __shared__ uint64_t s_bkey[BND_CAP];
-    __shared__ int32_t s_bidx[BND_CAP];
+    __shared__ uint32_t s_seg[NBINS];     // bin starts, then (after the scatter) bin ends
+    __shared__ uint64_t s_key[MAX_K];     // winners, grouped by bin
+    __shared__ int32_t s_src[MAX_K];      // their survivor index
+    __shared__ uint64_t s_bkey[BND_CAP];  // members of the threshold bin
+    __shared__ int32_t s_bsrc[BND_CAP];
+    __shared__ uint32_t s_wsum[SEL_THREADS / 64];
     __shared__ uint32_t s_cnt[256];
-    __shared__ int s_nsel, s_nbnd, s_digit, s_rem;
+    __shared__ uint32_t s_segpre[MAX_GX + 1];  // prefix sums of the segments' survivors
+    __shared__ uint32_t s_wsum2[SEL_THREADS / 64];
+    __shared__ int s_thr, s_below, s_nbnd, s_ncol, s_digit, s_rem;
 
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const uint32_t N = p.ctr[b * 4 + 0];
-    const uint32_t thr = p.ctr[b * 4 + 2];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float U = p.ubound[b];
     const int k = p.k_out;
-    const uint64_t *keys = p.skey + (size_t)b * p.cap;
+    // survivors of request b: segment x holds segcnt[b, x] keys at
+    // keys + x * seg_cap; a survivor is named by its offset in the request
+    const int gx = p.gx;
+    const uint64_t seg_cap = (uint64_t)p.seg_cap;
+    const uint64_t *keys = p.skey + (size_t)b * gx * seg_cap;
+    {   // exclusive prefix of the segment counts (gx <= 2 * SEL_THREADS)
+        const uint32_t *cnt = p.segcnt + (size_t)b * gx;
+        const uint32_t c0 = 2 * tid < gx ? cnt[2 * tid] : 0u;
+        const uint32_t c1 = 2 * tid + 1 < gx ? cnt[2 * tid + 1] : 0u;
+        uint32_t sinc = c0 + c1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(sinc, o, 64);
+            if (lane >= o) sinc += y;
+        }
+        if (lane == 63) s_wsum2[wave] = sinc;
+        __syncthreads();
+        uint32_t spre = 0;
+        for (int w = 0; w < wave; ++w) spre += s_wsum2[w];
+        const uint32_t ex = spre + sinc - c0 - c1;
+        if (2 * tid <= gx) s_segpre[2 * tid] = ex;
+        if (2 * tid + 1 <= gx) s_segpre[2 * tid + 1] = ex + c0;
+    }
+    const uint32_t *gh = p.hist + (size_t)b * NBINS;
+
+    // 1. Exclusive prefix of the score histogram; the threshold bin is the
+    //    one that holds the k-th best survivor.
+    constexpr int PER = NBINS / SEL_THREADS;
+    uint32_t c[PER];
+    uint32_t part = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = gh[tid * PER + i];
+        part += c[i];
+    }
+    uint32_t inc = part;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
     if (tid == 0) {
-        s_nsel = 0;
+        s_thr = NBINS;
         s_nbnd = 0;
+        s_ncol = 0;
     }
     __syncthreads();
-    for (uint32_t i = tid; i < N; i += SEL_THREADS) {
-        const uint64_t key = keys[i];
-        const int bin = thr >= (uint32_t)NBINS ? 0 : score_bin(key_score(key), U);
-        if (thr >= (uint32_t)NBINS || bin < (int)thr) {
-            const int pos = atomicAdd(&s_nsel, 1);
-            s_key[pos] = key;
-            s_idx[pos] = (int32_t)i;
-        } else if (bin == (int)thr) {
-            const int pos = atomicAdd(&s_nbnd, 1);
-            if (pos < BND_CAP) {
-                s_bkey[pos] = key;
-                s_bidx[pos] = (int32_t)i;
+    uint32_t pre = 0, total = 0;
+    for (int w = 0; w < SEL_THREADS / 64; ++w) {
+        const uint32_t x = s_wsum[w];
+        pre += w < wave ? x : 0u;
+        total += x;
+    }
+    uint32_t cum = pre + inc - part;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        s_seg[tid * PER + i] = cum;
+        if (total > (uint32_t)k && cum < (uint32_t)k && (uint32_t)k <= cum + c[i]) {
+            s_thr = tid * PER + i;
+            s_below = (int)cum;
+        }
+        cum += c[i];
+    }
+    if (tid == 0 && total <= (uint32_t)k) s_below = (int)total;
+    __syncthreads();
+    const int thr = s_thr, below = s_below;
+    const uint32_t n_surv = s_segpre[gx];
+    // offset of the f-th survivor (segments concatenated) in the request's keys
+    auto surv = [&](uint32_t f) -> uint32_t {
+        int lo = 0, hi = gx;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_segpre[mid] <= f) lo = mid;
+            else hi = mid;
+        }
+        return (uint32_t)(lo * seg_cap) + (f - s_segpre[lo]);
+    };
+
+    // 2. Survivors of bins below the threshold go to their bin's segment;
+    //    members of the threshold bin are buffered.
+    for (uint32_t f0 = 0; f0 < n_surv; f0 += 4 * SEL_THREADS) {
+        uint32_t src[4];
+        uint64_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {   // 4 loads in flight per thread
+            const uint32_t f = f0 + u * SEL_THREADS + tid;
+            src[u] = f < n_surv ? surv(f) : 0xFFFFFFFFu;
+            kk[u] = f < n_surv ? keys[src[u]] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (src[u] == 0xFFFFFFFFu) continue;
+            const uint64_t key = kk[u];
+            const int bin = score_bin(key_score(key), U);
+            if (bin < thr) {
+                const uint32_t pos = atomicAdd(&s_seg[bin], 1u);
+                if (pos < (uint32_t)MAX_K) {
+                    s_key[pos] = key;
+                    s_src[pos] = (int32_t)src[u];
+                }
+            } else if (bin == thr) {
+                const int pos = atomicAdd(&s_nbnd, 1);
+                if (pos < BND_CAP) {
+                    s_bkey[pos] = key;
+                    s_bsrc[pos] = (int32_t)src[u];
+                }
             }
         }
     }
     __syncthreads();
-    int nsel = s_nsel;
-    if (thr < (uint32_t)NBINS) {
-        const int need = k - nsel;
-        const int nb = s_nbnd;
-        if (nb <= BND_CAP) {
-            const int n2 = next_pow2(nb);
-            for (int i = nb + tid; i < n2; i += SEL_THREADS) {
-                s_bkey[i] = 0ull;
-                s_bidx[i] = -1;
-            }
-            __syncthreads();
-            bitonic_desc(s_bkey, s_bidx, n2);
-            for (int i = tid; i < need; i += SEL_THREADS) {
-                s_key[nsel + i] = s_bkey[i];
-                s_idx[nsel + i] = s_bidx[i];
-            }
-        } else {
-            // MSB-first radix select of the need-th best key of the bin.
+
+    // 3. The best k - below members of the threshold bin fill slots below..k-1.
+    int n_sel = below;
+    if (thr < NBINS) {
+        const int need = k - below;
+        int nb = s_nbnd;
+        if (nb > BND_CAP) {
+            // Too many to buffer: MSB-first radix select of the need-th best
+            // key of the bin over global memory, then collect the winners.
             uint64_t prefix = 0, pmask = 0;
             int rem = need;
             for (int shift = 56; shift >= 0; shift -= 8) {
                 for (int i = tid; i < 256; i += SEL_THREADS) s_cnt[i] = 0u;
                 __syncthreads();
-                for (uint32_t i = tid; i < N; i += SEL_THREADS) {
-                    const uint64_t key = keys[i];
-                    if (score_bin(key_score(key), U) == (int)thr && (key & pmask) == prefix)
+                for (uint32_t f = tid; f < n_surv; f += SEL_THREADS) {
+                    const uint64_t key = keys[surv(f)];
+                    if (score_bin(key_score(key), U) == thr && (key & pmask) == prefix)
                         atomicAdd(&s_cnt[(key >> shift) & 255u], 1u);
                 }
                 __syncthreads();
                 if (tid == 0) {
-                    uint32_t cum = 0;
+                    uint32_t acc = 0;
                     for (int d = 255; d >= 0; --d) {
-                        if (cum + s_cnt[d] >= (uint32_t)rem) {
+                        if (acc + s_cnt[d] >= (uint32_t)rem) {
                             s_digit = d;
-                            s_rem = rem - (int)cum;
+                            s_rem = rem - (int)acc;
                             break;
                         }
-                        cum += s_cnt[d];
+                        acc += s_cnt[d];
                     }
                 }
                 __syncthreads();
@@ -383,55 +785,89 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
                 rem = s_rem;
                 __syncthreads();
             }
-            for (uint32_t i = tid; i < N; i += SEL_THREADS) {
+            for (uint32_t f = tid; f < n_surv; f += SEL_THREADS) {
+                const uint32_t i = surv(f);
                 const uint64_t key = keys[i];
-                if (score_bin(key_score(key), U) == (int)thr && key >= prefix) {
-                    const int pos = atomicAdd(&s_nsel, 1);
-                    s_key[pos] = key;
-                    s_idx[pos] = (int32_t)i;
+                if (score_bin(key_score(key), U) == thr && key >= prefix) {
+                    const int pos = atomicAdd(&s_ncol, 1);
+                    if (pos < BND_CAP) {
+                        s_bkey[pos] = key;
+                        s_bsrc[pos] = (int32_t)i;
+                    }
                 }
             }
+            __syncthreads();
+            nb = min(s_ncol, need);
         }
-        nsel = k;
+        if (nb <= 256) {
+            // rank by counting: keys are distinct (the flat index is part of it)
+            for (int q = tid; q < nb; q += SEL_THREADS) {
+                const uint64_t kq = s_bkey[q];
+                int r = 0;
+                for (int o = 0; o < nb; ++o) r += s_bkey[o] > kq;
+                if (r < need) {
+                    s_key[below + r] = kq;
+                    s_src[below + r] = s_bsrc[q];
+                }
+            }
+        } else {
+            const int n2 = next_pow2(nb);
+            for (int i = nb + tid; i < n2; i += SEL_THREADS) {
+                s_bkey[i] = 0ull;
+                s_bsrc[i] = -1;
+            }
+            __syncthreads();
+            bitonic_desc(s_bkey, s_bsrc, n2);
+            for (int i = tid; i < need; i += SEL_THREADS) {
+                s_key[below + i] = s_bkey[i];
+                s_src[below + i] = s_bsrc[i];
+            }
+        }
+        n_sel = k;
     }
     __syncthreads();
-    const int n = nsel < k ? nsel : k;
-    const int n2 = next_pow2(n > 0 ? n : 1);
-    for (int i = n + tid; i < n2; i += SEL_THREADS) {
-        s_key[i] = 0ull;
-        s_idx[i] = -1;
-    }
-    __syncthreads();
-    bitonic_desc(s_key, s_idx, n2);
 
+    // 4. Output.  A winner of a bin below the threshold takes slot
+    //    (start of its bin) + (number of better keys in its bin); the
+    //    threshold-bin winners are already in order.  Slots past n_sel are dead.
     const int V = p.V, L = p.L, t = p.t;
-    for (int j = tid; j < k; j += SEL_THREADS) {
-        const size_t slot = (size_t)b * k + j;
-        if (j < n) {
-            const uint64_t key = s_key[j];
+    for (int pos = tid; pos < k; pos += SEL_THREADS) {
+        const size_t base = (size_t)b * k;
+        if (pos < n_sel) {
+            const uint64_t key = s_key[pos];
+            int slot = pos;
+            if (pos < below) {
+                const int bin = score_bin(key_score(key), U);
+                const int end = (int)s_seg[bin], start = bin ? (int)s_seg[bin - 1] : 0;
+                int r = 0;
+                for (int q = start; q < end; ++q) r += s_key[q] > key;
+                slot = start + r;
+            }
+            const size_t sl = base + slot;
             const uint32_t f = key_flat(key);
             const int m = (int)(f / (uint32_t)V), v = (int)(f % (uint32_t)V);
             const int parent = b * p.M_in + m;
-            p.parent_out[slot] = parent;
-            p.token_out[slot] = v;
-            p.node_out[slot] = p.schild[(size_t)b * p.cap + s_idx[j]];
-            p.acc_out[slot] = key_score(key);
+            p.parent_out[sl] = parent;
+            p.token_out[sl] = v;
+            p.node_out[sl] = p.schild[(size_t)b * gx * seg_cap + (uint32_t)s_src[pos]];
+            p.acc_out[sl] = key_score(key);
             if (p.tokens_out)
                 for (int l = 0; l < L; ++l)
-                    p.tokens_out[slot * L + l] =
+                    p.tokens_out[sl * L + l] =
                         l < t ? p.tokens_in[(size_t)parent * L + l] : (l == t ? v : -1);
             if (p.table_out)
                 for (int l = 0; l < L; ++l)
-                    p.table_out[slot * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
+                    p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
         } else {
-            p.parent_out[slot] = -1;
-            p.token_out[slot] = -1;
-            p.node_out[slot] = -1;
-            p.acc_out[slot] = -INFINITY;
+            const size_t sl = base + pos;
+            p.parent_out[sl] = -1;
+            p.token_out[sl] = -1;
+            p.node_out[sl] = -1;
+            p.acc_out[sl] = -INFINITY;
             if (p.tokens_out)
-                for (int l = 0; l < L; ++l) p.tokens_out[slot * L + l] = -1;
+                for (int l = 0; l < L; ++l) p.tokens_out[sl * L + l] = -1;
             if (p.table_out)
-                for (int l = 0; l < L; ++l) p.table_out[slot * L + l] = -1;
+                for (int l = 0; l < L; ++l) p.table_out[sl * L + l] = -1;
         }
     }
 }
@@ -447,6 +883,8 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipSt
     p.bli = tr.bloom_index;
     p.bm_tab = tr.bitmask_table;
     p.bl_tab = tr.bloom_table;
+    p.nslice = tr.node_slice;
+    p.slice_tab = tr.slice_table;
     p.w_bm = tr.w_bm;
     p.w_bl = tr.w_bl;
     p.bloom_k = tr.bloom_k;
@@ -477,19 +915,52 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipSt
     const TailWsLayout ly = tail_ws_layout(a.B, a.M_in, a.V);
     char *ws = (char *)a.ws;
     p.ubound = (float *)(ws + ly.ubound);
-    p.ctr = (uint32_t *)(ws + ly.ctr);
+    p.segcnt = (uint32_t *)(ws + ly.segcnt);
     p.hist = (uint32_t *)(ws + ly.hist);
     p.skey = (uint64_t *)(ws + ly.skey);
     p.schild = (int32_t *)(ws + ly.schild);
-    p.cap = ly.cap;
+    p.seg_cap = ly.shape.seg_cap;
+    p.gx = ly.shape.gx;
+
+    p.rows_wg = ly.shape.rows_wg;
+    const int gx = ly.shape.gx;
+    int log2_wq = 0;
+    while ((1 << log2_wq) < tr.w_bl) ++log2_wq;
+    p.log2_wq = log2_wq;
+    const int row_bytes = (2 * tr.w_bl + 1) * 4;
+    int G = 64;
+    while (G > 1 && G * row_bytes > STAGE_BYTES) G >>= 1;
+    p.G = G;
+    p.S = 64 / G;
+    int log2_s = 0;
+    while ((1 << log2_s) < p.S) ++log2_s;
+    p.log2_s = log2_s;
+    p.stage_dw = tr.w_bl ? G * (2 * tr.w_bl + 1) : 0;
+    p.mask_words = (a.dbg_mask || a.dbg_scores) ? (a.V + 63) / 64 : 0;
+    p.wmax = tr.node_slice ? (a.V + 63) / 64 : 0;
+    const int nprobe = tr.w_bl ? p.n_loc * ((tr.bloom_k + 3) & ~3) : 0;
+    const size_t shm = sizeof(uint64_t) * (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1) +
+                       sizeof(uint64_t) * (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1) +
+                       sizeof(uint32_t) * ((size_t)nprobe + (p.wmax ? 32 * (size_t)tr.w_bm : 0) +
+                                           (size_t)EXP_WAVES * p.stage_dw);
+
+    int tpr = 64;
+    while (tpr > 1 && tpr * p.rows_wg > EXP_THREADS) tpr >>= 1;
+    p.tpr = tpr;
+    int log2_tpr = 0;
+    while ((1 << log2_tpr) < tpr) ++log2_tpr;
+    p.log2_tpr = log2_tpr;
 
     k_tail_prep<<<a.B, 256, 0, s>>>(p);
-    dim3 g1((a.M_in + EXP_ROWS - 1) / EXP_ROWS, a.B);
-    const size_t shm = sizeof(float) * EXP_WAVES * a.V;
-    if (a.dtype == GR_BF16)
-        k_expand<true><<<g1, EXP_THREADS, shm, s>>>(p);
-    else
-        k_expand<false><<<g1, EXP_THREADS, shm, s>>>(p);
+    dim3 g1(gx, a.B);
+    const bool wide = tr.w_bl >= 64;
+    if (a.dtype == GR_BF16) {
+        if (wide) k_expand<true, true><<<g1, EXP_THREADS, shm, s>>>(p);
+        else k_expand<true, false><<<g1, EXP_THREADS, shm, s>>>(p);
+    } else {
+        if (wide) k_expand<false, true><<<g1, EXP_THREADS, shm, s>>>(p);
+        else k_expand<false, false><<<g1, EXP_THREADS, shm, s>>>(p);
+    }
     k_select<<<a.B, SEL_THREADS, 0, s>>>(p);
     return hipGetLastError();
 }

@@ -204,6 +204,8 @@ gr_status gr_trie_builder_create(const gr_trie_params *params, const int32_t *si
         if (p.bloom_k < 1 || p.bloom_k > 16)
             return fail(GR_E_INVALID, "bloom_k %d not in [1, 16]", p.bloom_k);
     }
+    if (p.bloom_slice_min < -1)
+        return fail(GR_E_INVALID, "bloom_slice_min %d is not -1, 0 or a child count", p.bloom_slice_min);
     if (n_sids < 1 || n_sids > (int64_t)1 << 30)
         return fail(GR_E_INVALID, "n_sids %lld not in [1, 2^30]", (long long)n_sids);
     int bpt = 1;
@@ -345,12 +347,81 @@ static void free_trie_dev(gr_trie *t) {
     hipFree((void *)t->d.bloom_index);
     hipFree((void *)t->d.bitmask_table);
     hipFree((void *)t->d.bloom_table);
+    hipFree((void *)t->d.node_slice);
+    hipFree((void *)t->d.slice_table);
     t->d = TrieDev{};
+}
+
+// Bit-sliced matcher blocks (a column-major copy of the children's rows).
+// A node with c >= min_c child entries gets a block of Wc = ceil(c / 64)
+// words per matcher bit position: first bloom_bits positions of the Bloom
+// rows (if any), then 64 * w_bm positions of the bitmask rows.  Word
+// pos * Wc + (j >> 6) has bit j & 63 set iff bit pos of child entry j's row
+// is set.  One block answers eqs 5 and 8 for all of a node's children at
+// once: AND the columns of the user's bitmask bits, AND the columns of a
+// location's probe positions and OR over locations.  The total is kept
+// under MAX_SLICE_WORDS by raising min_c.
+constexpr int DEFAULT_SLICE_MIN = 16;
+constexpr int64_t MAX_SLICE_WORDS = (int64_t)4 << 30;  // 32 GiB
+
+static void build_slices(int64_t num_nodes, const int32_t *off, const int32_t *bmi,
+                         const uint64_t *bm, int w_bm, const int32_t *bli, const uint64_t *bl,
+                         int w_bl, int bloom_bits, int min_c, int threads,
+                         std::vector<int64_t> &node_slice, std::vector<uint64_t> &tab) {
+    const int64_t npos = (int64_t)(w_bl ? bloom_bits : 0) + 64 * w_bm;
+    node_slice.assign((size_t)num_nodes, -1);
+    int64_t total = 0;
+    for (;;) {
+        total = 0;
+        for (int64_t n = 0; n < num_nodes; ++n) {
+            const int c = off[n + 1] - off[n];
+            if (c >= min_c) total += npos * ((c + 63) / 64);
+        }
+        if (total <= MAX_SLICE_WORDS) break;
+        min_c *= 2;
+    }
+    total = 0;
+    for (int64_t n = 0; n < num_nodes; ++n) {
+        const int c = off[n + 1] - off[n];
+        if (c >= min_c) {
+            node_slice[n] = total;
+            total += npos * ((c + 63) / 64);
+        }
+    }
+    tab.assign((size_t)total, 0ull);
+    int64_t *ns = node_slice.data();
+    uint64_t *tb = tab.data();
+    const int bl_pos = w_bl ? bloom_bits : 0;
+    parallel_for(num_nodes, threads, [&](int64_t n0, int64_t n1) {
+        auto scatter = [](uint64_t *blk, int64_t wc, int j, const uint64_t *row, int words) {
+            const uint64_t bit = 1ull << (j & 63);
+            for (int w = 0; w < words; ++w) {
+                uint64_t word = row[w];
+                while (word) {
+                    const int b = __builtin_ctzll(word);
+                    blk[(int64_t)(w * 64 + b) * wc + (j >> 6)] |= bit;
+                    word &= word - 1;
+                }
+            }
+        };
+        for (int64_t n = n0; n < n1; ++n) {
+            if (ns[n] < 0) continue;
+            const int c = off[n + 1] - off[n];
+            const int64_t wc = (c + 63) / 64;
+            uint64_t *blk = tb + ns[n];
+            for (int j = 0; j < c; ++j) {
+                const int32_t e = off[n] + j;
+                if (w_bl) scatter(blk, wc, j, bl + (size_t)bli[e] * w_bl, w_bl);
+                scatter(blk + (int64_t)bl_pos * wc, wc, j, bm + (size_t)bmi[e] * w_bm, w_bm);
+            }
+        }
+    });
 }
 
 static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *child,
                              const int16_t *tok, const int32_t *bmi, const int32_t *bli,
-                             const uint64_t *bm, const uint64_t *bl) {
+                             const uint64_t *bm, const uint64_t *bl, int slice_min,
+                             int threads) {
     hipError_t e;
     int32_t *d_off, *d_child, *d_bmi, *d_bli = nullptr;
     int16_t *d_tok;
@@ -372,6 +443,26 @@ static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *chil
         d.bloom_index = d_bli;
         if ((e = upload(&d_bl, bl, (size_t)d.bl_rows * d.w_bl)) != hipSuccess) goto err;
         d.bloom_table = d_bl;
+    }
+    if (slice_min >= 0) {
+        std::vector<int64_t> ns;
+        std::vector<uint64_t> tab;
+        try {
+            build_slices(d.num_nodes, off, bmi, bm, d.w_bm, bli, bl, d.w_bl, d.bloom_bits,
+                         slice_min ? slice_min : DEFAULT_SLICE_MIN, threads, ns, tab);
+        } catch (const std::bad_alloc &) {
+            free_trie_dev(t);
+            return fail(GR_E_NOMEM, "out of host memory building bit-sliced matcher blocks");
+        }
+        if (!tab.empty()) {
+            int64_t *d_ns;
+            uint64_t *d_tab;
+            if ((e = upload(&d_ns, ns.data(), ns.size())) != hipSuccess) goto err;
+            d.node_slice = d_ns;
+            if ((e = upload(&d_tab, tab.data(), tab.size())) != hipSuccess) goto err;
+            d.slice_table = d_tab;
+            d.slice_words = (int64_t)tab.size();
+        }
     }
     return GR_OK;
 err:
@@ -512,7 +603,7 @@ gr_status gr_trie_builder_finish(gr_trie_builder *b, gr_trie **out) {
         if (!t->host_only)
             st = upload_trie(t, off.data(), child.data(), tok.data(), bmi.data(),
                              wbl ? bli.data() : nullptr, b->leaf_bm.data(),
-                             wbl ? b->leaf_bl.data() : nullptr);
+                             wbl ? b->leaf_bl.data() : nullptr, b->p.bloom_slice_min, b->threads);
         if (st == GR_OK && (b->p.keep_host || t->host_only)) {
             t->has_host = true;
             t->h_off.swap(off);
@@ -589,7 +680,7 @@ gr_status gr_trie_create(const gr_trie_view *a, gr_trie **out) {
     d.bm_rows = a->bm_rows;
     d.bl_rows = bloom ? a->bl_rows : 0;
     gr_status st = upload_trie(t, a->node_offsets, a->child_nodes, a->tokens, a->bitmask_index,
-                               a->bloom_index, a->bitmask_table, a->bloom_table);
+                               a->bloom_index, a->bitmask_table, a->bloom_table, 0, hw_threads(0));
     if (st != GR_OK) {
         delete t;
         return st;
@@ -609,6 +700,7 @@ static void fill_sizes(const gr_trie *t, gr_trie_view *o) {
     o->num_entries = t->d.num_entries;
     o->bm_rows = t->d.bm_rows;
     o->bl_rows = t->d.bl_rows;
+    o->slice_words = t->d.slice_words;
 }
 
 gr_status gr_trie_info(const gr_trie *t, gr_trie_view *o) {
@@ -699,13 +791,15 @@ namespace gr {
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     TailWsLayout l{};
-    l.cap = (int64_t)M_in * V;
+    l.shape = tail_shape(B, M_in, V);
+    const size_t nseg = (size_t)B * l.shape.gx;
+    const size_t nsurv = nseg * (size_t)l.shape.seg_cap;
     size_t o = 0;
     l.ubound = o; o = al(o + sizeof(float) * B);
-    l.ctr = o;    o = al(o + sizeof(uint32_t) * 4 * B);
+    l.segcnt = o; o = al(o + sizeof(uint32_t) * nseg);
     l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * B);
-    l.skey = o;   o = al(o + sizeof(uint64_t) * (size_t)l.cap * B);
-    l.schild = o; o = al(o + sizeof(int32_t) * (size_t)l.cap * B);
+    l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);
+    l.schild = o; o = al(o + sizeof(int32_t) * nsurv);
     l.total = o;
     return l;
 }
@@ -730,14 +824,18 @@ static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const ch
     if (a->k_out > MAX_K) return fail(GR_E_UNSUPPORTED, "%s: k_out %d > %d", fn, a->k_out, MAX_K);
     if (a->L != d.L || a->t < 0 || a->t >= a->L) return fail(GR_E_INVALID, "%s: t %d / L %d invalid for the trie", fn, a->t, a->L);
     if ((int64_t)a->M_in * a->V > INT32_MAX) return fail(GR_E_UNSUPPORTED, "%s: M_in * V exceeds 2^31", fn);
+    if (a->M_in > MAX_M_IN) return fail(GR_E_UNSUPPORTED, "%s: M_in %d > %d", fn, a->M_in, MAX_M_IN);
     if ((int64_t)a->B * a->M_in > INT32_MAX || (int64_t)a->B * a->k_out > INT32_MAX)
         return fail(GR_E_INVALID, "%s: too many rows", fn);
     if (!a->user_bm || !a->logits || !a->node_in || !a->acc_in || !a->parent_out || !a->token_out ||
         !a->node_out || !a->acc_out)
         return fail(GR_E_INVALID, "%s: null pointer", fn);
+    if (d.bloom_bits > 32768)
+        return fail(GR_E_UNSUPPORTED, "%s: Bloom filters of %d bits exceed the 32768 the tail stages in LDS", fn, d.bloom_bits);
     if (d.w_bl) {
-        if (a->n_loc < 0 || (int64_t)a->n_loc * d.bloom_k > MAX_PROBES)
-            return fail(GR_E_UNSUPPORTED, "%s: n_loc %d * bloom_k %d exceeds %d", fn, a->n_loc, d.bloom_k, MAX_PROBES);
+        if (a->n_loc < 0 || (int64_t)a->n_loc * ((d.bloom_k + 3) & ~3) > MAX_PROBES)
+            return fail(GR_E_UNSUPPORTED, "%s: n_loc %d * bloom_k %d (rounded up to a multiple of 4) exceeds %d",
+                        fn, a->n_loc, d.bloom_k, MAX_PROBES);
         if (a->n_loc > 0 && !a->user_probes) return fail(GR_E_INVALID, "%s: user_probes is NULL", fn);
     }
     if (a->tokens_out && a->t > 0 && !a->tokens_in) return fail(GR_E_INVALID, "%s: tokens_in is NULL", fn);

@@ -21,21 +21,53 @@ struct TrieDev {
     const int32_t *bloom_index;
     const uint64_t *bitmask_table;
     const uint64_t *bloom_table;
+    // Bit-sliced matcher blocks of wide nodes: node_slice[n] is the word
+    // offset of node n's block in slice_table (-1: none).  The block holds,
+    // for each matcher bit position pos (bloom_bits Bloom positions if there
+    // is a Bloom matcher, then 64 * w_bm bitmask positions), ceil(c / 64)
+    // words whose bit j is bit pos of the row of the node's j-th child entry.
+    const int64_t *node_slice;
+    const uint64_t *slice_table;
+    int64_t slice_words;
 };
 
 // Score histogram of the top-k pre-selection: NBINS bins of width
 // 1 / BIN_SCALE nats below the best parent score of the request.
-constexpr int NBINS = 4096;
-constexpr float BIN_SCALE = 64.0f;
+constexpr int NBINS = 2048;
+constexpr float BIN_SCALE = 32.0f;
 constexpr int MAX_V = 4096;          // vocabulary limit of the tail kernels
 constexpr int MAX_K = 1024;          // top-k width limit (one slot per thread)
 constexpr int MAX_PROBES = 2048;     // n_loc * bloom_k staged in LDS
 constexpr int MAX_WBM = 64;
 
+constexpr int MAX_ROWS_WG = 32;      // beam rows per expand workgroup (upper bound)
+
+// Launch shape of the expand kernel: workgroup x of request b takes rows
+// m = x + i * gx (i < rows_wg) and owns a survivor segment of seg_cap
+// entries (a row has at most V children), so no segment can overflow.
+struct TailShape {
+    int rows_wg, gx;
+    int64_t seg_cap;
+};
+constexpr int MAX_M_IN = 65536;      // beam rows per request entering the tail
+constexpr int MAX_GX = 2048;         // expand workgroups per request
+inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
+    const int64_t R = (int64_t)B * M_in;
+    int64_t rw = R / 1024;
+    const int64_t rw_min = ((int64_t)M_in + MAX_GX - 1) / MAX_GX;   // keeps gx <= MAX_GX
+    if (rw < rw_min) rw = rw_min;
+    rw = rw < 1 ? 1 : (rw > MAX_ROWS_WG ? MAX_ROWS_WG : rw);
+    TailShape t;
+    t.rows_wg = (int)rw;
+    t.gx = (int)((M_in + rw - 1) / rw);
+    t.seg_cap = rw * V;
+    return t;
+}
+
 // Workspace carving of gr_constrain_topk (byte offsets).
 struct TailWsLayout {
-    size_t ubound, ctr, hist, skey, schild, total;
-    int64_t cap;  // survivor capacity per request
+    size_t ubound, segcnt, hist, skey, schild, total;
+    TailShape shape;
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
 
