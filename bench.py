@@ -171,7 +171,7 @@ def algorithmic_units(b: Bench):
         tab = d.table[t].cpu().numpy()[:, :t]
         uniq_blk = np.unique(tab[tab >= 0]).size if t else 0
         self_b = 6 * R * E * es + 2 * uniq_blk * E * es + R * (t + 1) * 4
-        # A3-A6: logits, node/acc, user rows, CSR entries of live rows
+        # A3-A6: logits of live rows, node/acc, user rows, CSR entries of live rows
         # (token 2 + child 4 + two matcher ids 8 bytes), distinct matcher rows
         # read (Bloom rows only behind a passing bitmask), the outputs and the
         # parents' token / table rows.
@@ -187,7 +187,7 @@ def algorithmic_units(b: Bench):
         n_bl = np.unique(bli[ent[ok]]).size if w.bloom_bits else 0
         ent_bytes = 10 + (4 if w.bloom_bits else 0)
         n_sel = int((d.parent[t].cpu().numpy() >= 0).sum())
-        tail_b = (R * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
+        tail_b = (int(live.sum()) * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
                   + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl
                   + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4)
         res.append(dict(t=t, R=R, live_in=int(live.sum()), cross_bytes=int(cross_b),
