@@ -264,7 +264,16 @@ def check_tail(w, ix, view, prefix, req, node_in, acc_in, logits64, M_in, k_out,
         assert (tb[live, t + 1:] == -1).all() and (tb[~live] == -1).all()
 
 
+# 70 two-valued attributes (3 bitmask words, 70 user bits set), 9 Bloom
+# probes per id and 100 user locations: the paths past 64 user bits, past 8
+# probes per location and past 64 locations.
+_WIDE_ATTR = W.Workload(
+    name="wide_attr", dtype="bf16", B=2, L=3, V=64, schedule=(64, 256, 256), T_ctx=40, H=2,
+    d_h=32, n_sids=20_000, zipf_s=1.1, ads_per_sid=(1, 8), bm_segments=(2,) * 70, bm_p=0.97,
+    bloom_bits=1024, bloom_k=9, geo_pool=2000, geo_per_ad=(1, 16), n_loc=100)
+
 TAIL_WORKLOADS = {
+    "wide_attr": _WIDE_ATTR,
     "tiny": W.WORKLOADS["tiny_fp32"],
     "main_50k": W.WORKLOADS["main_b16_m1024"].scaled(n_sids=50_000),
     "long_50k": W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000),
@@ -286,6 +295,8 @@ TAIL_CASES = [
     ("long_50k", 3, 3, 300, 900, 1, 0.1, "normal", "normal"),
     ("stress_20k", 4, 2, 1024, 1024, 1, 0.1, "normal", "normal"),
     ("stress_20k", 4, 2, 1024, 1024, 2, 0.1, "normal", "normal"),
+    ("wide_attr", 5, 2, 64, 256, 1, 0.1, "normal", "normal"),
+    ("wide_attr", 5, 2, 256, 256, 2, 0.1, "normal", "normal"),
 ]
 
 
@@ -324,6 +335,7 @@ def test_constrain_topk_k_at_survivor_count(name, seed, M_in, t):
 
 @pytest.mark.parametrize("slice_min", [-1, 1])
 @pytest.mark.parametrize("name,seed,M_in,k_out,t", [("tiny", 1, 8, 8, 1), ("main_50k", 1, 300, 1000, 1),
+                                                   ("wide_attr", 5, 64, 256, 1),
                                                    ("main_50k", 1, 700, 1024, 2),
                                                    ("stress_20k", 4, 512, 1024, 1)])
 def test_constrain_topk_bloom_layouts(slice_min, name, seed, M_in, k_out, t):

@@ -35,6 +35,7 @@ constexpr int EXP_WAVES = 4;
 constexpr int EXP_THREADS = 64 * EXP_WAVES;
 constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 4096 bits)
 constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
+constexpr int MAX_KP = 8;             // probes per location held in registers (more: LDS)
 constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
 constexpr int BND_CAP = 2048;         // threshold-bin entries buffered in LDS
@@ -64,7 +65,6 @@ struct TailParams {
     int32_t *tokens_out, *table_out;
     uint64_t *dbg_mask;
     float *dbg_scores;
-    float *ubound;
     uint32_t *segcnt;   // survivors of each expand workgroup [B, gx]
     uint32_t *hist;
     uint64_t *skey;     // survivor segments [B, gx, seg_cap]
@@ -73,7 +73,7 @@ struct TailParams {
     int gx;
     // expand launch shape
     int rows_wg;        // beam rows per workgroup
-    int G, S, log2_s;   // Bloom rows staged per sub-round, lanes per row
+    int G;              // Bloom rows staged per sub-round
     int log2_wq;        // log2 of the 8-byte words per Bloom row
     int stage_dw;       // staging dwords per wavefront
     int mask_words;     // per-row mask words kept in LDS (debug outputs), else 0
@@ -96,20 +96,26 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t f) {
 __device__ __forceinline__ float key_score(uint64_t k) { return f32_unord((uint32_t)(k >> 32)); }
 __device__ __forceinline__ uint32_t key_flat(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
 
-__global__ __launch_bounds__(256) void k_tail_prep(TailParams p) {
-    const int b = blockIdx.x, tid = threadIdx.x;
-    uint32_t *h = p.hist + (size_t)b * NBINS;
-    for (int i = tid; i < NBINS; i += 256) h[i] = 0u;
+// Clears the score histograms of all requests (standalone gr_constrain_topk;
+// gr_decode_step has the self-attention launch do it).
+__global__ __launch_bounds__(256) void k_tail_clear(uint32_t *hist, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) hist[i] = 0u;
+}
+
+// Partial max of the live parent scores of request b held by this thread;
+// the caller reduces it over the workgroup.  Every candidate score of the
+// request is at most the full max (log-probabilities are <= 0), so the score
+// histogram bins hang below it.  The same rows and the same max (exact in
+// floating point) give expand and select the same bound.
+__device__ __forceinline__ float bound_part(const TailParams &p, int b) {
     float mx = -INFINITY;
-    for (int m = tid; m < p.M_in; m += 256) {
+    for (int m = threadIdx.x; m < p.M_in; m += blockDim.x) {
         const int r = b * p.M_in + m;
-        if (p.node_in[r] >= 0) mx = fmaxf(mx, p.acc_in[r]);
+        const int node = p.node_in[r];
+        if (node >= 0 && node < p.num_nodes) mx = fmaxf(mx, p.acc_in[r]);
     }
-    mx = wave_max(mx);
-    __shared__ float s_m[4];
-    if ((tid & 63) == 0) s_m[tid >> 6] = mx;
-    __syncthreads();
-    if (tid == 0) p.ubound[b] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    return wave_max(mx);
 }
 
 template <bool BF16>
@@ -140,60 +146,62 @@ __device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
     return v;
 }
 
-// Words w0 .. w0 + n - 1 (n <= 4) of a bit-sliced column, 16 bytes at a time
-// when the column width wc is even (the block base is 512-byte aligned).
-__device__ __forceinline__ void col_words(const uint64_t *col, int n, bool even, uint64_t w[4]) {
+// Four words w0 .. w0 + 3 of a bit-sliced column, loaded unconditionally
+// (16 bytes at a time when the column width wc is even: blocks start
+// 512-byte aligned).  Words past the column belong to the next positions or
+// to the table's 4-word tail pad; callers ignore them.
+__device__ __forceinline__ void col4(const uint64_t *col, bool even, uint64_t w[4]) {
     if (even) {
         const uint4 u = *(const uint4 *)col;
+        const uint4 u2 = *(const uint4 *)(col + 2);
         w[0] = (uint64_t)u.x | ((uint64_t)u.y << 32);
         w[1] = (uint64_t)u.z | ((uint64_t)u.w << 32);
-        if (n > 2) {
-            const uint4 u2 = *(const uint4 *)(col + 2);
-            w[2] = (uint64_t)u2.x | ((uint64_t)u2.y << 32);
-            w[3] = (uint64_t)u2.z | ((uint64_t)u2.w << 32);
-        }
+        w[2] = (uint64_t)u2.x | ((uint64_t)u2.y << 32);
+        w[3] = (uint64_t)u2.z | ((uint64_t)u2.w << 32);
     } else {
         w[0] = col[0];
-        if (n > 1) w[1] = col[1];
-        if (n > 2) w[2] = col[2];
-        if (n > 3) w[3] = col[3];
+        w[1] = col[1];
+        w[2] = col[2];
+        w[3] = col[3];
     }
 }
 
-// Bloom test of G staged matcher rows (eq 8).  Lanes (g, s) with
-// g = lane / S: entry g's row is at stage + g * row_dw; lane s tries the
-// locations s, s + S, ...; the entry passes once any of them has all its
-// probe bits set, and its S lanes stop together.  probes holds kp positions
-// per location (a multiple of 4, padded with the location's first probe).  Returns the ballot: bit
-// g * S is set for every passing entry.
-__device__ __forceinline__ uint64_t bloom_test(const uint32_t *stage, int row_dw,
-                                               const int32_t *rowid, const uint32_t *probes,
-                                               int n_loc, int kp, int S, int sh_s,
+// Bloom test (eq 8) of one staged matcher row: lane l takes location l
+// (l < 64; further locations from probes in LDS), ANDs the row bits at its
+// probe positions, and the row passes if any lane's location has all of
+// them.  pr0 holds lane l's first kp (padded, a multiple of 4) positions.
+__device__ __forceinline__ bool bloom_row_test(const uint32_t *row, const uint4 *pr0,
+                                               const uint32_t *probes, int n_loc, int kp,
                                                int lane) {
-    const int g = lane >> sh_s, s = lane & (S - 1);
-    const bool act = rowid[g] >= 0;
-    const uint32_t *row = stage + g * row_dw;
-    const uint64_t gm = S == 64 ? ~0ull : ((1ull << S) - 1ull);
-    bool found = false;
-    for (int l0 = 0; l0 < n_loc; l0 += S) {
-        const int l = l0 + s;
-        if (act && !found && l < n_loc) {
-            // probes are padded to a multiple of 4 (pad = probe 0): one
-            // 16-byte read brings 4 positions, the 4 row reads are independent
+    uint32_t all = lane < n_loc ? 1u : 0u;
+#pragma unroll
+    for (int q = 0; q < MAX_KP / 4; ++q)
+        if (q * 4 < kp) {
+            const uint4 pp = pr0[q];
+            all &= (row[pp.x >> 5] >> (pp.x & 31u)) & (row[pp.y >> 5] >> (pp.y & 31u)) &
+                   (row[pp.z >> 5] >> (pp.z & 31u)) & (row[pp.w >> 5] >> (pp.w & 31u));
+        }
+    if (lane < n_loc)
+        for (int q = MAX_KP; q < kp; q += 4) {   // probes past the registers
+            const uint4 pp = *(const uint4 *)(probes + lane * kp + q);
+            all &= (row[pp.x >> 5] >> (pp.x & 31u)) & (row[pp.y >> 5] >> (pp.y & 31u)) &
+                   (row[pp.z >> 5] >> (pp.z & 31u)) & (row[pp.w >> 5] >> (pp.w & 31u));
+        }
+    bool any = __ballot(all & 1u) != 0ull;
+    for (int lg = 64; lg < n_loc && !any; lg += 64) {   // uniform
+        const int l = lg + lane;
+        uint32_t a2 = l < n_loc ? 1u : 0u;
+        if (l < n_loc) {
             const uint4 *pr = (const uint4 *)(probes + l * kp);
-            uint32_t all = 1u;
             for (int q = 0; q < kp; q += 4) {
                 const uint4 pp = pr[q >> 2];
-                all &= (row[pp.x >> 5] >> (pp.x & 31u)) & (row[pp.y >> 5] >> (pp.y & 31u)) &
-                       (row[pp.z >> 5] >> (pp.z & 31u)) & (row[pp.w >> 5] >> (pp.w & 31u));
+                a2 &= (row[pp.x >> 5] >> (pp.x & 31u)) & (row[pp.y >> 5] >> (pp.y & 31u)) &
+                      (row[pp.z >> 5] >> (pp.z & 31u)) & (row[pp.w >> 5] >> (pp.w & 31u));
             }
-            found = (all & 1u) != 0u;
         }
-        const uint64_t fb = __ballot(found);
-        found = ((fb >> (g * S)) & gm) != 0ull;  // any lane of the entry
-        if (__ballot(act && !found) == 0ull) break;
+        any = __ballot(a2 & 1u) != 0ull;
     }
-    return __ballot(found);
+    return any;
 }
 
 // One workgroup = up to rows_wg beam rows of one request, taken with a stride
@@ -206,7 +214,8 @@ __device__ __forceinline__ uint64_t bloom_test(const uint32_t *stage, int row_dw
 // round, then moved to LDS G rows at a time for the test; otherwise G rows
 // are loaded straight into LDS per sub-round.
 template <bool BF16, bool WIDE>
-__global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
+__global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
+void k_expand(TailParams p) {
     extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];  // [mask][probes][staging]
     __shared__ uint32_t s_hist[NBINS];
     __shared__ uint64_t s_ubm[MAX_WBM];
@@ -217,6 +226,9 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
     __shared__ float s_acc[MAX_ROWS_WG];
     __shared__ int64_t s_rblk[MAX_ROWS_WG];        // bit-sliced block of the row's node
     __shared__ uint32_t s_nsurv;                   // survivors written to the segment
+    __shared__ int32_t s_slist[MAX_ROWS_WG];       // rows with a bit-sliced block
+    __shared__ int s_nsl;
+    __shared__ float s_ub[EXP_WAVES];
     __shared__ int s_nub;
     __shared__ int32_t s_rowid[EXP_WAVES][64];     // Bloom row of each staged entry
 
@@ -242,7 +254,10 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
     }
     for (int i = tid; i < p.rows_wg * p.mask_words; i += EXP_THREADS) s_mask[i] = 0ull;
     if (tid == 0) s_nsurv = 0u;
-    const float U = p.ubound[b];
+    {
+        const float ub = bound_part(p, b);
+        if (lane == 0) s_ub[wave] = ub;
+    }
     if (p.wmax && wave == 1) {  // list the user's attribute bits (eq 5 columns)
         const uint64_t u = lane < p.w_bm ? p.user_bm[(size_t)b * p.w_bm + lane] : 0ull;
         const int n = __popcll(u);
@@ -289,8 +304,19 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
         }
         if (lane < nrows) s_rstart[lane + 1] = inc;
         if (lane == 0) s_rstart[0] = 0;
+        const uint64_t sl = __ballot(lane < nrows && cnt > 0 && s_rblk[lane < nrows ? lane : 0] >= 0);
+        if ((sl >> lane) & 1ull) s_slist[__popcll(sl & ((1ull << lane) - 1ull))] = lane;
+        if (lane == 0) s_nsl = __popcll(sl);
     }
     __syncthreads();
+    const float U = fmaxf(fmaxf(s_ub[0], s_ub[1]), fmaxf(s_ub[2], s_ub[3]));
+    // lane l's location l: its probe positions, kept in registers
+    uint4 pr0[MAX_KP / 4];
+#pragma unroll
+    for (int q = 0; q < MAX_KP / 4; ++q) {
+        pr0[q] = make_uint4(0u, 0u, 0u, 0u);
+        if (q * 4 < kp && lane < p.n_loc && p.w_bl) pr0[q] = ((const uint4 *)(s_probe + lane * kp))[q];
+    }
 
     // Full-vocabulary log-sum-exp of every row with candidates (eq 3 masks
     // log-probabilities, so the normaliser runs over all V tokens): TPR
@@ -329,57 +355,124 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
     // bits.  Eq 8: lane l ANDs the columns of location l's probe positions
     // (bit j set = child j has all of them), then the lanes OR (ANY location).
     if (p.wmax) {
-        const int nub = s_nub;
+        const int nub = s_nub, nsl = s_nsl;
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
-        for (int i = wave; i < nrows; i += EXP_WAVES) {
+        const int ub0 = nub ? s_ubit[lane < nub ? lane : 0] : 0;   // lane's user bit
+        for (int li = wave; li < nsl; li += EXP_WAVES) {
+            const int i = s_slist[li];
             const int64_t blk = s_rblk[i];
             const int c = s_rstart[i + 1] - s_rstart[i];
-            if (blk < 0 || c == 0) continue;
             const int wc = (c + 63) >> 6;
-            const bool even = (wc & 1) == 0;
             const uint64_t *tab = p.slice_tab + blk;
+            if (wc == 1) {
+                // one word per column (fewer than 65 children): every load
+                // first, then one AND and one OR reduction
+                uint64_t bm = lane < nub ? tab[bl_pos + ub0] : ~0ull;
+                for (int qg = 64; qg < nub; qg += 64)   // user bits past 64
+                    if (qg + lane < nub) bm &= tab[bl_pos + s_ubit[qg + lane]];
+                uint64_t acc = 0ull;
+                if (p.w_bl) {
+                    uint64_t a = ~0ull;
+#pragma unroll
+                    for (int qq = 0; qq < MAX_KP / 4; ++qq)
+                        if (qq * 4 < kp)
+                            a &= tab[pr0[qq].x] & tab[pr0[qq].y] & tab[pr0[qq].z] & tab[pr0[qq].w];
+                    if (lane < p.n_loc)
+                        for (int q = MAX_KP; q < kp; q += 4) {   // probes past the registers
+                            const uint4 pp = *(const uint4 *)(s_probe + lane * kp + q);
+                            a &= tab[pp.x] & tab[pp.y] & tab[pp.z] & tab[pp.w];
+                        }
+                    acc = lane < p.n_loc ? a : 0ull;
+                    for (int lg = 64; lg < p.n_loc; lg += 64) {   // locations past 64
+                        const int l = lg + lane;
+                        if (l < p.n_loc) {
+                            uint64_t a2 = ~0ull;
+                            const uint4 *pr = (const uint4 *)(s_probe + l * kp);
+                            for (int q = 0; q < kp; q += 4) {
+                                const uint4 pp = pr[q >> 2];
+                                a2 &= tab[pp.x] & tab[pp.y] & tab[pp.z] & tab[pp.w];
+                            }
+                            acc |= a2;
+                        }
+                    }
+                }
+                uint64_t pass = wave_and64(bm);
+                if (p.w_bl) pass &= wave_or64(acc);
+                if (lane == 0) s_pass[(size_t)i * p.wmax] = pass;
+                continue;
+            }
+            const bool even = (wc & 1) == 0;
             for (int w0 = 0; w0 < wc; w0 += 4) {
                 const int n = min(4, wc - w0);
-                uint64_t bm[4] = {~0ull, ~0ull, ~0ull, ~0ull};
-                for (int qg = 0; qg < nub; qg += 64) {
+                // every column load of the row first, the reductions after
+                uint64_t bm[4];
+                col4(tab + (size_t)(bl_pos + ub0) * wc + w0, even, bm);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (lane >= nub) bm[u] = ~0ull;
+                for (int qg = 64; qg < nub; qg += 64) {   // user bits past 64
                     const int q = qg + lane;
                     if (q < nub) {
                         uint64_t cw[4];
-                        col_words(tab + (size_t)(bl_pos + s_ubit[q]) * wc + w0, n, even, cw);
+                        col4(tab + (size_t)(bl_pos + s_ubit[q]) * wc + w0, even, cw);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (u < n) bm[u] &= cw[u];
+                        for (int u = 0; u < 4; ++u) bm[u] &= cw[u];
                     }
                 }
-                uint64_t pass[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) pass[u] = wave_and64(bm[u]);
+                uint64_t acc[4] = {0ull, 0ull, 0ull, 0ull};
                 if (p.w_bl) {
-                    uint64_t acc[4] = {0ull, 0ull, 0ull, 0ull};
-                    for (int lg = 0; lg < p.n_loc; lg += 64) {
+                    uint64_t a[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+#pragma unroll
+                    for (int qq = 0; qq < MAX_KP / 4; ++qq)
+                        if (qq * 4 < kp) {
+                            uint64_t c0[4], c1[4], c2[4], c3[4];
+                            col4(tab + (size_t)pr0[qq].x * wc + w0, even, c0);
+                            col4(tab + (size_t)pr0[qq].y * wc + w0, even, c1);
+                            col4(tab + (size_t)pr0[qq].z * wc + w0, even, c2);
+                            col4(tab + (size_t)pr0[qq].w * wc + w0, even, c3);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) a[u] &= c0[u] & c1[u] & c2[u] & c3[u];
+                        }
+                    if (lane < p.n_loc)
+                        for (int q = MAX_KP; q < kp; q += 4) {   // probes past the registers
+                            const uint4 pp = *(const uint4 *)(s_probe + lane * kp + q);
+                            const uint32_t pos[4] = {pp.x, pp.y, pp.z, pp.w};
+                            for (int t4 = 0; t4 < 4; ++t4) {
+                                uint64_t cw[4];
+                                col4(tab + (size_t)pos[t4] * wc + w0, even, cw);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) a[u] &= cw[u];
+                            }
+                        }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = lane < p.n_loc ? a[u] : 0ull;
+                    for (int lg = 64; lg < p.n_loc; lg += 64) {   // locations past 64
                         const int l = lg + lane;
                         if (l < p.n_loc) {
-                            uint64_t a[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+                            uint64_t a2[4] = {~0ull, ~0ull, ~0ull, ~0ull};
                             const uint4 *pr = (const uint4 *)(s_probe + l * kp);
                             for (int q = 0; q < kp; q += 4) {
                                 const uint4 pp = pr[q >> 2];
                                 const uint32_t pos[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
                                 for (int t4 = 0; t4 < 4; ++t4) {
                                     uint64_t cw[4];
-                                    col_words(tab + (size_t)pos[t4] * wc + w0, n, even, cw);
+                                    col4(tab + (size_t)pos[t4] * wc + w0, even, cw);
 #pragma unroll
-                                    for (int u = 0; u < 4; ++u)
-                                        if (u < n) a[u] &= cw[u];
+                                    for (int u = 0; u < 4; ++u) a2[u] &= cw[u];
                                 }
                             }
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) acc[u] |= a[u];
+                            for (int u = 0; u < 4; ++u) acc[u] |= a2[u];
                         }
                     }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) pass[u] &= wave_or64(acc[u]);
                 }
+                uint64_t pass[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (u < n) {   // uniform
+                        pass[u] = wave_and64(bm[u]);
+                        if (p.w_bl) pass[u] &= wave_or64(acc[u]);
+                    }
                 if (lane < n) {
                     uint64_t x = pass[0];
 #pragma unroll
@@ -397,7 +490,7 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
     // this workgroup's survivor segment: slots come from an LDS counter
     uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
     int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
-    const int G = p.G, S = p.S, sh_s = p.log2_s, wq = p.w_bl, sh_wq = p.log2_wq;
+    const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
     const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
 
     for (int c0 = wave * 64; c0 < n_ent; c0 += EXP_THREADS) {
@@ -490,10 +583,12 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
                             }
                         }
                         wave_lds_sync();
-                        const uint64_t fb = bloom_test(s_stage, row_dw, rowid + s0, s_probe, p.n_loc,
-                                                       kp, S, sh_s, lane);
-                        const int q = lane - b0 - s0;
-                        if (q >= 0 && q < G && ((fb >> (q * S)) & 1ull)) bl_ok = true;
+                        for (int g = 0; g < G && s0 + g < CH; ++g) {
+                            if (rowid[s0 + g] < 0) continue;   // uniform
+                            if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane) &&
+                                lane == b0 + s0 + g)
+                                bl_ok = true;
+                        }
                         wave_lds_sync();
                     }
                 }
@@ -529,10 +624,12 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
                             }
                     }
                     wave_lds_sync();
-                    const uint64_t fb = bloom_test(s_stage, row_dw, rowid, s_probe, p.n_loc,
-                                                   kp, S, sh_s, lane);
-                    const int q = lane - sr;
-                    if (q >= 0 && q < G && ((fb >> (q * S)) & 1ull)) bl_ok = true;
+                    for (int g = 0; g < G; ++g) {
+                        if (rowid[g] < 0) continue;   // uniform
+                        if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane) &&
+                            lane == sr + g)
+                            bl_ok = true;
+                    }
                     wave_lds_sync();
                 }
             }
@@ -585,7 +682,11 @@ __global__ __launch_bounds__(EXP_THREADS) void k_expand(TailParams p) {
     // segment's count; k_select reads both after the kernel boundary, so no
     // device-scope fence is needed here.
     __syncthreads();
-    if (tid == 0) p.segcnt[(size_t)b * gx + x] = min(s_nsurv, (uint32_t)p.seg_cap);
+    if (tid == 0) {
+        uint32_t n = min(s_nsurv, (uint32_t)p.seg_cap);
+        if (n & 1u) skey[n++] = 0ull;   // pad to a key pair (seg_cap is even)
+        p.segcnt[(size_t)b * gx + x] = n;
+    }
     uint32_t *gh = p.hist + (size_t)b * NBINS;
     for (int i = tid; i < NBINS; i += EXP_THREADS) {
         const uint32_t c = s_hist[i];
@@ -635,7 +736,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     __shared__ int s_thr, s_below, s_nbnd, s_ncol, s_digit, s_rem;
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float U = p.ubound[b];
+    __shared__ float s_ub[SEL_THREADS / 64];
+    {
+        const float ub = bound_part(p, b);
+        if (lane == 0) s_ub[wave] = ub;
+    }
     const int k = p.k_out;
     // survivors of request b: segment x holds segcnt[b, x] keys at
     // keys + x * seg_cap; a survivor is named by its offset in the request
@@ -660,6 +765,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         if (2 * tid <= gx) s_segpre[2 * tid] = ex;
         if (2 * tid + 1 <= gx) s_segpre[2 * tid + 1] = ex + c0;
     }
+    float U = s_ub[0];
+    for (int w = 1; w < SEL_THREADS / 64; ++w) U = fmaxf(U, s_ub[w]);
     const uint32_t *gh = p.hist + (size_t)b * NBINS;
 
     // 1. Exclusive prefix of the score histogram; the threshold bin is the
@@ -718,33 +825,40 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
 
     // 2. Survivors of bins below the threshold go to their bin's segment;
     //    members of the threshold bin are buffered.
-    for (uint32_t f0 = 0; f0 < n_surv; f0 += 4 * SEL_THREADS) {
-        uint32_t src[4];
-        uint64_t kk[4];
+    // Survivors are read as 16-byte key pairs (segment counts are even), 8
+    // pairs in flight per thread; zero keys are the segments' pads.
+    auto take = [&](uint64_t key, uint32_t src) {
+        if (key == 0ull) return;
+        const int bin = score_bin(key_score(key), U);
+        if (bin < thr) {
+            const uint32_t pos = atomicAdd(&s_seg[bin], 1u);
+            if (pos < (uint32_t)MAX_K) {
+                s_key[pos] = key;
+                s_src[pos] = (int32_t)src;
+            }
+        } else if (bin == thr) {
+            const int pos = atomicAdd(&s_nbnd, 1);
+            if (pos < BND_CAP) {
+                s_bkey[pos] = key;
+                s_bsrc[pos] = (int32_t)src;
+            }
+        }
+    };
+    const uint32_t n_pairs = n_surv >> 1;
+    for (uint32_t p0 = 0; p0 < n_pairs; p0 += 8 * SEL_THREADS) {
+        uint32_t src[8];
+        uint4 kv[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {   // 4 loads in flight per thread
-            const uint32_t f = f0 + u * SEL_THREADS + tid;
-            src[u] = f < n_surv ? surv(f) : 0xFFFFFFFFu;
-            kk[u] = f < n_surv ? keys[src[u]] : 0ull;
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t pp = p0 + u * SEL_THREADS + tid;
+            src[u] = pp < n_pairs ? surv(2 * pp) : 0xFFFFFFFFu;
+            kv[u] = pp < n_pairs ? *(const uint4 *)(keys + src[u]) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             if (src[u] == 0xFFFFFFFFu) continue;
-            const uint64_t key = kk[u];
-            const int bin = score_bin(key_score(key), U);
-            if (bin < thr) {
-                const uint32_t pos = atomicAdd(&s_seg[bin], 1u);
-                if (pos < (uint32_t)MAX_K) {
-                    s_key[pos] = key;
-                    s_src[pos] = (int32_t)src[u];
-                }
-            } else if (bin == thr) {
-                const int pos = atomicAdd(&s_nbnd, 1);
-                if (pos < BND_CAP) {
-                    s_bkey[pos] = key;
-                    s_bsrc[pos] = (int32_t)src[u];
-                }
-            }
+            take((uint64_t)kv[u].x | ((uint64_t)kv[u].y << 32), src[u]);
+            take((uint64_t)kv[u].z | ((uint64_t)kv[u].w << 32), src[u] + 1);
         }
     }
     __syncthreads();
@@ -764,7 +878,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
                 __syncthreads();
                 for (uint32_t f = tid; f < n_surv; f += SEL_THREADS) {
                     const uint64_t key = keys[surv(f)];
-                    if (score_bin(key_score(key), U) == thr && (key & pmask) == prefix)
+                    if (key && score_bin(key_score(key), U) == thr && (key & pmask) == prefix)
                         atomicAdd(&s_cnt[(key >> shift) & 255u], 1u);
                 }
                 __syncthreads();
@@ -788,7 +902,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             for (uint32_t f = tid; f < n_surv; f += SEL_THREADS) {
                 const uint32_t i = surv(f);
                 const uint64_t key = keys[i];
-                if (score_bin(key_score(key), U) == thr && key >= prefix) {
+                if (key && score_bin(key_score(key), U) == thr && key >= prefix) {
                     const int pos = atomicAdd(&s_ncol, 1);
                     if (pos < BND_CAP) {
                         s_bkey[pos] = key;
@@ -874,7 +988,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
 
 }  // namespace
 
-hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
+hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool hist_cleared,
+                                 hipStream_t s) {
     TailParams p{};
     p.off = tr.node_offsets;
     p.child = tr.child_nodes;
@@ -914,7 +1029,6 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipSt
     p.dbg_scores = a.dbg_scores;
     const TailWsLayout ly = tail_ws_layout(a.B, a.M_in, a.V);
     char *ws = (char *)a.ws;
-    p.ubound = (float *)(ws + ly.ubound);
     p.segcnt = (uint32_t *)(ws + ly.segcnt);
     p.hist = (uint32_t *)(ws + ly.hist);
     p.skey = (uint64_t *)(ws + ly.skey);
@@ -931,10 +1045,6 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipSt
     int G = 64;
     while (G > 1 && G * row_bytes > STAGE_BYTES) G >>= 1;
     p.G = G;
-    p.S = 64 / G;
-    int log2_s = 0;
-    while ((1 << log2_s) < p.S) ++log2_s;
-    p.log2_s = log2_s;
     p.stage_dw = tr.w_bl ? G * (2 * tr.w_bl + 1) : 0;
     p.mask_words = (a.dbg_mask || a.dbg_scores) ? (a.V + 63) / 64 : 0;
     p.wmax = tr.node_slice ? (a.V + 63) / 64 : 0;
@@ -951,7 +1061,10 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, hipSt
     while ((1 << log2_tpr) < tpr) ++log2_tpr;
     p.log2_tpr = log2_tpr;
 
-    k_tail_prep<<<a.B, 256, 0, s>>>(p);
+    if (!hist_cleared) {
+        const int nh = a.B * NBINS;
+        k_tail_clear<<<(nh + 255) / 256, 256, 0, s>>>(p.hist, nh);
+    }
     dim3 g1(gx, a.B);
     const bool wide = tr.w_bl >= 64;
     if (a.dtype == GR_BF16) {

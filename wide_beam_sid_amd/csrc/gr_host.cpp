@@ -388,7 +388,7 @@ static void build_slices(int64_t num_nodes, const int32_t *off, const int32_t *b
             total += npos * ((c + 63) / 64);
         }
     }
-    tab.assign((size_t)total, 0ull);
+    tab.assign((size_t)total + 4, 0ull);   // + a tail pad for 4-word column reads
     int64_t *ns = node_slice.data();
     uint64_t *tb = tab.data();
     const int bl_pos = w_bl ? bloom_bits : 0;
@@ -795,7 +795,6 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     const size_t nseg = (size_t)B * l.shape.gx;
     const size_t nsurv = nseg * (size_t)l.shape.seg_cap;
     size_t o = 0;
-    l.ubound = o; o = al(o + sizeof(float) * B);
     l.segcnt = o; o = al(o + sizeof(uint32_t) * nseg);
     l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * B);
     l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);
@@ -850,7 +849,7 @@ static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const ch
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *stream) {
     gr_status st = check_tail(trie, a, "gr_constrain_topk");
     if (st) return st;
-    hipError_t e = launch_constrain_topk(trie->d, *a, (hipStream_t)stream);
+    hipError_t e = launch_constrain_topk(trie->d, *a, false, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk launch");
     return GR_OK;
 }
@@ -881,11 +880,14 @@ gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *strea
     hipError_t e = launch_cross_attn(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
                                      s->d_h, a.dtype, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step cross-attention launch");
+    // the self-attention launch also clears the tail's score histograms
+    const TailWsLayout ly = tail_ws_layout(a.B, a.M_in, a.V);
     e = launch_self_attn(s->q, s->k_new, s->v_new, s->k_pool, s->v_pool, s->pool_blocks,
                          const_cast<int32_t *>(a.table_in),
-                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs);
+                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs,
+                         (uint32_t *)((char *)a.ws + ly.hist), (int64_t)a.B * NBINS);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step self-attention launch");
-    e = launch_constrain_topk(trie->d, a, hs);
+    e = launch_constrain_topk(trie->d, a, true, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");
     return GR_OK;
 }

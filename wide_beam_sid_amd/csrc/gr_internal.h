@@ -44,7 +44,8 @@ constexpr int MAX_ROWS_WG = 32;      // beam rows per expand workgroup (upper bo
 
 // Launch shape of the expand kernel: workgroup x of request b takes rows
 // m = x + i * gx (i < rows_wg) and owns a survivor segment of seg_cap
-// entries (a row has at most V children), so no segment can overflow.
+// entries (a row has at most V children), so no segment can overflow.  A
+// segment's count is made even with a zero key (never a real key).
 struct TailShape {
     int rows_wg, gx;
     int64_t seg_cap;
@@ -60,13 +61,13 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
     TailShape t;
     t.rows_wg = (int)rw;
     t.gx = (int)((M_in + rw - 1) / rw);
-    t.seg_cap = rw * V;
+    t.seg_cap = (rw * V + 1) & ~(int64_t)1;   // even: segments are read in key pairs
     return t;
 }
 
 // Workspace carving of gr_constrain_topk (byte offsets).
 struct TailWsLayout {
-    size_t ubound, segcnt, hist, skey, schild, total;
+    size_t segcnt, hist, skey, schild, total;
     TailShape shape;
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
@@ -74,11 +75,14 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out,
                              int B, int M, int H, int T, int d, gr_dtype dt,
                              hipStream_t s);
+// launch_self_attn can also zero n_zero words at zero_ptr in extra
+// workgroups of the same launch (the tail's histogram in gr_decode_step).
 hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t pool_blocks, int32_t *table,
                             int64_t fresh_base, int R, int t, int L, int H, int d,
-                            gr_dtype dt, void *out, hipStream_t s);
-hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a,
+                            gr_dtype dt, void *out, hipStream_t s,
+                            uint32_t *zero_ptr = nullptr, int64_t n_zero = 0);
+hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool hist_cleared,
                                  hipStream_t s);
 
 }  // namespace gr
