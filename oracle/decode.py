@@ -72,13 +72,17 @@ class OracleStepOut:
 
 def step(w, ix, req, ctx, t: int, st: OracleState, inp: dict, as_float,
          gpu_scores: Optional[np.ndarray] = None, attention: bool = True,
-         rows_subset: Optional[np.ndarray] = None) -> OracleStepOut:
+         rows_subset: Optional[np.ndarray] = None,
+         mask_rows: Optional[np.ndarray] = None,
+         given_mask: Optional[np.ndarray] = None) -> OracleStepOut:
     """One decode step.
 
     ``gpu_scores`` (float32 [R, V]) are the GPU's own candidate scores; when
     given, top-k sorts them (so that the selection can be compared bit for
     bit), otherwise it sorts float32(oracle fp64 score).
     ``rows_subset`` restricts attention to some rows (others stay NaN).
+    ``mask_rows`` restricts the CD/TM masks to some rows (for catalogs too
+    large to enumerate every row); the other rows take ``given_mask``.
     """
     B, V, L = w.B, w.V, w.L
     R = st.tokens.shape[0]
@@ -115,10 +119,13 @@ def step(w, ix, req, ctx, t: int, st: OracleState, inp: dict, as_float,
     logits = as_float(inp["logits"]).astype(np.float64)
     lp = np.empty((R, V))
     blooms = [ix.user_blooms(req.locs[b]) for b in range(B)]
-    for r in range(R):
+    if mask_rows is not None:
+        mask[:] = given_mask
+    for r in (range(R) if mask_rows is None else mask_rows):
         b = r // M
         mask[r] = ix.mask_row(st.tokens[r, :t], t if st.live[r] else -1,
                               req.user_bm[b], req.locs[b], blooms[b])
+    for r in range(R):
         lp[r] = log_softmax(logits[r])
     keep = mask_bits_to_bool(mask, V)
     cand = np.where(keep, st.acc[:, None] + lp, -np.inf)

@@ -27,7 +27,7 @@ def _gpu():
     yield
 
 
-def run_chain(w, seed, sample_rows=None):
+def run_chain(w, seed, sample_rows=None, mask_sample=None):
     import wide_beam_sid_amd as gr
     from wide_beam_sid_amd.runner import Decoder
     print(f"[chain] {w.name} B={w.B} sched={w.schedule} n_sids={w.n_sids} seed={seed}", flush=True)
@@ -57,10 +57,14 @@ def run_chain(w, seed, sample_rows=None):
         rows = None
         if sample_rows is not None and R > sample_rows:
             rows = np.sort(rng.choice(R, size=sample_rows, replace=False))
+        gmask = dec.dbg_mask[t].cpu().numpy().view(np.uint64)
+        mrows = None
+        if mask_sample is not None and R > mask_sample:
+            mrows = np.sort(rng.choice(R, size=mask_sample, replace=False))
         ref = oracle_step(w, ix, req, (kc, vc), t, st, inp, as_f, gpu_scores=scores,
-                          rows_subset=rows)
-        # A3 mask, A4 scores
-        assert np.array_equal(dec.dbg_mask[t].cpu().numpy().view(np.uint64), ref.mask), f"mask t={t}"
+                          rows_subset=rows, mask_rows=mrows, given_mask=gmask)
+        # A3 mask (bit-exact on every row, or on the sampled rows), A4 scores
+        assert np.array_equal(gmask, ref.mask), f"mask t={t}"
         fin = np.isfinite(ref.cand)
         assert np.array_equal(np.isfinite(scores), fin), f"finite t={t}"
         if fin.any():
@@ -133,3 +137,30 @@ def test_decode_chain_main_full_size():
     masks, scores, selection and reorder on every row; attention on 512
     sampled rows per step."""
     run_chain(W.WORKLOADS["main_b16_m1024"], 1, sample_rows=512)
+
+
+@pytest.mark.timeout(1200)
+def test_decode_chain_dynamic_full_size():
+    """Dynamic widths 64 -> 256 -> 1024 -> 1024 over B = 32 at the real size
+    (4M SIDs, 4096-bit Bloom, T_ctx 256, 8 x 64 heads): masks, scores,
+    selection and reorder on every row; attention on 256 sampled rows."""
+    run_chain(W.WORKLOADS["dynamic_b32"], 2, sample_rows=256)
+
+
+@pytest.mark.timeout(1200)
+def test_decode_chain_longctx_full_size():
+    """Long shared context at the real size: B = 8, widths 20 -> 300 -> 900,
+    V = 1024, T_ctx 2048, 16 x 128 heads, 2M SIDs, bitmask-only GTM."""
+    run_chain(W.WORKLOADS["longctx_b8"], 3, sample_rows=256)
+
+
+@pytest.mark.timeout(1200)
+def test_decode_chain_stress_full_shape():
+    """The stress shape (B = 64, M = 1024, V = 1024, T_ctx 512, 8 x 64 heads,
+    8192-bit Bloom with k = 5, 64 user locations, geo lists of 1-256 ids from
+    1M, per-request eligibility ~10%) on a 2M-SID catalog (the 16M one is
+    exercised by the benchmark's index build, not by the oracle).  Masks are
+    compared bit for bit on 2048 sampled rows per step; scores, selection,
+    child nodes, token history and block table on every row."""
+    run_chain(W.WORKLOADS["stress_b64"].scaled(n_sids=2_000_000), 4, sample_rows=256,
+              mask_sample=2048)
