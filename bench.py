@@ -47,6 +47,41 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ["wide_beam_sid_amd/csrc/constrain.hip", "wide_beam_sid_amd/csrc/cross_attn.hip",
+                  "wide_beam_sid_amd/csrc/self_attn.hip", "wide_beam_sid_amd/csrc/gr_device.h",
+                  "wide_beam_sid_amd/csrc/gr_internal.h"]
+TRAFFIC_FILE = "profiles/traffic_main_b16_m1024.json"
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources: a stored counter reading applies to
+    the kernels it was taken on only."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, steps, workload: str):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a plain copy's reading) from the committed counter summary,
+    averaged over `steps`; None if there is none for these kernel sources."""
+    import json
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("workload") != workload or doc.get("source_sha256") != kernel_source_hash():
+        return None
+    rows = doc["per_step"].get(kernel)
+    if not rows:
+        return None
+    return float(np.mean([rows[t]["read_bytes"] + rows[t]["write_bytes"] for t in steps]))
+
+
 # ---------------------------------------------------------------------------
 # Setup
 # ---------------------------------------------------------------------------
@@ -125,7 +160,7 @@ class Bench:
         for t in range(w.L):
             a = self.args[s][t]
             R = w.rows(t)
-            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(5)]
             e[0].record(self.stream)
             st = self.L.gr_cross_attn(a.qx, a.k_ctx, a.v_ctx, a.cross_out, w.B, d.M[t], w.H,
                                       w.T_ctx, w.d_h, gdt, self.sp)
@@ -134,8 +169,10 @@ class Bench:
                                             a.pool_blocks, a.tail.table_in, a.fresh_base, R, t,
                                             w.L, w.H, w.d_h, gdt, a.self_out, self.sp)
             e[2].record(self.stream)
-            st |= self.L.gr_constrain_topk(self.h, ctypes.byref(a.tail), self.sp)
+            st |= self.L.gr_constrain(self.h, ctypes.byref(a.tail), self.sp)
             e[3].record(self.stream)
+            st |= self.L.gr_topk_reorder(self.h, ctypes.byref(a.tail), self.sp)
+            e[4].record(self.stream)
             if st != 0:
                 raise RuntimeError(self.L.gr_last_error().decode())
             out.append(e)
@@ -159,6 +196,15 @@ def algorithmic_units(b: Bench):
     ubm = b.req.user_bm
     b.decode(0)
     torch.cuda.synchronize()
+    # survivors (kept tokens of live rows) from a debug decode of the same inputs
+    from wide_beam_sid_amd.runner import Decoder
+    dd = Decoder(b.trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype, debug=True)
+    ctx, steps = b.sets[0]
+    dd.run(b.ubm, b.upr if w.bloom_bits else None, w.n_loc, ctx[0], ctx[1], steps)
+    torch.cuda.synchronize()
+    surv = [int(np.unpackbits(dd.dbg_mask[t].cpu().numpy().view(np.uint8)).sum())
+            for t in range(w.L)]
+    del dd
     res = []
     for t in range(w.L):
         R, M, k = w.rows(t), d.M[t], w.schedule[t]
@@ -187,12 +233,18 @@ def algorithmic_units(b: Bench):
         n_bl = np.unique(bli[ent[ok]]).size if w.bloom_bits else 0
         ent_bytes = 10 + (4 if w.bloom_bits else 0)
         n_sel = int((d.parent[t].cpu().numpy() >= 0).sum())
-        tail_b = (int(live.sum()) * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
-                  + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl
-                  + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4)
+        # gr_constrain: logits of live rows, node/acc, user rows, CSR entries,
+        # distinct matcher rows, survivors written (8-byte key + 4-byte child)
+        con_b = (int(live.sum()) * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
+                 + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl + 12 * surv[t])
+        # gr_topk_reorder: survivor keys, the winners' child ids, outputs and
+        # the parents' token / block-table rows
+        sel_b = 8 * surv[t] + 4 * n_sel + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4
+        tail_b = con_b + sel_b
         res.append(dict(t=t, R=R, live_in=int(live.sum()), cross_bytes=int(cross_b),
                         cross_flops=int(cross_f), self_bytes=int(self_b),
                         uniq_prefix_blocks=int(uniq_blk), tail_bytes=int(tail_b),
+                        constrain_bytes=int(con_b), topk_bytes=int(sel_b), survivors=surv[t],
                         csr_entries=n_ent, bitmask_pass=int(ok.sum()),
                         bm_rows_read=int(n_bm), bloom_rows_read=int(n_bl),
                         live_out=n_sel))
@@ -351,7 +403,7 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
 
-    names = ["gr_cross_attn", "gr_self_attn_paged", "gr_constrain_topk"]
+    names = ["gr_cross_attn", "gr_self_attn_paged", "gr_constrain", "gr_topk_reorder"]
     per = {n: [[] for _ in range(w.L)] for n in names}
     for dec in split:
         for t, e in enumerate(dec):
@@ -368,11 +420,12 @@ def main():
             p99_us=float(np.percentile(x, 99)),
             rows_per_s=u["R"] / (float(np.mean(x)) * 1e-6),
             cross_us=mean_us["gr_cross_attn"][t], self_us=mean_us["gr_self_attn_paged"][t],
-            tail_us=mean_us["gr_constrain_topk"][t],
+            constrain_us=mean_us["gr_constrain"][t], topk_us=mean_us["gr_topk_reorder"][t],
             cross_tflops=u["cross_flops"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e12,
             cross_gbs=u["cross_bytes"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e9,
             self_gbs=u["self_bytes"] / (mean_us["gr_self_attn_paged"][t] * 1e-6) / 1e9,
-            tail_gbs=u["tail_bytes"] / (mean_us["gr_constrain_topk"][t] * 1e-6) / 1e9))
+            constrain_gbs=u["constrain_bytes"] / (mean_us["gr_constrain"][t] * 1e-6) / 1e9,
+            topk_gbs=u["topk_bytes"] / (mean_us["gr_topk_reorder"][t] * 1e-6) / 1e9))
 
     # Dominant entry point: largest total time over the decode.
     tot = {n: sum(mean_us[n]) for n in names}
@@ -386,15 +439,20 @@ def main():
         roof = dict(bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s", frac=ach / peak)
         algo = fl
     else:
-        key = "self_bytes" if dom == "gr_self_attn_paged" else "tail_bytes"
+        key = {"gr_self_attn_paged": "self_bytes", "gr_constrain": "constrain_bytes",
+               "gr_topk_reorder": "topk_bytes"}[dom]
         by = sum(units[t][key] for t in wide) / len(wide)
         dur = sum(mean_us[dom][t] for t in wide) / len(wide)
         ach = by / (dur * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=ach / HBM_PEAK_GBS)
         algo = by
-    roof.update(kernel=dom, steps=wide, mean_us=dur, algorithmic_per_launch=algo,
-                traffic=None)
+    kern = {"gr_cross_attn": "k_cross_bf16", "gr_self_attn_paged": "k_self_attn",
+            "gr_constrain": "k_expand", "gr_topk_reorder": "k_select"}[dom]
+    roof.update(kernel=kern, entry_point=dom, steps=wide, mean_us=dur,
+                algorithmic_per_launch=algo,
+                traffic=measured_traffic({"k_cross_bf16": "k_cross", "k_self_attn": "k_self"}.get(
+                    kern, kern), wide, w.name))
 
     all_steps = np.concatenate([np.array(lat[t]) for t in range(w.L)]) * 1e3
     wide_steps = np.concatenate([np.array(lat[t]) for t in wide]) * 1e3

@@ -235,12 +235,25 @@ gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new
  *   table_out[s, 0..t] = table_in[parent, 0..t]; other entries -1.
  * Rows with node_in < 0 (or not a node of the trie) are dead: no candidates.
  * Probe positions are taken modulo bloom_bits.
- * Limits: V <= 4096, k_out <= 1024, M_in <= 65536, M_in * V < 2^31,
- * n_loc * (bloom_k rounded up to a multiple of 4) <= 2048, w_bm <= 64, Bloom
- * filters of at most 32768 bits (GR_E_UNSUPPORTED beyond).
- * The workspace must be 256-byte aligned and at least gr_constrain_topk_workspace(B, M_in, V, k_out) bytes
- * (GR_E_WORKSPACE); its contents need no initialisation.  Calls sharing a
- * workspace must be ordered (same stream).
+ * Limits: B <= 1024, V <= 4096, k_out <= 1024, M_in <= 65536,
+ * M_in * V < 2^31, n_loc * (bloom_k rounded up to a multiple of 4) <= 2048,
+ * w_bm <= 64, Bloom filters of at most 32768 bits (GR_E_UNSUPPORTED beyond).
+ *
+ * Workspace: device memory, 256-byte aligned, at least
+ * gr_constrain_topk_workspace(B, M_in, V, k_out) bytes (GR_E_WORKSPACE
+ * otherwise).  It must be zero-filled once before its first use (for
+ * example with hipMemsetAsync); every completed call leaves it zero-filled
+ * again, whatever the shapes of later calls.  Calls sharing a workspace must
+ * be ordered (same stream).  A workspace that was not zero-filled gives
+ * wrong selections, never an out-of-range access.
+ *
+ * The tail runs as two stages that can also be called one by one, in this
+ * order, with the same arguments and workspace:
+ *   gr_constrain      A3-A4: masks, log-softmax, scores; the survivors and
+ *                     a score histogram go to the workspace (and dbg_mask /
+ *                     dbg_scores when given);
+ *   gr_topk_reorder   A5-A6: per-request top-k from the workspace, reorder,
+ *                     all outputs.
  */
 typedef struct {
     int32_t B, M_in, V, k_out, t, L, n_loc;
@@ -266,6 +279,8 @@ typedef struct {
 
 size_t gr_constrain_topk_workspace(int32_t B, int32_t M_in, int32_t V, int32_t k_out);
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *args, void *stream);
+gr_status gr_constrain(const gr_trie *trie, const gr_tail_args *args, void *stream);
+gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *args, void *stream);
 
 /* ===================================================================== */
 /* A7: one decode step = A1 -> A2 -> A3..A6 (GRACE Sections 3.1, 3.3).   */

@@ -135,6 +135,15 @@ def test_self_attn_paged_parity(R, H, d, L, t, dt):
 # ---------------------------------------------------------------------------
 
 _TRIES = {}
+_WS = {}
+
+
+def _workspace(nbytes):
+    """One zero-filled workspace reused by every tail call of the session
+    (each call leaves it zero-filled), grown when a call needs more."""
+    if _WS.get("ws") is None or _WS["ws"].numel() < nbytes:
+        _WS["ws"] = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    return _WS["ws"]
 
 
 def _trie_case(w, seed, slice_min=0):
@@ -156,7 +165,7 @@ def _trie_case(w, seed, slice_min=0):
 
 
 def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mode="normal",
-             B=None, slice_min=0):
+             B=None, slice_min=0, staged=False):
     """Run gr_constrain_topk on synthetic beam rows at depth t and check every
     output against the oracle."""
     gr = _gr()
@@ -197,14 +206,18 @@ def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mo
                dbg_mask=torch.empty((R, (w.V + 63) // 64), dtype=torch.int64, device="cuda"),
                dbg_scores=torch.empty((R, w.V), dtype=torch.float32, device="cuda"))
     ws_bytes = gr.constrain_topk_workspace(B, M_in, w.V, k_out)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = _workspace(ws_bytes)
     args = gr.tail_args(B=B, M_in=M_in, V=w.V, k_out=k_out, t=t, L=L, n_loc=w.n_loc,
                         dtype=gr.GR_BF16 if w.dtype == "bf16" else gr.GR_F32,
                         user_bm=dev["user_bm"], user_probes=dev["user_probes"] if w.bloom_bits else None,
                         logits=dev["logits"], node_in=dev["node_in"], acc_in=dev["acc_in"],
                         tokens_in=dev["tokens_in"], table_in=dev["table_in"], ws=ws,
                         ws_bytes=ws_bytes, **out)
-    gr.constrain_topk(trie, args)
+    if staged:
+        gr.constrain(trie, args)
+        gr.topk_reorder(trie, args)
+    else:
+        gr.constrain_topk(trie, args)
     torch.cuda.synchronize()
     o = {k: v.cpu().numpy() for k, v in out.items()}
     check_tail(w, ix, view, prefix, req, node_in, acc_in, W.as_float(w, logits).astype(np.float64),
@@ -346,3 +359,18 @@ def test_constrain_topk_bloom_layouts(slice_min, name, seed, M_in, k_out, t):
     info = trie.info()
     assert (info["slice_words"] == 0) == (slice_min == -1)
     run_tail(w, seed, M_in, k_out, t, 0.1, B=2, slice_min=slice_min)
+
+
+@pytest.mark.parametrize("name,seed,M_in,k_out,t", [("main_50k", 1, 300, 1000, 1),
+                                                   ("stress_20k", 4, 512, 1024, 2)])
+def test_constrain_then_topk_reorder(name, seed, M_in, k_out, t):
+    """The two stages called one by one give the outputs of the fused call
+    (the oracle checks both), and leave the shared workspace reusable."""
+    w = TAIL_WORKLOADS[name]
+    a = run_tail(w, seed, M_in, k_out, t, 0.1, B=2, staged=True)
+    b = run_tail(w, seed, M_in, k_out, t, 0.1, B=2)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    ws = _WS["ws"]
+    lay_hist = 2048 * 1024 * 4
+    assert int(ws[:lay_hist].count_nonzero()) == 0   # histograms left zero-filled

@@ -19,7 +19,8 @@ from ._lib import GR_BF16, GR_F32, GrError, StepArgs, TailArgs, TrieParams, Trie
 
 __all__ = [
     "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged",
-    "constrain_topk_workspace", "constrain_topk", "decode_step", "version",
+    "constrain_topk_workspace", "constrain_topk", "constrain", "topk_reorder", "decode_step",
+    "version",
 ]
 
 
@@ -205,8 +206,18 @@ def tail_args(**kw) -> TailArgs:
 
 
 def constrain_topk(trie: Trie, args: TailArgs, stream=None) -> None:
-    """A3-A6 (see gr_constrain_topk)."""
+    """A3-A6 (see gr_constrain_topk).  The workspace must start zero-filled."""
     check(_lib.lib().gr_constrain_topk(trie.h, ctypes.byref(args), _stream(stream)))
+
+
+def constrain(trie: Trie, args: TailArgs, stream=None) -> None:
+    """A3-A4, the first stage of gr_constrain_topk (see gr_constrain)."""
+    check(_lib.lib().gr_constrain(trie.h, ctypes.byref(args), _stream(stream)))
+
+
+def topk_reorder(trie: Trie, args: TailArgs, stream=None) -> None:
+    """A5-A6, the second stage of gr_constrain_topk (see gr_topk_reorder)."""
+    check(_lib.lib().gr_topk_reorder(trie.h, ctypes.byref(args), _stream(stream)))
 
 
 def decode_step(trie: Trie, args: StepArgs, stream=None) -> None:

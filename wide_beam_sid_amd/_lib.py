@@ -22,7 +22,8 @@ EXPORTS = [
     "gr_trie_builder_create", "gr_trie_builder_add_ads", "gr_trie_builder_finish",
     "gr_trie_builder_destroy", "gr_trie_create", "gr_trie_host_view", "gr_trie_info",
     "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged",
-    "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_decode_step",
+    "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
+    "gr_decode_step",
 ]
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.gr_constrain_topk_workspace.argtypes = [i32, i32, i32, i32]
     L.gr_constrain_topk_workspace.restype = sz
     L.gr_constrain_topk.argtypes = [P, ctypes.POINTER(TailArgs), P]
+    L.gr_constrain.argtypes = [P, ctypes.POINTER(TailArgs), P]
+    L.gr_topk_reorder.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_decode_step.argtypes = [P, ctypes.POINTER(StepArgs), P]
     for name in EXPORTS:
         if name not in ("gr_last_error", "gr_version", "gr_trie_builder_destroy",

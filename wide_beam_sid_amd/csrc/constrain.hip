@@ -96,13 +96,6 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t f) {
 __device__ __forceinline__ float key_score(uint64_t k) { return f32_unord((uint32_t)(k >> 32)); }
 __device__ __forceinline__ uint32_t key_flat(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
 
-// Clears the score histograms of all requests (standalone gr_constrain_topk;
-// gr_decode_step has the self-attention launch do it).
-__global__ __launch_bounds__(256) void k_tail_clear(uint32_t *hist, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) hist[i] = 0u;
-}
-
 // Partial max of the live parent scores of request b held by this thread;
 // the caller reduces it over the workgroup.  Every candidate score of the
 // request is at most the full max (log-probabilities are <= 0), so the score
@@ -767,9 +760,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     }
     float U = s_ub[0];
     for (int w = 1; w < SEL_THREADS / 64; ++w) U = fmaxf(U, s_ub[w]);
-    const uint32_t *gh = p.hist + (size_t)b * NBINS;
+    uint32_t *gh = p.hist + (size_t)b * NBINS;
 
-    // 1. Exclusive prefix of the score histogram; the threshold bin is the
+    // 1. Exclusive prefix of the score histogram (read, then zeroed for the
+    //    next call: the workspace stays zero-filled between calls); the threshold bin is the
     //    one that holds the k-th best survivor.
     constexpr int PER = NBINS / SEL_THREADS;
     uint32_t c[PER];
@@ -779,6 +773,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         c[i] = gh[tid * PER + i];
         part += c[i];
     }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gh[tid * PER + i] = 0u;
+    for (int i = tid; i < MAX_K; i += SEL_THREADS) s_key[i] = 0ull;
     uint32_t inc = part;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -947,8 +944,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     const int V = p.V, L = p.L, t = p.t;
     for (int pos = tid; pos < k; pos += SEL_THREADS) {
         const size_t base = (size_t)b * k;
-        if (pos < n_sel) {
-            const uint64_t key = s_key[pos];
+        const uint64_t keyp = pos < n_sel ? s_key[pos] : 0ull;
+        const uint32_t fp = key_flat(keyp);
+        const uint32_t srcp = (uint32_t)s_src[pos];
+        // a zero key or an out-of-range survivor (only with a workspace that
+        // was not zero-filled) gives a dead slot instead of a wild read
+        if (keyp != 0ull && fp < (uint32_t)p.M_in * (uint32_t)V && srcp < (uint32_t)(gx * seg_cap)) {
+            const uint64_t key = keyp;
             int slot = pos;
             if (pos < below) {
                 const int bin = score_bin(key_score(key), U);
@@ -963,7 +965,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             const int parent = b * p.M_in + m;
             p.parent_out[sl] = parent;
             p.token_out[sl] = v;
-            p.node_out[sl] = p.schild[(size_t)b * gx * seg_cap + (uint32_t)s_src[pos]];
+            p.node_out[sl] = p.schild[(size_t)b * gx * seg_cap + srcp];
             p.acc_out[sl] = key_score(key);
             if (p.tokens_out)
                 for (int l = 0; l < L; ++l)
@@ -988,8 +990,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
 
 }  // namespace
 
-hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool hist_cleared,
-                                 hipStream_t s) {
+namespace {
+
+TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out) {
     TailParams p{};
     p.off = tr.node_offsets;
     p.child = tr.child_nodes;
@@ -1061,11 +1064,17 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool 
     while ((1 << log2_tpr) < tpr) ++log2_tpr;
     p.log2_tpr = log2_tpr;
 
-    if (!hist_cleared) {
-        const int nh = a.B * NBINS;
-        k_tail_clear<<<(nh + 255) / 256, 256, 0, s>>>(p.hist, nh);
-    }
-    dim3 g1(gx, a.B);
+    (void)gx;
+    *shm_out = shm;
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
+    size_t shm = 0;
+    const TailParams p = tail_params(tr, a, &shm);
+    dim3 g1(p.gx, a.B);
     const bool wide = tr.w_bl >= 64;
     if (a.dtype == GR_BF16) {
         if (wide) k_expand<true, true><<<g1, EXP_THREADS, shm, s>>>(p);
@@ -1074,6 +1083,12 @@ hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool 
         if (wide) k_expand<false, true><<<g1, EXP_THREADS, shm, s>>>(p);
         else k_expand<false, false><<<g1, EXP_THREADS, shm, s>>>(p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
+    size_t shm = 0;
+    const TailParams p = tail_params(tr, a, &shm);
     k_select<<<a.B, SEL_THREADS, 0, s>>>(p);
     return hipGetLastError();
 }

@@ -795,8 +795,10 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     const size_t nseg = (size_t)B * l.shape.gx;
     const size_t nsurv = nseg * (size_t)l.shape.seg_cap;
     size_t o = 0;
+    // the histograms first, at a fixed size: the region is only ever used as
+    // histograms and stays zero between calls of any shape
+    l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * MAX_B);
     l.segcnt = o; o = al(o + sizeof(uint32_t) * nseg);
-    l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * B);
     l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);
     l.schild = o; o = al(o + sizeof(int32_t) * nsurv);
     l.total = o;
@@ -818,6 +820,7 @@ static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const ch
     const TrieDev &d = trie->d;
     if (!dtype_ok(a->dtype)) return fail(GR_E_INVALID, "%s: unknown dtype %d", fn, (int)a->dtype);
     if (a->B < 1 || a->M_in < 1 || a->k_out < 1) return fail(GR_E_INVALID, "%s: B, M_in, k_out must be >= 1", fn);
+    if (a->B > MAX_B) return fail(GR_E_UNSUPPORTED, "%s: B %d > %d", fn, a->B, MAX_B);
     if (a->V != d.V) return fail(GR_E_INVALID, "%s: V %d differs from the trie's %d", fn, a->V, d.V);
     if (a->V > MAX_V) return fail(GR_E_UNSUPPORTED, "%s: V %d > %d", fn, a->V, MAX_V);
     if (a->k_out > MAX_K) return fail(GR_E_UNSUPPORTED, "%s: k_out %d > %d", fn, a->k_out, MAX_K);
@@ -846,10 +849,27 @@ static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const ch
     return GR_OK;
 }
 
+gr_status gr_constrain(const gr_trie *trie, const gr_tail_args *a, void *stream) {
+    gr_status st = check_tail(trie, a, "gr_constrain");
+    if (st) return st;
+    hipError_t e = launch_constrain(trie->d, *a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_constrain launch");
+    return GR_OK;
+}
+
+gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *a, void *stream) {
+    gr_status st = check_tail(trie, a, "gr_topk_reorder");
+    if (st) return st;
+    hipError_t e = launch_topk_reorder(trie->d, *a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_topk_reorder launch");
+    return GR_OK;
+}
+
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *stream) {
     gr_status st = check_tail(trie, a, "gr_constrain_topk");
     if (st) return st;
-    hipError_t e = launch_constrain_topk(trie->d, *a, false, (hipStream_t)stream);
+    hipError_t e = launch_constrain(trie->d, *a, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_topk_reorder(trie->d, *a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk launch");
     return GR_OK;
 }
@@ -880,14 +900,12 @@ gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *strea
     hipError_t e = launch_cross_attn(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
                                      s->d_h, a.dtype, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step cross-attention launch");
-    // the self-attention launch also clears the tail's score histograms
-    const TailWsLayout ly = tail_ws_layout(a.B, a.M_in, a.V);
     e = launch_self_attn(s->q, s->k_new, s->v_new, s->k_pool, s->v_pool, s->pool_blocks,
                          const_cast<int32_t *>(a.table_in),
-                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs,
-                         (uint32_t *)((char *)a.ws + ly.hist), (int64_t)a.B * NBINS);
+                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step self-attention launch");
-    e = launch_constrain_topk(trie->d, a, true, hs);
+    e = launch_constrain(trie->d, a, hs);
+    if (e == hipSuccess) e = launch_topk_reorder(trie->d, a, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");
     return GR_OK;
 }

@@ -51,6 +51,7 @@ struct TailShape {
     int64_t seg_cap;
 };
 constexpr int MAX_M_IN = 65536;      // beam rows per request entering the tail
+constexpr int MAX_B = 1024;          // requests per tail call (histogram region)
 constexpr int MAX_GX = 2048;         // expand workgroups per request
 inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
     const int64_t R = (int64_t)B * M_in;
@@ -75,14 +76,11 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out,
                              int B, int M, int H, int T, int d, gr_dtype dt,
                              hipStream_t s);
-// launch_self_attn can also zero n_zero words at zero_ptr in extra
-// workgroups of the same launch (the tail's histogram in gr_decode_step).
 hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t pool_blocks, int32_t *table,
                             int64_t fresh_base, int R, int t, int L, int H, int d,
-                            gr_dtype dt, void *out, hipStream_t s,
-                            uint32_t *zero_ptr = nullptr, int64_t n_zero = 0);
-hipError_t launch_constrain_topk(const TrieDev &tr, const gr_tail_args &a, bool hist_cleared,
-                                 hipStream_t s);
+                            gr_dtype dt, void *out, hipStream_t s);
+hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
+hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 
 }  // namespace gr

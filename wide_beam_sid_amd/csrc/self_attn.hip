@@ -29,8 +29,6 @@ struct SelfParams {
     int64_t fresh_base, pool_blocks;
     int R, t, L, H, d, E, G;
     float scale;
-    uint32_t *zero_ptr;   // extra workgroups past the rows zero this range
-    int64_t n_zero;
 };
 
 template <bool BF16>
@@ -64,12 +62,6 @@ template <bool BF16, int NCH>
 __global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
     using C = Chunk<BF16>;
     constexpr int VEC = C::VEC;
-    const int row_blocks = (p.R + 3) / 4;
-    if ((int)blockIdx.x >= row_blocks) {   // side job: zero a range for the next kernel
-        const int64_t z = ((int64_t)blockIdx.x - row_blocks) * 256 + threadIdx.x;
-        if (z < p.n_zero) p.zero_ptr[z] = 0u;
-        return;
-    }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = blockIdx.x * 4 + wave;
     if (i >= p.R) return;
@@ -164,7 +156,7 @@ template <bool BF16>
 hipError_t dispatch(const SelfParams &p, hipStream_t s) {
     constexpr int VEC = Chunk<BF16>::VEC;
     const int nch = (p.E / VEC + 63) / 64;
-    dim3 grid((p.R + 3) / 4 + (int)((p.n_zero + 255) / 256));
+    dim3 grid((p.R + 3) / 4);
     if (nch <= 1) k_self_attn<BF16, 1><<<grid, 256, 0, s>>>(p);
     else if (nch <= 2) k_self_attn<BF16, 2><<<grid, 256, 0, s>>>(p);
     else if (nch <= 4) k_self_attn<BF16, 4><<<grid, 256, 0, s>>>(p);
@@ -178,10 +170,8 @@ hipError_t dispatch(const SelfParams &p, hipStream_t s) {
 hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new, void *k_pool,
                             void *v_pool, int64_t pool_blocks, int32_t *table,
                             int64_t fresh_base, int R, int t, int L, int H, int d, gr_dtype dt,
-                            void *out, hipStream_t s, uint32_t *zero_ptr, int64_t n_zero) {
+                            void *out, hipStream_t s) {
     SelfParams p{};
-    p.zero_ptr = zero_ptr;
-    p.n_zero = zero_ptr ? n_zero : 0;
     p.pool_blocks = pool_blocks;
     p.q = q;
     p.k_new = k_new;

@@ -49,7 +49,7 @@ class Decoder:
         self.self_out = [torch.empty((r, H, d_h), dtype=tdt, device=dev) for r in self.rows]
         self.ws_bytes = max(constrain_topk_workspace(B, self.M[t], V, self.schedule[t])
                             for t in range(L))
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled once
         self.debug = debug
         words = (V + 63) // 64
         if debug:
