@@ -24,6 +24,7 @@ and, on request, the CPU oracle's rate on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -317,6 +318,8 @@ def main():
                     help="decodes issued per entry point for the event breakdown")
     ap.add_argument("--cpu-requests", type=int, default=-1,
                     help="requests in the oracle's sample (-1: the whole batch, 0: skip)")
+    ap.add_argument("--n-sids", type=int, default=0,
+                    help="catalog size override (0: the workload's own); per-step shapes stay")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -334,6 +337,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     w = W.WORKLOADS[args.workload]
+    if args.n_sids:
+        w = dataclasses.replace(w, n_sids=args.n_sids)
     stream = torch.cuda.Stream()
     b = Bench(w, args.seed, args.sets, stream)
     rows_per_decode = w.total_rows
