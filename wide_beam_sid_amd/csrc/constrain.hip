@@ -7,22 +7,25 @@
 // of the user's locations), Section 4.4 / Appendix A (CSR Lookup over a
 // node's child entries with deduplicated matcher rows).
 //
-// Three launches on one stream:
-//   k_tail_prep  one workgroup per request: clears the request's score
-//                histogram and counters and takes U_b = the best live parent
-//                score (every candidate score is <= U_b since log-probs <= 0).
-//   k_expand     wavefront per beam row: log-softmax over all V logits (row
-//                staged in LDS), child-entry lanes run the bitmask test then
-//                the Bloom probes with early exits, survivors are compacted
-//                per request (one atomic per wavefront and 64 entries) and
-//                binned into a 4096-bin histogram of U_b - score; the last
-//                workgroup of a request finds the bin holding the k-th best.
-//   k_select     one workgroup per request: bins above the threshold bin are
-//                in, the threshold bin is resolved exactly (LDS bitonic sort,
-//                or an MSB radix select over global memory when it is large),
-//                the k winners are sorted by (score desc, flat index asc) and
-//                the reorder writes parent / token / child node / score and
-//                the token and block-table rows of the new beams.
+// Two launches on one stream (gr_constrain, then gr_topk_reorder):
+//   k_expand   a workgroup takes up to 32 beam rows of one request: the
+//              request's bound U_b (best live parent score; every candidate
+//              is <= U_b since log-probs are <= 0), each row's log-sum-exp
+//              over all V logits, eqs 5 and 8 for every child of a node with
+//              a bit-sliced matcher block, then the child entries one per
+//              thread: eq 5 from the entry-ordered bitmask row, eq 8 for the
+//              entries still in (their Bloom rows tested by all wavefronts
+//              from a per-round list).  Survivors go to the workgroup's own
+//              segment and a 2048-bin histogram of U_b - score, merged into
+//              the request's histogram.
+//   k_select   one workgroup per request: the bin holding the k-th best
+//              survivor from the histogram (which it clears again), every
+//              survivor of a better bin, the threshold bin resolved exactly
+//              (rank by counting, bitonic sort, or an MSB radix select over
+//              global memory when it is large), the winners ordered by
+//              (score desc, flat index asc), and the reorder writes parent /
+//              token / child node / score and the token and block-table rows
+//              of the new beams.
 #include <algorithm>
 
 #include "gr_device.h"
@@ -79,6 +82,8 @@ struct TailParams {
     int mask_words;     // per-row mask words kept in LDS (debug outputs), else 0
     int tpr, log2_tpr;  // threads per row of the log-sum-exp
     int wmax;           // pass-vector words per row (bit-sliced rows), else 0
+    int vec_logits;     // bf16 logits readable 8 at a time (V % 8 == 0, 16-byte base)
+    const uint64_t *ent_bm;   // entry-ordered bitmask rows (null: gather through bmi)
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -103,10 +108,21 @@ __device__ __forceinline__ uint32_t key_flat(uint64_t k) { return 0xFFFFFFFFu - 
 // floating point) give expand and select the same bound.
 __device__ __forceinline__ float bound_part(const TailParams &p, int b) {
     float mx = -INFINITY;
-    for (int m = threadIdx.x; m < p.M_in; m += blockDim.x) {
-        const int r = b * p.M_in + m;
-        const int node = p.node_in[r];
-        if (node >= 0 && node < p.num_nodes) mx = fmaxf(mx, p.acc_in[r]);
+    const int32_t *nd = p.node_in + (size_t)b * p.M_in;
+    const float *ac = p.acc_in + (size_t)b * p.M_in;
+    const int nt = blockDim.x;
+    for (int m0 = threadIdx.x; m0 < p.M_in; m0 += 4 * nt) {
+        int32_t n4[4];
+        float a4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // every load first, then the compares
+            const int m = m0 + q * nt;
+            n4[q] = m < p.M_in ? nd[m] : -1;
+            a4[q] = m < p.M_in ? ac[m] : -INFINITY;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (n4[q] >= 0 && n4[q] < p.num_nodes) mx = fmaxf(mx, a4[q]);
     }
     return wave_max(mx);
 }
@@ -223,7 +239,11 @@ void k_expand(TailParams p) {
     __shared__ int s_nsl;
     __shared__ float s_ub[EXP_WAVES];
     __shared__ int s_nub;
-    __shared__ int32_t s_rowid[EXP_WAVES][64];     // Bloom row of each staged entry
+    __shared__ float s_ls[2][EXP_THREADS];         // round lists of entries awaiting eq 8:
+    __shared__ uint32_t s_lf[2][EXP_THREADS];      //   score, flat index m * V + v,
+    __shared__ int32_t s_lc[2][EXP_THREADS];       //   child node,
+    __shared__ int32_t s_lb[2][EXP_THREADS];       //   Bloom row (-1 once the test fails)
+    __shared__ uint32_t s_nl[2];                   // entries listed so far, per parity
 
     const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gx = gridDim.x, x = blockIdx.x;
@@ -236,7 +256,6 @@ void k_expand(TailParams p) {
     uint32_t *s_probe = (uint32_t *)(s_pass + (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1));
     int16_t *s_ubit = (int16_t *)(s_probe + nprobe);   // positions of the user's bitmask bits
     uint32_t *s_stage = s_probe + nprobe + (p.wmax ? 32 * p.w_bm : 0) + wave * p.stage_dw;
-    int32_t *rowid = s_rowid[wave];
 
     for (int i = tid; i < NBINS; i += EXP_THREADS) s_hist[i] = 0u;
     for (int i = tid; i < p.w_bm; i += EXP_THREADS) s_ubm[i] = p.user_bm[(size_t)b * p.w_bm + i];
@@ -246,7 +265,11 @@ void k_expand(TailParams p) {
         s_probe[i] = p.user_probes[((size_t)b * p.n_loc + l) * p.bloom_k + qs] & (uint32_t)(p.bloom_bits - 1);
     }
     for (int i = tid; i < p.rows_wg * p.mask_words; i += EXP_THREADS) s_mask[i] = 0ull;
-    if (tid == 0) s_nsurv = 0u;
+    if (tid == 0) {
+        s_nsurv = 0u;
+        s_nl[0] = 0u;
+        s_nl[1] = 0u;
+    }
     {
         const float ub = bound_part(p, b);
         if (lane == 0) s_ub[wave] = ub;
@@ -321,14 +344,41 @@ void k_expand(TailParams p) {
         const bool has = i < nrows && s_rstart[i + 1] > s_rstart[i];
         if (has) {
             const size_t rowoff = (size_t)(b * p.M_in + s_rm[i]) * V;
-            if (BF16 && (V & 3) == 0) {
-                const uint2 *x4 = (const uint2 *)((const uint16_t *)p.logits + rowoff);
-                for (int c = part; c < (V >> 2); c += tpr) {
-                    const uint2 u = x4[c];
-                    lse_push(__uint_as_float(u.x << 16), m, s);
-                    lse_push(__uint_as_float(u.x & 0xFFFF0000u), m, s);
-                    lse_push(__uint_as_float(u.y << 16), m, s);
-                    lse_push(__uint_as_float(u.y & 0xFFFF0000u), m, s);
+            if (BF16 && p.vec_logits) {
+                // 8 logits per 16-byte load and up to 8 loads in flight per
+                // thread; then one max and one rescaled sum per batch
+                const uint4 *x8 = (const uint4 *)((const uint16_t *)p.logits + rowoff);
+                const int nv = V >> 3;
+                for (int c0 = part; c0 < nv; c0 += 8 * tpr) {
+                    uint4 u[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int c = c0 + q * tpr;
+                        u[q] = c < nv ? x8[c] : make_uint4(0u, 0u, 0u, 0u);
+                    }
+                    float mx = m;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (c0 + q * tpr < nv) {
+                            const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+                            for (int h = 0; h < 4; ++h)
+                                mx = fmaxf(mx, fmaxf(__uint_as_float(w4[h] << 16),
+                                                     __uint_as_float(w4[h] & 0xFFFF0000u)));
+                        }
+                    if (mx == -INFINITY) continue;   // nothing finite yet
+                    float sm = m == -INFINITY ? 0.0f : s * __expf(m - mx);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (c0 + q * tpr < nv) {
+                            const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+                            for (int h = 0; h < 4; ++h)
+                                sm += __expf(__uint_as_float(w4[h] << 16) - mx) +
+                                      __expf(__uint_as_float(w4[h] & 0xFFFF0000u) - mx);
+                        }
+                    m = mx;
+                    s = sm;
                 }
             } else {
                 for (int v = part; v < V; v += tpr) lse_push(logit_at<BF16>(p.logits, rowoff + v), m, s);
@@ -486,8 +536,38 @@ void k_expand(TailParams p) {
     const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
     const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
 
-    for (int c0 = wave * 64; c0 < n_ent; c0 += EXP_THREADS) {
-        const int e = c0 + lane;
+    // A candidate that passed CD + TM with a finite score: its bin in the
+    // workgroup histogram and its (key, child) in the segment.  Called by
+    // whole wavefronts.
+    auto emit = [&](bool sel, float score, uint32_t f, int32_t ch) {
+        if (sel) atomicAdd(&s_hist[score_bin(score, U)], 1u);
+        const uint64_t bal = __ballot(sel);
+        if (bal) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
+            base = __shfl(base, 0, 64);
+            if (sel) {
+                const uint32_t idx = base + (uint32_t)__popcll(bal & lanemask_lt);
+                if (idx < (uint32_t)p.seg_cap) {
+                    skey[idx] = make_key(score, f);
+                    schild[idx] = ch;
+                }
+            }
+        }
+    };
+    auto mark = [&](int i, int v) {   // debug mask bit of row i, token v
+        atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
+    };
+
+    // Rounds of EXP_THREADS entries, one per thread (the round count is the
+    // same for every thread).  Entries that pass eq 5 and still need eq 8
+    // go to a round list; the list's Bloom tests are then shared by all
+    // wavefronts.  Lists and their counters alternate between rounds, so a
+    // round's list is never written while the previous one is read.
+    uint32_t nlb0 = 0u, nlb1 = 0u;   // list entries consumed, per parity
+    for (int c0 = 0, round = 0; c0 < n_ent; c0 += EXP_THREADS, ++round) {
+        const int par = round & 1;
+        const int e = c0 + tid;
         const bool valid = e < n_ent;
         int i = 0;
         if (valid) {  // row of entry e: the largest i with s_rstart[i] <= e
@@ -499,15 +579,22 @@ void k_expand(TailParams p) {
             }
             i = lo;
         }
-        // One round of loads for the entry, then one for what it points at.
+        // One round of loads for the entry (token, child, matcher rows or
+        // ids), then the logit.
         int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
+        uint64_t bw0 = 0ull, bw1 = 0ull;
         const bool sliced = valid && s_rblk[i] >= 0;
         if (valid) {
             j = s_roff[i] + (e - s_rstart[i]);
             v = p.tok[j];
             child = p.child[j];
             if (!sliced) {
-                bmi = p.bmi[j];
+                if (p.ent_bm) {
+                    bw0 = p.ent_bm[(size_t)j * p.w_bm];
+                    if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
+                } else {
+                    bmi = p.bmi[j];
+                }
                 if (wq) bli = p.bli[j];
             }
             m = s_rm[i];
@@ -519,8 +606,10 @@ void k_expand(TailParams p) {
             if (sliced) {  // eqs 5 and 8 came from the node's bit-sliced block
                 const int jj = e - s_rstart[i];
                 ok = (s_pass[(size_t)i * p.wmax + (jj >> 6)] >> (jj & 63)) & 1ull;
+            } else if (p.ent_bm) {
+                // eq 5: every user attribute bit present in the entry's row
+                ok = (bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (bw1 & s_ubm[1]) == s_ubm[1]);
             } else {
-                // eq 5: every user attribute bit present in the node's row
                 const uint64_t *bmr = p.bm_tab + (size_t)bmi * p.w_bm;
                 ok = true;
                 for (int w = 0; w < p.w_bm; ++w) {
@@ -532,126 +621,123 @@ void k_expand(TailParams p) {
                 }
             }
         }
-        if (wq) {
-            // eq 8: ANY user location whose probe bits are all set in the row
-            // (children of a bit-sliced node already have it in ok).
-            bool bl_ok = sliced;
-            const uint64_t need = __ballot(ok && !sliced);
-            if (!need) {
-            } else if (WIDE) {
-                const int CH = (64 * NQ) >> sh_wq;   // entries per register batch
-                const int bli_m = ((need >> lane) & 1ull) ? bli : -1;
-                const uint64_t chm = CH >= 64 ? ~0ull : ((1ull << CH) - 1ull);
-                for (int b0 = 0; b0 < 64; b0 += CH) {
-                    const uint64_t grp = (need >> b0) & chm;
-                    if (!grp) continue;
-                    const int src = __shfl(bli, (b0 + lane) & 63, 64);
-                    if (lane < CH) rowid[lane] = ((grp >> lane) & 1ull) ? src : -1;
-                    wave_lds_sync();
-                    // register q holds 8-byte word ((q * 64) mod w_bl) + lane
-                    // of entry b0 + (q * 64) / w_bl
-                    uint2 r[NQ];
+        const float score = ok ? s_acc[i] + (xv - s_lse[i]) : -INFINITY;
+        const uint32_t f = (uint32_t)(m * V + v);
+        const bool defer = wq && ok && !sliced;   // eq 8 still to test
+        if (ok && !defer && p.mask_words) mark(i, v);
+        emit(ok && !defer && score > -INFINITY, score, f, child);
+        if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
+
+        const uint64_t dm = __ballot(defer);
+        if (dm) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nl[par], (uint32_t)__popcll(dm));
+            base = __shfl(base, 0, 64) - (par ? nlb1 : nlb0);
+            if (defer) {
+                const uint32_t q = base + (uint32_t)__popcll(dm & lanemask_lt);
+                s_ls[par][q] = score;
+                s_lf[par][q] = f;
+                s_lc[par][q] = child;
+                s_lb[par][q] = bli;
+            }
+        }
+        __syncthreads();
+        const uint32_t tot = s_nl[par];
+        const int n_bl = (int)(tot - (par ? nlb1 : nlb0));
+        if (par) nlb1 = tot;
+        else nlb0 = tot;
+        if (n_bl == 0) continue;   // uniform
+
+        // eq 8 for the round's list: ANY user location whose probe bits are
+        // all set in the entry's Bloom row.  A failed entry's row id becomes -1.
+        int32_t *lb = s_lb[par];
+        if (WIDE) {
+            // CH rows per wavefront batch, loaded into registers in one round
+            // (register q holds 8-byte word ((q * 64) mod w_bl) + lane of row
+            // (q * 64) / w_bl), then moved to LDS G rows at a time.
+            const int CH = (64 * NQ) >> sh_wq;
+            for (int g0 = wave * CH; g0 < n_bl; g0 += EXP_WAVES * CH) {
+                const int nq = min(CH, n_bl - g0);
+                const int myrow = lane < nq ? lb[g0 + lane] : -1;
+                uint2 r[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    // the row id is uniform: a scalar buffer descriptor per row,
+                    // empty (loads return 0, no memory access) past the list
+                    const int g = (q << 6) >> sh_wq;
+                    const int rid = __builtin_amdgcn_readlane(myrow, g);
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(p.bl_tab + (size_t)(rid < 0 ? 0 : rid) * wq), (short)0,
+                        rid < 0 ? 0 : wq * 8, BUF_DWORD3);
+                    const auto u = __builtin_amdgcn_raw_buffer_load_b64(
+                        rs, lane * 8, ((q << 6) & (wq - 1)) * 8, 0);
+                    r[q] = make_uint2(u[0], u[1]);
+                }
+                uint64_t pm = 0ull;
+                for (int s0 = 0; s0 < nq; s0 += G) {
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
-                        // the row id is uniform: a scalar buffer descriptor per row,
-                        // empty (loads return 0, no memory access) for a skipped entry
                         const int g = (q << 6) >> sh_wq;
-                        const int rid = __builtin_amdgcn_readlane(bli_m, b0 + g);
-                        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                            (void *)(p.bl_tab + (size_t)(rid < 0 ? 0 : rid) * wq), (short)0,
-                            rid < 0 ? 0 : wq * 8, BUF_DWORD3);
-                        const auto u = __builtin_amdgcn_raw_buffer_load_b64(
-                            rs, lane * 8, ((q << 6) & (wq - 1)) * 8, 0);
-                        r[q] = make_uint2(u[0], u[1]);
-                    }
-                    for (int s0 = 0; s0 < CH; s0 += G) {
-#pragma unroll
-                        for (int q = 0; q < NQ; ++q) {
-                            const int g = (q << 6) >> sh_wq;
-                            if (g >= s0 && g < s0 + G) {   // zeros for a skipped entry
-                                uint32_t *dst = s_stage + 2 * lane +
-                                                ((g - s0) * row_dw + 2 * ((q << 6) & (wq - 1)));
-                                dst[0] = r[q].x;
-                                dst[1] = r[q].y;
-                            }
+                        if (g >= s0 && g < s0 + G) {
+                            uint32_t *dst = s_stage + 2 * lane +
+                                            ((g - s0) * row_dw + 2 * ((q << 6) & (wq - 1)));
+                            dst[0] = r[q].x;
+                            dst[1] = r[q].y;
                         }
-                        wave_lds_sync();
-                        for (int g = 0; g < G && s0 + g < CH; ++g) {
-                            if (rowid[s0 + g] < 0) continue;   // uniform
-                            if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane) &&
-                                lane == b0 + s0 + g)
-                                bl_ok = true;
-                        }
-                        wave_lds_sync();
-                    }
-                }
-            } else {
-                for (int sr = 0; sr < 64; sr += G) {
-                    const uint64_t grp = G == 64 ? need : (need >> sr) & ((1ull << G) - 1ull);
-                    if (!grp) continue;
-                    const int src = __shfl(bli, (sr + lane) & 63, 64);
-                    if (lane < G) rowid[lane] = ((grp >> lane) & 1ull) ? src : -1;
-                    wave_lds_sync();
-                    const int nld = G << sh_wq;   // 8-byte words to stage
-                    for (int base = 0; base < nld; base += 4 * 64) {
-                        uint2 u[4];
-                        int dsto[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int idx = base + q * 64 + lane;
-                            dsto[q] = -1;
-                            if (idx < nld) {
-                                const int g = idx >> sh_wq, cw = idx & (wq - 1);
-                                const int rid = rowid[g];
-                                if (rid >= 0) {
-                                    u[q] = *(const uint2 *)(p.bl_tab + (size_t)rid * wq + cw);
-                                    dsto[q] = g * row_dw + 2 * cw;
-                                }
-                            }
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (dsto[q] >= 0) {
-                                s_stage[dsto[q]] = u[q].x;
-                                s_stage[dsto[q] + 1] = u[q].y;
-                            }
                     }
                     wave_lds_sync();
-                    for (int g = 0; g < G; ++g) {
-                        if (rowid[g] < 0) continue;   // uniform
-                        if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane) &&
-                            lane == sr + g)
-                            bl_ok = true;
-                    }
+                    for (int g = 0; g < G && s0 + g < nq; ++g)
+                        if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane))
+                            pm |= 1ull << (s0 + g);
                     wave_lds_sync();
                 }
+                if (lane < nq && !((pm >> lane) & 1ull)) lb[g0 + lane] = -1;
             }
-            ok = ok && bl_ok;
-        }
-        float score = -INFINITY;
-        if (ok) {
-            score = s_acc[i] + (xv - s_lse[i]);
-            if (p.mask_words)
-                atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
-        }
-        const bool sel = ok && score > -INFINITY;
-        uint64_t key = 0;
-        if (sel) {
-            key = make_key(score, (uint32_t)(m * V + v));
-            atomicAdd(&s_hist[score_bin(score, U)], 1u);
-        }
-        const uint64_t bal = __ballot(sel);
-        if (bal) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
-            base = __shfl(base, 0, 64);
-            if (sel) {
-                const uint32_t idx = base + (uint32_t)__popcll(bal & lanemask_lt);
-                if (idx < (uint32_t)p.seg_cap) {
-                    skey[idx] = key;
-                    schild[idx] = child;
+        } else {
+            // G rows per wavefront batch, loaded straight into LDS
+            for (int g0 = wave * G; g0 < n_bl; g0 += EXP_WAVES * G) {
+                const int nq = min(G, n_bl - g0);
+                const int nld = nq << sh_wq;   // 8-byte words to stage
+                for (int base = 0; base < nld; base += 4 * 64) {
+                    uint2 u[4];
+                    int dsto[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int idx = base + q * 64 + lane;
+                        dsto[q] = -1;
+                        if (idx < nld) {
+                            const int g = idx >> sh_wq, cw = idx & (wq - 1);
+                            u[q] = *(const uint2 *)(p.bl_tab + (size_t)lb[g0 + g] * wq + cw);
+                            dsto[q] = g * row_dw + 2 * cw;
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (dsto[q] >= 0) {
+                            s_stage[dsto[q]] = u[q].x;
+                            s_stage[dsto[q] + 1] = u[q].y;
+                        }
                 }
+                wave_lds_sync();
+                uint64_t pm = 0ull;
+                for (int g = 0; g < nq; ++g)
+                    if (bloom_row_test(s_stage + g * row_dw, pr0, s_probe, p.n_loc, kp, lane))
+                        pm |= 1ull << g;
+                wave_lds_sync();
+                if (lane < nq && !((pm >> lane) & 1ull)) lb[g0 + lane] = -1;
             }
+        }
+        __syncthreads();
+        {   // the list's survivors (n_bl <= EXP_THREADS: one entry per thread)
+            const bool in = tid < n_bl;
+            const bool okq = in && lb[tid] >= 0;
+            const float sc = in ? s_ls[par][tid] : -INFINITY;
+            const uint32_t fq = in ? s_lf[par][tid] : 0u;
+            if (okq && p.mask_words) {
+                const int mq = (int)(fq / (uint32_t)V);
+                mark((mq - x) / gx, (int)(fq % (uint32_t)V));
+            }
+            emit(okq && sc > -INFINITY, sc, fq, in ? s_lc[par][tid] : 0);
         }
     }
 
@@ -1051,6 +1137,8 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.stage_dw = tr.w_bl ? G * (2 * tr.w_bl + 1) : 0;
     p.mask_words = (a.dbg_mask || a.dbg_scores) ? (a.V + 63) / 64 : 0;
     p.wmax = tr.node_slice ? (a.V + 63) / 64 : 0;
+    p.vec_logits = a.dtype == GR_BF16 && (a.V & 7) == 0 && ((uintptr_t)a.logits & 15) == 0;
+    p.ent_bm = tr.entry_bitmask;
     const int nprobe = tr.w_bl ? p.n_loc * ((tr.bloom_k + 3) & ~3) : 0;
     const size_t shm = sizeof(uint64_t) * (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1) +
                        sizeof(uint64_t) * (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1) +

@@ -349,6 +349,7 @@ static void free_trie_dev(gr_trie *t) {
     hipFree((void *)t->d.bloom_table);
     hipFree((void *)t->d.node_slice);
     hipFree((void *)t->d.slice_table);
+    hipFree((void *)t->d.entry_bitmask);
     t->d = TrieDev{};
 }
 
@@ -438,6 +439,24 @@ static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *chil
     d.bitmask_index = d_bmi;
     if ((e = upload(&d_bm, bm, (size_t)d.bm_rows * d.w_bm)) != hipSuccess) goto err;
     d.bitmask_table = d_bm;
+    if (d.w_bm <= ENTRY_BM_MAX_W && d.num_entries > 0) {
+        std::vector<uint64_t> ebm;
+        try {
+            ebm.resize((size_t)d.num_entries * d.w_bm);
+        } catch (const std::bad_alloc &) {
+            free_trie_dev(t);
+            return fail(GR_E_NOMEM, "out of host memory building the entry-ordered bitmask rows");
+        }
+        const int wb = d.w_bm;
+        uint64_t *eb = ebm.data();
+        parallel_for(d.num_entries, threads, [&](int64_t e0, int64_t e1) {
+            for (int64_t j = e0; j < e1; ++j)
+                for (int w = 0; w < wb; ++w) eb[j * wb + w] = bm[(size_t)bmi[j] * wb + w];
+        });
+        uint64_t *d_ebm;
+        if ((e = upload(&d_ebm, ebm.data(), ebm.size())) != hipSuccess) goto err;
+        d.entry_bitmask = d_ebm;
+    }
     if (d.w_bl) {
         if ((e = upload(&d_bli, bli, (size_t)d.num_entries)) != hipSuccess) goto err;
         d.bloom_index = d_bli;

@@ -29,7 +29,12 @@ struct TrieDev {
     const int64_t *node_slice;
     const uint64_t *slice_table;
     int64_t slice_words;
+    // Each child entry's bitmask row in entry order ([num_entries, w_bm];
+    // null when w_bm > ENTRY_BM_MAX_W): one contiguous read with the entry
+    // instead of a dependent gather through bitmask_index.
+    const uint64_t *entry_bitmask;
 };
+constexpr int ENTRY_BM_MAX_W = 2;
 
 // Score histogram of the top-k pre-selection: NBINS bins of width
 // 1 / BIN_SCALE nats below the best parent score of the request.
