@@ -52,6 +52,8 @@ CROSS_CASES = [
     (16, 256, 4, 64, 64, "bf16"),
     (2, 1, 8, 256, 64, "bf16"),      # one beam per request
     (1, 20, 16, 1, 128, "bf16"),     # T_ctx = 1: output = V
+    (2, 200, 2, 333, 64, "bf16"),    # 128-row workgroups, ragged last key tile
+    (1, 150, 2, 200, 32, "bf16"),    # 128-row workgroups at d_h = 32
 ]
 
 

@@ -6,9 +6,10 @@
 // request.  The flattening is request-major (row b*M + m), which is the
 // layout bijection of eqs 13-14: no data moves, only the indexing changes.
 //
-// bf16 path: one workgroup = one (request, head) and up to 128 beam rows
-// (4 wavefronts x 2 blocks of 16 rows).  Per 64-key tile, K is staged in LDS
-// row-major and V transposed; S^T = K Q^T and O^T += V^T P^T run on
+// bf16 path: one workgroup = one (request, head) and 64 or 128 beam rows
+// (4 wavefronts x 1 or 2 blocks of 16 rows).  Per 64-key tile (double
+// buffered), K is staged in LDS row-major and V transposed; S^T = K Q^T and
+// O^T += V^T P^T run on
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation and an online softmax in
 // registers.  Computing the transposed products keeps each lane on one query
 // row: its S values are exactly the B operand of the P.V product (the
@@ -22,8 +23,6 @@ namespace gr {
 namespace {
 
 constexpr int TT = 64;          // keys per LDS tile
-constexpr int RB = 2;           // 16-row blocks per wavefront
-constexpr int ROWS_WG = 4 * RB * 16;
 constexpr int PAD = 8;          // bf16 padding per LDS row
 
 union V8 {
@@ -31,23 +30,84 @@ union V8 {
     bf16x8 b;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__ q,
-                                                    const uint16_t *__restrict__ K,
-                                                    const uint16_t *__restrict__ Vv,
-                                                    uint16_t *__restrict__ out, int M, int H,
-                                                    int T, float scale_log2) {
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
+
+// One workgroup = (request b, head h, 64 * RB beam rows); wavefront w takes
+// RB blocks of 16 rows.  The K / V tiles of 64 keys are double-buffered in
+// LDS: the global loads of tile i + 1 are in flight (in registers) while
+// tile i is computed, then written to the other buffer, one barrier per
+// tile.  K is stored row-major; V transposed, two keys per 32-bit store.
+template <int D, int RB>
+__global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ K,
+                                                       const uint16_t *__restrict__ Vv,
+                                                       uint16_t *__restrict__ out, int M, int H,
+                                                       int T, float scale_log2) {
     constexpr int NDC = D / 32;   // k steps of S = Q K^T
     constexpr int NDB = D / 16;   // 16-wide blocks of d in O^T
-    __shared__ __attribute__((aligned(16))) uint16_t sK[TT][D + PAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D][TT + PAD];
+    constexpr int ROWS = 4 * RB * 16;
+    constexpr int KIT = TT * (D / 8);              // 16-byte K pieces per tile
+    constexpr int VIT = (TT / 2) * (D / 8);        // (key pair, 8 d) V pieces per tile
+    constexpr int KU = (KIT + 255) / 256, VU = (VIT + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][TT][D + PAD];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D][TT + PAD];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, a = lane & 15;
     const int b = blockIdx.z, h = blockIdx.y;
-    const int mbase = blockIdx.x * ROWS_WG + wave * RB * 16;
+    const int mbase = blockIdx.x * ROWS + wave * RB * 16;
     const size_t kvbase = ((size_t)b * H + h) * (size_t)T * D;
 
+    uint4 kr[KU], vr[VU][2];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int it = tid + u * 256, key = it / (D / 8), dc = it % (D / 8);
+            kr[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (it < KIT && t0 + key < T)
+                kr[u] = *(const uint4 *)(K + kvbase + (size_t)(t0 + key) * D + dc * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            // consecutive threads take consecutive key pairs of one 8-wide d
+            // block, so the transposed stores below fill consecutive dwords
+            const int it = tid + u * 256, dc = it / (TT / 2), kp = it % (TT / 2);
+            vr[u][0] = vr[u][1] = make_uint4(0u, 0u, 0u, 0u);
+            if (it < VIT) {
+                const int k0 = t0 + 2 * kp;
+                if (k0 < T) vr[u][0] = *(const uint4 *)(Vv + kvbase + (size_t)k0 * D + dc * 8);
+                if (k0 + 1 < T) vr[u][1] = *(const uint4 *)(Vv + kvbase + (size_t)(k0 + 1) * D + dc * 8);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int it = tid + u * 256, key = it / (D / 8), dc = it % (D / 8);
+            if (it < KIT) *(uint4 *)&sK[buf][key][dc * 8] = kr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const int it = tid + u * 256, dc = it / (TT / 2), kp = it % (TT / 2);
+            if (it < VIT) {
+                const uint32_t w0[4] = {vr[u][0].x, vr[u][0].y, vr[u][0].z, vr[u][0].w};
+                const uint32_t w1[4] = {vr[u][1].x, vr[u][1].y, vr[u][1].z, vr[u][1].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    *(uint32_t *)&sVt[buf][dc * 8 + 2 * e][2 * kp] = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+                    *(uint32_t *)&sVt[buf][dc * 8 + 2 * e + 1][2 * kp] = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+                }
+            }
+        }
+    };
+
+    load_tile(0);
     // Q^T as the B operand: lane (g, a) holds Q[row a][c*32 + g*8 .. +8].
     bf16x8 qf[RB][NDC];
 #pragma unroll
@@ -71,26 +131,12 @@ __global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    store_tile(0);
+    __syncthreads();
 
-    for (int t0 = 0; t0 < T; t0 += TT) {
-        __syncthreads();
-        for (int idx = tid; idx < TT * (D / 8); idx += 256) {
-            const int key = idx / (D / 8), dc = idx % (D / 8);
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-            if (t0 + key < T) {
-                kv = *(const uint4 *)(K + kvbase + (size_t)(t0 + key) * D + dc * 8);
-                vv = *(const uint4 *)(Vv + kvbase + (size_t)(t0 + key) * D + dc * 8);
-            }
-            *(uint4 *)&sK[key][dc * 8] = kv;
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVt[dc * 8 + 2 * e][key] = (uint16_t)(w[e] & 0xFFFFu);
-                sVt[dc * 8 + 2 * e + 1][key] = (uint16_t)(w[e] >> 16);
-            }
-        }
-        __syncthreads();
-
+    for (int t0 = 0, cur = 0; t0 < T; t0 += TT, cur ^= 1) {
+        const bool more = t0 + TT < T;
+        if (more) load_tile(t0 + TT);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // S^T block kb: lane holds S[row a][key t0 + kb*16 + g*4 + i].
@@ -101,7 +147,7 @@ __global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__
 #pragma unroll
                 for (int c = 0; c < NDC; ++c) {
                     V8 ka;
-                    ka.u = *(const uint4 *)&sK[kb * 16 + a][c * 32 + g * 8];
+                    ka.u = *(const uint4 *)&sK[cur][kb * 16 + a][c * 32 + g * 8];
                     s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[kb], 0, 0, 0);
                 }
             }
@@ -124,15 +170,14 @@ __global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__
             uint32_t pk[4][2];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                float pv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint16_t hb = f32_to_bf16(__builtin_amdgcn_exp2f(s[kb][i] - mnew));
-                    pv[i] = bf16_to_f32(hb);   // the weight the product uses
-                    lsum += pv[i];
+                for (int hp = 0; hp < 2; ++hp) {
+                    const uint32_t w = cvt_bf16x2(__builtin_amdgcn_exp2f(s[kb][2 * hp] - mnew),
+                                                  __builtin_amdgcn_exp2f(s[kb][2 * hp + 1] - mnew));
+                    // the normaliser sums the weights the product uses
+                    lsum += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+                    pk[kb][hp] = w;
                 }
-                pk[kb][0] = pack_bf16x2(pv[0], pv[1]);
-                pk[kb][1] = pack_bf16x2(pv[2], pv[3]);
             }
             lpart[rb] = lpart[rb] * alpha + lsum;
 #pragma unroll
@@ -148,14 +193,16 @@ __global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__
                 for (int db = 0; db < NDB; ++db) {
                     // A row a <-> d = (a/4)*4*NDB + db*4 + a%4
                     const int d = (a >> 2) * (4 * NDB) + db * 4 + (a & 3);
-                    const uint2 lo = *(const uint2 *)&sVt[d][(2 * pc) * 16 + g * 4];
-                    const uint2 hi = *(const uint2 *)&sVt[d][(2 * pc + 1) * 16 + g * 4];
+                    const uint2 lo = *(const uint2 *)&sVt[cur][d][(2 * pc) * 16 + g * 4];
+                    const uint2 hi = *(const uint2 *)&sVt[cur][d][(2 * pc + 1) * 16 + g * 4];
                     V8 va;
                     va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.b, pb.b, o[rb][db], 0, 0, 0);
                 }
             }
         }
+        if (more) store_tile(cur ^ 1);
+        __syncthreads();
     }
 
     // Lane (g, a) holds O[row a][d = g*4*NDB + db*4 + i].
@@ -170,8 +217,8 @@ __global__ __launch_bounds__(256) void k_cross_bf16(const uint16_t *__restrict__
         uint32_t w[2 * NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            w[2 * db] = pack_bf16x2(o[rb][db][0] * inv, o[rb][db][1] * inv);
-            w[2 * db + 1] = pack_bf16x2(o[rb][db][2] * inv, o[rb][db][3] * inv);
+            w[2 * db] = cvt_bf16x2(o[rb][db][0] * inv, o[rb][db][1] * inv);
+            w[2 * db + 1] = cvt_bf16x2(o[rb][db][2] * inv, o[rb][db][3] * inv);
         }
         uint16_t *dst = out + (((size_t)b * M + m) * H + h) * D + g * 4 * NDB;
 #pragma unroll
@@ -219,12 +266,25 @@ hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *
         return hipGetLastError();
     }
     const float sl2 = 1.4426950408889634f / sqrtf((float)d);
-    dim3 grid((M + ROWS_WG - 1) / ROWS_WG, H, B);
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *oo = (uint16_t *)out;
-    if (d == 32) k_cross_bf16<32><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
-    else if (d == 64) k_cross_bf16<64><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
-    else k_cross_bf16<128><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
+    // long key loops amortise the per-workgroup tile loads over 128 rows;
+    // short ones take 64 rows per workgroup for more workgroups in flight
+    // (d_h = 128 always: 128 rows would not fit the registers of two waves
+    // per SIMD)
+    const bool big = T > 2 * TT && d <= 64;
+    dim3 grid((M + (big ? 127 : 63)) / (big ? 128 : 64), H, B);
+#define GR_CROSS(DD)                                                                          \
+    if (big) k_cross_bf16<DD, 2><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);          \
+    else k_cross_bf16<DD, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
+    if (d == 32) {
+        GR_CROSS(32)
+    } else if (d == 64) {
+        GR_CROSS(64)
+    } else {
+        k_cross_bf16<128, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
+    }
+#undef GR_CROSS
     return hipGetLastError();
 }
 
