@@ -235,9 +235,10 @@ def algorithmic_units(b: Bench):
         ent_bytes = 10 + (4 if w.bloom_bits else 0)
         n_sel = int((d.parent[t].cpu().numpy() >= 0).sum())
         # gr_constrain: logits of live rows, node/acc, user rows, CSR entries,
-        # distinct matcher rows, survivors written (8-byte key + 4-byte child)
+        # distinct matcher rows, survivors written (8-byte key, 4-byte child,
+        # 2-byte bin)
         con_b = (int(live.sum()) * w.V * es + R * 8 + w.B * (8 * w.w_bm + w.n_loc * w.bloom_k * 4)
-                 + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl + 12 * surv[t])
+                 + n_ent * ent_bytes + n_bm * 8 * w.w_bm + n_bl * 8 * w.w_bl + 14 * surv[t])
         # gr_topk_reorder: survivor keys, the winners' child ids, outputs and
         # the parents' token / block-table rows
         sel_b = 8 * surv[t] + 4 * n_sel + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4
@@ -391,6 +392,20 @@ def main():
         torch.cuda.synchronize()
         warm_elapsed = time.perf_counter() - t0w
 
+        # The same decodes replayed as HIP graphs (one graph per input set,
+        # each capturing all L steps of gr_decode_step).
+        graphs = [b.gr.DecodeGraph(b.trie, b.args[s], stream) for s in range(args.sets)]
+        for i in range(args.warmup):
+            graphs[i % args.sets].launch(stream)
+        torch.cuda.synchronize()
+        t0g = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % args.sets].launch(stream)
+        torch.cuda.synchronize()
+        graph_elapsed = time.perf_counter() - t0g
+        for g in graphs:
+            g.close()
+
         # Entry-point breakdown: the same decodes issued call by call with
         # events around each call; a spin kernel first lets the host queue
         # run ahead so that no gap of host time sits inside an event pair.
@@ -487,6 +502,8 @@ def main():
                             "decode_p50_us": float(np.percentile(dec_ms, 50)) * 1e3,
                             "decode_p99_us": float(np.percentile(dec_ms, 99)) * 1e3},
         "warm_value": rows_per_decode * args.steps / warm_elapsed,
+        "graph": {"value": rows_per_decode * args.steps / graph_elapsed,
+                  "ms_per_step": graph_elapsed / args.steps * 1e3},
         "per_step": steps_tab,
         "roofline": roof,
         "cpu_baseline": None,

@@ -306,6 +306,33 @@ typedef struct {
 
 gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *args, void *stream);
 
+/* ===================================================================== */
+/* A whole decode as one HIP graph (GRACE Section 3.1: the decode loop is */
+/* captured once and replayed, so the per-step launches cost no host      */
+/* round trips).                                                           */
+/* ===================================================================== */
+/*
+ * gr_decode_graph_create captures n_steps consecutive gr_decode_step calls
+ * (steps[t] exactly as for gr_decode_step, t = 0..n_steps-1) issued on
+ * `stream` into a HIP graph and instantiates it.  Nothing runs during
+ * creation.  Every pointer in steps[] is baked into the graph: each launch
+ * reads and writes exactly those caller-owned buffers, so the caller
+ * refreshes inputs in place between launches and keeps the buffers alive
+ * while the graph exists.  `stream` must be a created stream (not the
+ * legacy default stream) that is not already capturing.  As for
+ * gr_constrain_topk, the tail workspaces are zero-filled before the first
+ * launch and every completed launch leaves them zeroed.
+ * Errors: GR_E_INVALID for bad arguments (every step is validated as by
+ * gr_decode_step, before anything is captured), GR_E_HIP when capture or
+ * instantiation fails; *out is NULL then.  The graph owns no buffer;
+ * gr_decode_graph_destroy frees the graph itself (NULL is a no-op).
+ */
+typedef struct gr_graph gr_graph;
+gr_status gr_decode_graph_create(const gr_trie *trie, const gr_step_args *steps,
+                                 int32_t n_steps, void *stream, gr_graph **out);
+gr_status gr_decode_graph_launch(const gr_graph *graph, void *stream);
+void gr_decode_graph_destroy(gr_graph *graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,3 +141,15 @@ def test_trie_builder_matches_oracle_unions(name, w, seed):
     if name == "main_20k":
         # single-child chains share rows: fewer rows than non-root nodes
         assert v["bl_rows"] < v["num_entries"]
+
+
+def test_decode_graph_argument_errors_without_capture():
+    L = _lib.lib()
+    out = ctypes.c_void_p(123)
+    # no steps, no trie, no out: rejected before any stream or capture call
+    assert L.gr_decode_graph_create(None, None, 0, ctypes.c_void_p(16), ctypes.byref(out)) \
+        == _lib.GR_E_INVALID
+    assert out.value is None
+    assert L.gr_decode_graph_create(None, None, 1, ctypes.c_void_p(16), None) == _lib.GR_E_INVALID
+    assert L.gr_decode_graph_launch(None, None) == _lib.GR_E_INVALID
+    L.gr_decode_graph_destroy(None)   # no-op

@@ -20,7 +20,7 @@ from ._lib import GR_BF16, GR_F32, GrError, StepArgs, TailArgs, TrieParams, Trie
 __all__ = [
     "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged",
     "constrain_topk_workspace", "constrain_topk", "constrain", "topk_reorder", "decode_step",
-    "version",
+    "DecodeGraph", "version",
 ]
 
 
@@ -223,3 +223,32 @@ def topk_reorder(trie: Trie, args: TailArgs, stream=None) -> None:
 def decode_step(trie: Trie, args: StepArgs, stream=None) -> None:
     """A1 -> A2 -> A3..A6 for one step (see gr_decode_step)."""
     check(_lib.lib().gr_decode_step(trie.h, ctypes.byref(args), _stream(stream)))
+
+
+class DecodeGraph:
+    """A whole decode (consecutive gr_decode_step calls) captured once as a
+    HIP graph (see gr_decode_graph_create); launch() replays it on a stream.
+    The step arguments' buffers are baked in and must stay alive."""
+
+    def __init__(self, trie: Trie, steps, stream):
+        arr = (StepArgs * len(steps))(*steps)
+        h = ctypes.c_void_p()
+        check(_lib.lib().gr_decode_graph_create(trie.h, arr, len(steps), _stream(stream),
+                                                ctypes.byref(h)))
+        self.h = h
+        self.trie = trie      # the graph reads the trie's device arrays
+
+    def launch(self, stream=None) -> None:
+        check(_lib.lib().gr_decode_graph_launch(self.h, _stream(stream)))
+
+    def close(self) -> None:
+        h = getattr(self, "h", None)
+        if h is not None and h.value:
+            _lib.lib().gr_decode_graph_destroy(h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

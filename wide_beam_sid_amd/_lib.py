@@ -23,7 +23,8 @@ EXPORTS = [
     "gr_trie_builder_destroy", "gr_trie_create", "gr_trie_host_view", "gr_trie_info",
     "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged",
     "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
-    "gr_decode_step",
+    "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
+    "gr_decode_graph_destroy",
 ]
 
 
@@ -102,9 +103,14 @@ def lib() -> ctypes.CDLL:
     L.gr_constrain.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_topk_reorder.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_decode_step.argtypes = [P, ctypes.POINTER(StepArgs), P]
+    L.gr_decode_graph_create.argtypes = [P, ctypes.POINTER(StepArgs), i32, P, ctypes.POINTER(P)]
+    L.gr_decode_graph_launch.argtypes = [P, P]
+    L.gr_decode_graph_destroy.argtypes = [P]
+    L.gr_decode_graph_destroy.restype = None
     for name in EXPORTS:
         if name not in ("gr_last_error", "gr_version", "gr_trie_builder_destroy",
-                        "gr_trie_destroy", "gr_constrain_topk_workspace"):
+                        "gr_trie_destroy", "gr_constrain_topk_workspace",
+                        "gr_decode_graph_destroy"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

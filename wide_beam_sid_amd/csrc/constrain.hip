@@ -42,6 +42,7 @@ constexpr int MAX_KP = 8;             // probes per location held in registers (
 constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
 constexpr int BND_CAP = 2048;         // threshold-bin entries buffered in LDS
+constexpr uint32_t BIN_SCAN_MIN = 16 * SEL_THREADS;   // survivors from which select reads bins first
 
 struct TailParams {
     const int32_t *off;
@@ -72,6 +73,7 @@ struct TailParams {
     uint32_t *hist;
     uint64_t *skey;     // survivor segments [B, gx, seg_cap]
     int32_t *schild;
+    uint16_t *sbin;     // each survivor's histogram bin (0xFFFF: a pad)
     int64_t seg_cap;
     int gx;
     // expand launch shape
@@ -84,6 +86,7 @@ struct TailParams {
     int wmax;           // pass-vector words per row (bit-sliced rows), else 0
     int vec_logits;     // bf16 logits readable 8 at a time (V % 8 == 0, 16-byte base)
     const uint64_t *ent_bm;   // entry-ordered bitmask rows (null: gather through bmi)
+    int vec_rows;             // token / block-table rows movable as 16-byte pieces
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -141,6 +144,11 @@ __device__ __forceinline__ void lse_push(float x, float &m, float &s) {
     } else {
         s += __expf(x - m);
     }
+}
+
+// Set bits of a ballot in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
@@ -229,6 +237,7 @@ void k_expand(TailParams p) {
     __shared__ uint32_t s_hist[NBINS];
     __shared__ uint64_t s_ubm[MAX_WBM];
     __shared__ int32_t s_rstart[MAX_ROWS_WG + 1];  // prefix sums of child counts
+    __shared__ int32_t s_nstart[MAX_ROWS_WG + 1];  // the same over rows without a block
     __shared__ int32_t s_roff[MAX_ROWS_WG];        // first CSR entry of the row's node
     __shared__ int32_t s_rm[MAX_ROWS_WG];          // beam index m of the row
     __shared__ float s_lse[MAX_ROWS_WG];
@@ -323,9 +332,50 @@ void k_expand(TailParams p) {
         const uint64_t sl = __ballot(lane < nrows && cnt > 0 && s_rblk[lane < nrows ? lane : 0] >= 0);
         if ((sl >> lane) & 1ull) s_slist[__popcll(sl & ((1ull << lane) - 1ull))] = lane;
         if (lane == 0) s_nsl = __popcll(sl);
+        // prefix over the rows without a block: their entries go through the rounds
+        int inc2 = ((sl >> lane) & 1ull) ? 0 : cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc2, o, 64);
+            if (lane >= o) inc2 += y;
+        }
+        if (lane < nrows) s_nstart[lane + 1] = inc2;
+        if (lane == 0) s_nstart[0] = 0;
     }
     __syncthreads();
     const float U = fmaxf(fmaxf(s_ub[0], s_ub[1]), fmaxf(s_ub[2], s_ub[3]));
+    // this workgroup's survivor segment: slots come from an LDS counter
+    uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
+    int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
+    uint16_t *sbin = p.sbin + ((size_t)b * gx + x) * p.seg_cap;
+    const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
+    const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
+
+    // A candidate that passed CD + TM with a finite score: its bin in the
+    // workgroup histogram and its (key, child) in the segment.  Called by
+    // whole wavefronts.
+    auto emit = [&](bool sel, float score, uint32_t f, int32_t ch) {
+        const int bin = score_bin(score, U);
+        if (sel) atomicAdd(&s_hist[bin], 1u);
+        const uint64_t bal = __ballot(sel);
+        if (bal) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
+            base = __shfl(base, 0, 64);
+            if (sel) {
+                const uint32_t idx = base + lanes_below(bal);
+                if (idx < (uint32_t)p.seg_cap) {
+                    skey[idx] = make_key(score, f);
+                    schild[idx] = ch;
+                    sbin[idx] = (uint16_t)bin;
+                }
+            }
+        }
+    };
+    auto mark = [&](int i, int v) {   // debug mask bit of row i, token v
+        atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
+    };
+
     // lane l's location l: its probe positions, kept in registers
     uint4 pr0[MAX_KP / 4];
 #pragma unroll
@@ -392,6 +442,7 @@ void k_expand(TailParams p) {
         }
         if (i < nrows && part == 0) s_lse[i] = has ? m + __logf(s) : 0.0f;
     }
+    __syncthreads();
 
     // eqs 5 and 8 for every child of a node with a bit-sliced block, one
     // wavefront per row.  Eq 5: AND of the columns of the user's attribute
@@ -442,8 +493,7 @@ void k_expand(TailParams p) {
                 uint64_t pass = wave_and64(bm);
                 if (p.w_bl) pass &= wave_or64(acc);
                 if (lane == 0) s_pass[(size_t)i * p.wmax] = pass;
-                continue;
-            }
+            } else {
             const bool even = (wc & 1) == 0;
             for (int w0 = 0; w0 < wc; w0 += 4) {
                 const int n = min(4, wc - w0);
@@ -524,57 +574,60 @@ void k_expand(TailParams p) {
                     s_pass[(size_t)i * p.wmax + w0 + lane] = x;
                 }
             }
+            }
+            wave_lds_sync();
+            // The row's candidates: the children whose pass bit is set, 64
+            // per chunk and up to 4 chunks of loads in flight.
+            const int off0 = s_roff[i], m = s_rm[i];
+            const float acc = s_acc[i], lse = s_lse[i];
+            const size_t lrow = (size_t)(b * p.M_in + m) * V;
+            const uint64_t *pw = s_pass + (size_t)i * p.wmax;
+            for (int u0 = 0; u0 < wc; u0 += 4) {
+                int tk[4], ch[4];
+                bool okc[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int u = u0 + q, jj = u * 64 + lane;
+                    okc[q] = u < wc && jj < c && ((pw[u < wc ? u : 0] >> lane) & 1ull);
+                    tk[q] = 0;
+                    ch[q] = 0;
+                    if (okc[q]) {
+                        tk[q] = p.tok[off0 + jj];
+                        ch[q] = p.child[off0 + jj];
+                    }
+                }
+                float xv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[q] = okc[q] ? logit_at<BF16>(p.logits, lrow + tk[q]) : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (u0 + q >= wc) break;   // uniform
+                    const float sc = okc[q] ? acc + (xv[q] - lse) : -INFINITY;
+                    if (okc[q] && p.mask_words) mark(i, tk[q]);
+                    emit(okc[q] && sc > -INFINITY, sc, (uint32_t)(m * V + tk[q]), ch[q]);
+                }
+            }
         }
     }
     __syncthreads();
 
-    const int n_ent = s_rstart[nrows];
-    const uint64_t lanemask_lt = (1ull << lane) - 1ull;
-    // this workgroup's survivor segment: slots come from an LDS counter
-    uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
-    int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
-    const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
-    const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
-
-    // A candidate that passed CD + TM with a finite score: its bin in the
-    // workgroup histogram and its (key, child) in the segment.  Called by
-    // whole wavefronts.
-    auto emit = [&](bool sel, float score, uint32_t f, int32_t ch) {
-        if (sel) atomicAdd(&s_hist[score_bin(score, U)], 1u);
-        const uint64_t bal = __ballot(sel);
-        if (bal) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
-            base = __shfl(base, 0, 64);
-            if (sel) {
-                const uint32_t idx = base + (uint32_t)__popcll(bal & lanemask_lt);
-                if (idx < (uint32_t)p.seg_cap) {
-                    skey[idx] = make_key(score, f);
-                    schild[idx] = ch;
-                }
-            }
-        }
-    };
-    auto mark = [&](int i, int v) {   // debug mask bit of row i, token v
-        atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
-    };
-
-    // Rounds of EXP_THREADS entries, one per thread (the round count is the
-    // same for every thread).  Entries that pass eq 5 and still need eq 8
+    // The entries of rows without a bit-sliced block: rounds of EXP_THREADS
+    // entries, one per thread (the round count is the same for every thread).  Entries that pass eq 5 and still need eq 8
     // go to a round list; the list's Bloom tests are then shared by all
     // wavefronts.  Lists and their counters alternate between rounds, so a
     // round's list is never written while the previous one is read.
     uint32_t nlb0 = 0u, nlb1 = 0u;   // list entries consumed, per parity
+    const int n_ent = s_nstart[nrows];
     for (int c0 = 0, round = 0; c0 < n_ent; c0 += EXP_THREADS, ++round) {
         const int par = round & 1;
         const int e = c0 + tid;
         const bool valid = e < n_ent;
         int i = 0;
-        if (valid) {  // row of entry e: the largest i with s_rstart[i] <= e
+        if (valid) {  // row of entry e: the largest i with s_nstart[i] <= e
             int lo = 0, hi = nrows;
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
-                if (s_rstart[mid] <= e) lo = mid;
+                if (s_nstart[mid] <= e) lo = mid;
                 else hi = mid;
             }
             i = lo;
@@ -583,30 +636,24 @@ void k_expand(TailParams p) {
         // ids), then the logit.
         int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
         uint64_t bw0 = 0ull, bw1 = 0ull;
-        const bool sliced = valid && s_rblk[i] >= 0;
         if (valid) {
-            j = s_roff[i] + (e - s_rstart[i]);
+            j = s_roff[i] + (e - s_nstart[i]);
             v = p.tok[j];
             child = p.child[j];
-            if (!sliced) {
-                if (p.ent_bm) {
-                    bw0 = p.ent_bm[(size_t)j * p.w_bm];
-                    if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
-                } else {
-                    bmi = p.bmi[j];
-                }
-                if (wq) bli = p.bli[j];
+            if (p.ent_bm) {
+                bw0 = p.ent_bm[(size_t)j * p.w_bm];
+                if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
+            } else {
+                bmi = p.bmi[j];
             }
+            if (wq) bli = p.bli[j];
             m = s_rm[i];
         }
         bool ok = false;
         float xv = 0.0f;
         if (valid) {
             xv = logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
-            if (sliced) {  // eqs 5 and 8 came from the node's bit-sliced block
-                const int jj = e - s_rstart[i];
-                ok = (s_pass[(size_t)i * p.wmax + (jj >> 6)] >> (jj & 63)) & 1ull;
-            } else if (p.ent_bm) {
+            if (p.ent_bm) {
                 // eq 5: every user attribute bit present in the entry's row
                 ok = (bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (bw1 & s_ubm[1]) == s_ubm[1]);
             } else {
@@ -623,7 +670,7 @@ void k_expand(TailParams p) {
         }
         const float score = ok ? s_acc[i] + (xv - s_lse[i]) : -INFINITY;
         const uint32_t f = (uint32_t)(m * V + v);
-        const bool defer = wq && ok && !sliced;   // eq 8 still to test
+        const bool defer = wq && ok;   // eq 8 still to test
         if (ok && !defer && p.mask_words) mark(i, v);
         emit(ok && !defer && score > -INFINITY, score, f, child);
         if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
@@ -634,7 +681,7 @@ void k_expand(TailParams p) {
             if (lane == 0) base = atomicAdd(&s_nl[par], (uint32_t)__popcll(dm));
             base = __shfl(base, 0, 64) - (par ? nlb1 : nlb0);
             if (defer) {
-                const uint32_t q = base + (uint32_t)__popcll(dm & lanemask_lt);
+                const uint32_t q = base + lanes_below(dm);
                 s_ls[par][q] = score;
                 s_lf[par][q] = f;
                 s_lc[par][q] = child;
@@ -761,10 +808,14 @@ void k_expand(TailParams p) {
     // segment's count; k_select reads both after the kernel boundary, so no
     // device-scope fence is needed here.
     __syncthreads();
-    if (tid == 0) {
-        uint32_t n = min(s_nsurv, (uint32_t)p.seg_cap);
-        if (n & 1u) skey[n++] = 0ull;   // pad to a key pair (seg_cap is even)
-        p.segcnt[(size_t)b * gx + x] = n;
+    {   // pad the segment to a multiple of 8 (seg_cap is one)
+        const uint32_t n = min(s_nsurv, (uint32_t)p.seg_cap);
+        const uint32_t n8 = (n + 7u) & ~7u;
+        if ((uint32_t)tid < n8 - n) {
+            skey[n + tid] = 0ull;
+            sbin[n + tid] = 0xFFFFu;
+        }
+        if (tid == 0) p.segcnt[(size_t)b * gx + x] = n8;
     }
     uint32_t *gh = p.hist + (size_t)b * NBINS;
     for (int i = tid; i < NBINS; i += EXP_THREADS) {
@@ -816,20 +867,27 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_ub[SEL_THREADS / 64];
-    {
-        const float ub = bound_part(p, b);
-        if (lane == 0) s_ub[wave] = ub;
-    }
     const int k = p.k_out;
     // survivors of request b: segment x holds segcnt[b, x] keys at
     // keys + x * seg_cap; a survivor is named by its offset in the request
     const int gx = p.gx;
     const uint64_t seg_cap = (uint64_t)p.seg_cap;
     const uint64_t *keys = p.skey + (size_t)b * gx * seg_cap;
-    {   // exclusive prefix of the segment counts (gx <= 2 * SEL_THREADS)
-        const uint32_t *cnt = p.segcnt + (size_t)b * gx;
-        const uint32_t c0 = 2 * tid < gx ? cnt[2 * tid] : 0u;
-        const uint32_t c1 = 2 * tid + 1 < gx ? cnt[2 * tid + 1] : 0u;
+    uint32_t *gh = p.hist + (size_t)b * NBINS;
+    // The segment counts and this thread's histogram bins are loaded before
+    // the bound's rows, so the three reads share one round trip.
+    const uint32_t *cnt = p.segcnt + (size_t)b * gx;
+    const uint32_t c0 = 2 * tid < gx ? cnt[2 * tid] : 0u;       // gx <= 2 * SEL_THREADS
+    const uint32_t c1 = 2 * tid + 1 < gx ? cnt[2 * tid + 1] : 0u;
+    constexpr int PER = NBINS / SEL_THREADS;
+    uint32_t c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = gh[tid * PER + i];
+    {
+        const float ub = bound_part(p, b);
+        if (lane == 0) s_ub[wave] = ub;
+    }
+    {   // exclusive prefix of the segment counts
         uint32_t sinc = c0 + c1;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -846,19 +904,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     }
     float U = s_ub[0];
     for (int w = 1; w < SEL_THREADS / 64; ++w) U = fmaxf(U, s_ub[w]);
-    uint32_t *gh = p.hist + (size_t)b * NBINS;
 
-    // 1. Exclusive prefix of the score histogram (read, then zeroed for the
-    //    next call: the workspace stays zero-filled between calls); the threshold bin is the
-    //    one that holds the k-th best survivor.
-    constexpr int PER = NBINS / SEL_THREADS;
-    uint32_t c[PER];
+    // 1. Exclusive prefix of the score histogram (read above, zeroed here
+    //    for the next call: the workspace stays zero-filled between calls);
+    //    the threshold bin is the one that holds the k-th best survivor.
     uint32_t part = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = gh[tid * PER + i];
-        part += c[i];
-    }
+    for (int i = 0; i < PER; ++i) part += c[i];
 #pragma unroll
     for (int i = 0; i < PER; ++i) gh[tid * PER + i] = 0u;
     for (int i = tid; i < MAX_K; i += SEL_THREADS) s_key[i] = 0ull;
@@ -906,10 +958,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         return (uint32_t)(lo * seg_cap) + (f - s_segpre[lo]);
     };
 
-    // 2. Survivors of bins below the threshold go to their bin's segment;
-    //    members of the threshold bin are buffered.
-    // Survivors are read as 16-byte key pairs (segment counts are even), 8
-    // pairs in flight per thread; zero keys are the segments' pads.
+    // 2. Survivors of bins below the threshold go to their bin's slots;
+    //    members of the threshold bin are buffered.  Zero keys are the
+    //    segments' pads.
     auto take = [&](uint64_t key, uint32_t src) {
         if (key == 0ull) return;
         const int bin = score_bin(key_score(key), U);
@@ -927,21 +978,52 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             }
         }
     };
-    const uint32_t n_pairs = n_surv >> 1;
-    for (uint32_t p0 = 0; p0 < n_pairs; p0 += 8 * SEL_THREADS) {
-        uint32_t src[8];
-        uint4 kv[8];
+    if (n_surv >= BIN_SCAN_MIN) {
+        // Many survivors: their bins are read 8 at a time (16 bytes, 4 groups
+        // in flight per thread) and only the keys of bins at or below the
+        // threshold bin are fetched; pads carry bin 0xFFFF.
+        const uint16_t *bins = p.sbin + (size_t)b * gx * seg_cap;
+        const uint32_t n_oct = n_surv >> 3;
+        for (uint32_t o0 = 0; o0 < n_oct; o0 += 4 * SEL_THREADS) {
+            uint32_t src[4];
+            uint4 bv[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint32_t pp = p0 + u * SEL_THREADS + tid;
-            src[u] = pp < n_pairs ? surv(2 * pp) : 0xFFFFFFFFu;
-            kv[u] = pp < n_pairs ? *(const uint4 *)(keys + src[u]) : make_uint4(0u, 0u, 0u, 0u);
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t oo = o0 + u * SEL_THREADS + tid;
+                src[u] = oo < n_oct ? surv(8 * oo) : 0xFFFFFFFFu;
+                bv[u] = oo < n_oct ? *(const uint4 *)(bins + src[u])
+                                   : make_uint4(~0u, ~0u, ~0u, ~0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (src[u] == 0xFFFFFFFFu) continue;
+                const uint32_t wv[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int bn = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                    if (bn <= thr) take(keys[src[u] + e], src[u] + e);
+                }
+            }
         }
+    } else {
+        // Pairs are read coalesced (consecutive threads take consecutive
+        // pairs), 8 pairs in flight per thread.
+        const uint32_t n_pairs = n_surv >> 1;
+        for (uint32_t p0 = 0; p0 < n_pairs; p0 += 8 * SEL_THREADS) {
+            uint32_t src[8];
+            uint4 kv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (src[u] == 0xFFFFFFFFu) continue;
-            take((uint64_t)kv[u].x | ((uint64_t)kv[u].y << 32), src[u]);
-            take((uint64_t)kv[u].z | ((uint64_t)kv[u].w << 32), src[u] + 1);
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t pp = p0 + u * SEL_THREADS + tid;
+                src[u] = pp < n_pairs ? surv(2 * pp) : 0xFFFFFFFFu;
+                kv[u] = pp < n_pairs ? *(const uint4 *)(keys + src[u]) : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (src[u] == 0xFFFFFFFFu) continue;
+                take((uint64_t)kv[u].x | ((uint64_t)kv[u].y << 32), src[u]);
+                take((uint64_t)kv[u].z | ((uint64_t)kv[u].w << 32), src[u] + 1);
+            }
         }
     }
     __syncthreads();
@@ -1053,13 +1135,30 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             p.token_out[sl] = v;
             p.node_out[sl] = p.schild[(size_t)b * gx * seg_cap + srcp];
             p.acc_out[sl] = key_score(key);
-            if (p.tokens_out)
-                for (int l = 0; l < L; ++l)
-                    p.tokens_out[sl * L + l] =
-                        l < t ? p.tokens_in[(size_t)parent * L + l] : (l == t ? v : -1);
-            if (p.table_out)
-                for (int l = 0; l < L; ++l)
-                    p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
+            if (p.vec_rows) {   // rows of L int32 as 16-byte pieces
+                for (int l0 = 0; l0 < L; l0 += 4) {
+                    int4 tk = make_int4(-1, -1, -1, -1), tb = tk;
+                    if (p.tokens_out && l0 < t) tk = *(const int4 *)(p.tokens_in + (size_t)parent * L + l0);
+                    if (p.table_out && l0 <= t) tb = *(const int4 *)(p.table_in + (size_t)parent * L + l0);
+                    int *tkv = (int *)&tk, *tbv = (int *)&tb;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int l = l0 + e;
+                        tkv[e] = l < t ? tkv[e] : (l == t ? v : -1);
+                        tbv[e] = l <= t ? tbv[e] : -1;
+                    }
+                    if (p.tokens_out) *(int4 *)(p.tokens_out + sl * L + l0) = tk;
+                    if (p.table_out) *(int4 *)(p.table_out + sl * L + l0) = tb;
+                }
+            } else {
+                if (p.tokens_out)
+                    for (int l = 0; l < L; ++l)
+                        p.tokens_out[sl * L + l] =
+                            l < t ? p.tokens_in[(size_t)parent * L + l] : (l == t ? v : -1);
+                if (p.table_out)
+                    for (int l = 0; l < L; ++l)
+                        p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
+            }
         } else {
             const size_t sl = base + pos;
             p.parent_out[sl] = -1;
@@ -1122,6 +1221,7 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.hist = (uint32_t *)(ws + ly.hist);
     p.skey = (uint64_t *)(ws + ly.skey);
     p.schild = (int32_t *)(ws + ly.schild);
+    p.sbin = (uint16_t *)(ws + ly.sbin);
     p.seg_cap = ly.shape.seg_cap;
     p.gx = ly.shape.gx;
 
@@ -1139,6 +1239,9 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.wmax = tr.node_slice ? (a.V + 63) / 64 : 0;
     p.vec_logits = a.dtype == GR_BF16 && (a.V & 7) == 0 && ((uintptr_t)a.logits & 15) == 0;
     p.ent_bm = tr.entry_bitmask;
+    auto al16 = [](const void *x) { return ((uintptr_t)x & 15) == 0; };
+    p.vec_rows = (a.L & 3) == 0 && al16(a.tokens_in) && al16(a.tokens_out) && al16(a.table_in) &&
+                 al16(a.table_out);
     const int nprobe = tr.w_bl ? p.n_loc * ((tr.bloom_k + 3) & ~3) : 0;
     const size_t shm = sizeof(uint64_t) * (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1) +
                        sizeof(uint64_t) * (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1) +

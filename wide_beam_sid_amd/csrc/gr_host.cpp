@@ -820,6 +820,7 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     l.segcnt = o; o = al(o + sizeof(uint32_t) * nseg);
     l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);
     l.schild = o; o = al(o + sizeof(int32_t) * nsurv);
+    l.sbin = o;   o = al(o + sizeof(uint16_t) * nsurv);
     l.total = o;
     return l;
 }
@@ -893,7 +894,8 @@ gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *st
     return GR_OK;
 }
 
-gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
+// Validation of one decode step; nothing is launched.
+static gr_status check_step(const gr_trie *trie, const gr_step_args *s) {
     if (!trie || !s) return fail(GR_E_INVALID, "gr_decode_step: null argument");
     const gr_tail_args &a = s->tail;
     gr_status st = check_tail(trie, &a, "gr_decode_step");
@@ -915,6 +917,12 @@ gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *strea
     const int vec = a.dtype == GR_BF16 ? 4 : 2;
     if (s->d_h % vec || (int64_t)s->H * s->d_h > 64 * vec * 16)
         return fail(GR_E_UNSUPPORTED, "gr_decode_step: H*d_h unsupported for self-attention");
+    return GR_OK;
+}
+
+static gr_status launch_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
+    const gr_tail_args &a = s->tail;
+    const int R = a.B * a.M_in;
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e = launch_cross_attn(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
                                      s->d_h, a.dtype, hs);
@@ -927,6 +935,77 @@ gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *strea
     if (e == hipSuccess) e = launch_topk_reorder(trie->d, a, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");
     return GR_OK;
+}
+
+
+gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
+    gr_status st = check_step(trie, s);
+    if (st) return st;
+    return launch_step(trie, s, stream);
+}
+
+struct gr_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int device = 0;
+};
+
+gr_status gr_decode_graph_create(const gr_trie *trie, const gr_step_args *steps, int32_t n_steps,
+                                 void *stream, gr_graph **out) {
+    if (!out) return fail(GR_E_INVALID, "gr_decode_graph_create: out is NULL");
+    *out = nullptr;
+    if (!trie || !steps || n_steps < 1) return fail(GR_E_INVALID, "gr_decode_graph_create: no steps");
+    if (!stream) return fail(GR_E_INVALID, "gr_decode_graph_create: capture needs a created stream");
+    for (int32_t t = 0; t < n_steps; ++t) {
+        gr_status st = check_step(trie, &steps[t]);
+        if (st) return st;
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(hs, &cs);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_graph_create: stream query");
+    if (cs != hipStreamCaptureStatusNone) return fail(GR_E_INVALID, "gr_decode_graph_create: stream is already capturing");
+    e = hipStreamBeginCapture(hs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_graph_create: begin capture");
+    gr_status st = GR_OK;
+    for (int32_t t = 0; t < n_steps && st == GR_OK; ++t) st = launch_step(trie, &steps[t], stream);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(hs, &g);
+    if (st != GR_OK || e != hipSuccess) {
+        if (g) hipGraphDestroy(g);
+        return st != GR_OK ? st : hip_fail(e, "gr_decode_graph_create: end capture");
+    }
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        hipGraphDestroy(g);
+        return hip_fail(e, "gr_decode_graph_create: instantiate");
+    }
+    gr_graph *gg = new (std::nothrow) gr_graph;
+    if (!gg) {
+        hipGraphExecDestroy(x);
+        hipGraphDestroy(g);
+        return fail(GR_E_NOMEM, "gr_decode_graph_create: out of host memory");
+    }
+    gg->graph = g;
+    gg->exec = x;
+    hipGetDevice(&gg->device);
+    *out = gg;
+    return GR_OK;
+}
+
+gr_status gr_decode_graph_launch(const gr_graph *graph, void *stream) {
+    if (!graph || !graph->exec) return fail(GR_E_INVALID, "gr_decode_graph_launch: null graph");
+    hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_graph_launch");
+    return GR_OK;
+}
+
+void gr_decode_graph_destroy(gr_graph *graph) {
+    if (!graph) return;
+    if (graph->exec) hipGraphExecDestroy(graph->exec);
+    if (graph->graph) hipGraphDestroy(graph->graph);
+    delete graph;
 }
 
 }  // extern "C"

@@ -50,7 +50,8 @@ constexpr int MAX_ROWS_WG = 32;      // beam rows per expand workgroup (upper bo
 // Launch shape of the expand kernel: workgroup x of request b takes rows
 // m = x + i * gx (i < rows_wg) and owns a survivor segment of seg_cap
 // entries (a row has at most V children), so no segment can overflow.  A
-// segment's count is made even with a zero key (never a real key).
+// segment's count is padded to a multiple of 8 with zero keys (never a real
+// key) whose bin is 0xFFFF (never a real bin).
 struct TailShape {
     int rows_wg, gx;
     int64_t seg_cap;
@@ -67,13 +68,13 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
     TailShape t;
     t.rows_wg = (int)rw;
     t.gx = (int)((M_in + rw - 1) / rw);
-    t.seg_cap = (rw * V + 1) & ~(int64_t)1;   // even: segments are read in key pairs
+    t.seg_cap = (rw * V + 7) & ~(int64_t)7;   // segments are read 8 bins / 2 keys at a time
     return t;
 }
 
 // Workspace carving of gr_constrain_topk (byte offsets).
 struct TailWsLayout {
-    size_t segcnt, hist, skey, schild, total;
+    size_t segcnt, hist, skey, schild, sbin, total;
     TailShape shape;
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);

@@ -13,8 +13,9 @@
 // lanes in 8-byte chunks (4 bf16 or 2 fp32 per lane per chunk), so every load
 // and store of q, k, v, out and of a gathered pool block is one fully
 // coalesced wavefront access; the d_h/VEC lanes of a head reduce their dot
-// products with xor shuffles.  Positions are consumed with an online softmax,
-// so at most L <= 16 blocks are gathered once each.
+// products with xor shuffles.  The prefix block ids are read in one load,
+// the blocks' K/V are gathered in batches with all loads of a batch in
+// flight, and positions are consumed with an online softmax.
 #include "gr_device.h"
 #include "gr_internal.h"
 
@@ -62,6 +63,7 @@ template <bool BF16, int NCH>
 __global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
     using C = Chunk<BF16>;
     constexpr int VEC = C::VEC;
+    constexpr int JB = NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1);   // prefix blocks per load batch
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = blockIdx.x * 4 + wave;
     if (i >= p.R) return;
@@ -96,47 +98,62 @@ __global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
 #pragma unroll
         for (int x = 0; x < VEC; ++x) o[c][x] = 0.0f;
     }
+    // The row's prefix block ids, lane j holding position j (L <= 64).
+    const int32_t tb = lane < p.t ? p.table[(size_t)i * p.L + lane] : -1;
     if (lane == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
 
-    for (int j = 0; j <= p.t; ++j) {
-        float kj[NCH][VEC], vj[NCH][VEC];
-        if (j < p.t) {
-            const int32_t blk = p.table[(size_t)i * p.L + j];
-            if (blk < 0 || blk >= p.pool_blocks) continue;  // a dead row's missing past
+    // Prefix positions in batches of JB: every block load of a batch is
+    // issued before the first dot product, then the current token.
+    for (int j0 = 0; j0 <= p.t; j0 += JB) {
+        uint2 kr[JB][NCH], vr[JB][NCH];
+        bool use[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            const int32_t blk = __builtin_amdgcn_readlane(tb, j < 64 ? j : 0);
+            // a dead row's missing past is skipped; position t is the current token
+            use[jj] = j < p.t && blk >= 0 && blk < p.pool_blocks;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int e = c * 64 + lane;
-                uint2 uk = make_uint2(0, 0), uv = uk;
-                if (act[c]) {
-                    uk = kp[(size_t)blk * E2 + e];
-                    uv = vp[(size_t)blk * E2 + e];
+                kr[jj][c] = vr[jj][c] = make_uint2(0, 0);
+                if (use[jj] && act[c]) {
+                    kr[jj][c] = kp[(size_t)blk * E2 + e];
+                    vr[jj][c] = vp[(size_t)blk * E2 + e];
                 }
-                C::unpack(uk, kj[c]);
-                C::unpack(uv, vj[c]);
             }
-        } else {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-#pragma unroll
-                for (int x = 0; x < VEC; ++x) {
-                    kj[c][x] = kc[c][x];
-                    vj[c][x] = vc[c][x];
-                }
         }
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            float dot = 0.0f;
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            if (j > p.t) break;                  // uniform
+            if (j < p.t && !use[jj]) continue;   // uniform
 #pragma unroll
-            for (int x = 0; x < VEC; ++x) dot += qf[c][x] * kj[c][x];
-            for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
-            const float s = dot * p.scale;
-            const float mn = fmaxf(mrun[c], s);
-            const float alpha = __expf(mrun[c] - mn);
-            const float pe = __expf(s - mn);
-            lrun[c] = lrun[c] * alpha + pe;
+            for (int c = 0; c < NCH; ++c) {
+                float kj[VEC], vj[VEC];
+                if (j < p.t) {
+                    C::unpack(kr[jj][c], kj);
+                    C::unpack(vr[jj][c], vj);
+                } else {
 #pragma unroll
-            for (int x = 0; x < VEC; ++x) o[c][x] = o[c][x] * alpha + pe * vj[c][x];
-            mrun[c] = mn;
+                    for (int x = 0; x < VEC; ++x) {
+                        kj[x] = kc[c][x];
+                        vj[x] = vc[c][x];
+                    }
+                }
+                float dot = 0.0f;
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) dot += qf[c][x] * kj[x];
+                for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
+                const float sc = dot * p.scale;
+                const float mn = fmaxf(mrun[c], sc);
+                const float alpha = __expf(mrun[c] - mn);
+                const float pe = __expf(sc - mn);
+                lrun[c] = lrun[c] * alpha + pe;
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) o[c][x] = o[c][x] * alpha + pe * vj[x];
+                mrun[c] = mn;
+            }
         }
     }
     uint2 *out = (uint2 *)p.out + (size_t)i * E2;

@@ -11,7 +11,8 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import StepArgs, Trie, _ptr, constrain_topk_workspace, decode_step, tail_args
+from . import (DecodeGraph, StepArgs, Trie, _ptr, constrain_topk_workspace, decode_step,
+               tail_args)
 from ._lib import GR_BF16, GR_F32
 
 
@@ -89,3 +90,12 @@ class Decoder:
             stream=None) -> None:
         for t in range(self.L):
             self.step(t, user_bm, user_probes, n_loc, k_ctx, v_ctx, inputs[t], stream)
+
+    def graph(self, user_bm, user_probes, n_loc: int, k_ctx, v_ctx, inputs: List[Dict],
+              stream) -> DecodeGraph:
+        """The L steps of run() captured as one HIP graph on `stream` (a
+        created stream); each launch() replays the whole decode on the same
+        buffers."""
+        steps = [self.step_args(t, user_bm, user_probes, n_loc, k_ctx, v_ctx, inputs[t])
+                 for t in range(self.L)]
+        return DecodeGraph(self.trie, steps, stream)
