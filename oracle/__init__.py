@@ -19,6 +19,9 @@ Parity status per function (pins live in tests/test_oracle_*.py):
                     T_ctx = 1, q = 0, identical keys
   self_attn         pinned: T_self = 1, coalesced block-diagonal tile of
                     Section 5.2, torch SDPA fp64 per row
+  joint_attn        pinned: no beam positions = cross_attn; the log-sum-exp
+                    merge of the pinned cross_attn and self_attn results;
+                    identical keys (mean of every value); q = 0
 """
 from __future__ import annotations
 
@@ -79,6 +82,7 @@ def lib():
         L.orc_topk.argtypes = [P, i64, i64, P, P]
         L.orc_cross_attn.argtypes = [P, P, P, i32, i32, i32, i32, i32, P]
         L.orc_self_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, P]
+        L.orc_joint_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
         _lib = L
     return _lib
 
@@ -252,4 +256,22 @@ def self_attn(q, hk, hv, valid) -> np.ndarray:
     assert hk.shape == (R, T, H, d) and va.shape == (R, T) and T <= 64
     out = np.empty_like(q)
     lib().orc_self_attn(_p(q), _p(hk), _p(hv), _p(va), R, T, H, d, _p(out))
+    return out
+
+
+def joint_attn(q, K, Vv, hk, hv, valid, B: int, M: int) -> np.ndarray:
+    """One softmax over request b's context keys followed by row r's own beam
+    prefix positions (hk/hv [R, Tb, H, d], valid [R, Tb])."""
+    q = _c(q, np.float64)
+    K = _c(K, np.float64)
+    Vv = _c(Vv, np.float64)
+    hk = _c(hk, np.float64)
+    hv = _c(hv, np.float64)
+    va = _c(valid, np.uint8)
+    R, H, d = q.shape
+    T, Tb = K.shape[2], hk.shape[1]
+    assert R == B * M and K.shape == (B, H, T, d) and Vv.shape == K.shape
+    assert hk.shape == (R, Tb, H, d) and hv.shape == hk.shape and va.shape == (R, Tb)
+    out = np.empty_like(q)
+    lib().orc_joint_attn(_p(q), _p(K), _p(Vv), _p(hk), _p(hv), _p(va), B, M, H, T, Tb, d, _p(out))
     return out

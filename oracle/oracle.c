@@ -376,3 +376,57 @@ void orc_self_attn(const double *q, const double *hk, const double *hv,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* F2: joint attention over the request's context and the row's own beam    */
+/* prefix, one softmax over the concatenated key sequence (the shared-      */
+/* prefix beam attention of the Meituan engine article; GR-Inference's      */
+/* GR-Decode-Attention, whose K1 / K2 partial results its K3 merges with a  */
+/* log-sum-exp, computes the same thing).  Row r = b*M + m.                 */
+/* q [R,H,d]; K/V [B,H,T,d]; hk/hv [R,Tb,H,d]; valid [R,Tb] (0 = excluded). */
+/* out [R,H,d]; scale 1/sqrt(d).                                            */
+/* ------------------------------------------------------------------------ */
+void orc_joint_attn(const double *q, const double *K, const double *Vv,
+                    const double *hk, const double *hv, const uint8_t *valid,
+                    int B, int M, int H, int T, int Tb, int d, double *out)
+{
+    double scale = 1.0 / sqrt((double)d);
+    int64_t R = (int64_t)B * M;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++) {
+        int64_t b = r / M;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(T + Tb));
+        for (int h = 0; h < H; h++) {
+            const double *qr = q + (r * H + h) * d;
+            const double *Kb = K + ((b * H + h) * (int64_t)T) * d;
+            const double *Vb = Vv + ((b * H + h) * (int64_t)T) * d;
+            /* scores: context positions 0..T-1, then beam positions T..T+Tb-1 */
+            double mx = -INFINITY;
+            for (int j = 0; j < T + Tb; j++) {
+                if (j >= T && !valid[r * Tb + (j - T)]) continue;
+                const double *kr = j < T ? Kb + (int64_t)j * d : hk + ((r * Tb + (j - T)) * H + h) * d;
+                double acc = 0.0;
+                for (int i = 0; i < d; i++) acc += qr[i] * kr[i];
+                s[j] = acc * scale;
+                if (s[j] > mx) mx = s[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < T + Tb; j++) {
+                if (j >= T && !valid[r * Tb + (j - T)]) continue;
+                s[j] = exp(s[j] - mx);
+                z += s[j];
+            }
+            double *o = out + (r * H + h) * d;
+            for (int i = 0; i < d; i++) {
+                double acc = 0.0;
+                for (int j = 0; j < T + Tb; j++) {
+                    if (j >= T && !valid[r * Tb + (j - T)]) continue;
+                    const double *vr = j < T ? Vb + (int64_t)j * d : hv + ((r * Tb + (j - T)) * H + h) * d;
+                    acc += s[j] * vr[i];
+                }
+                o[i] = acc / z;
+            }
+        }
+        free(s);
+    }
+}

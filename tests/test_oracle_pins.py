@@ -337,6 +337,55 @@ def test_self_attn_single_position_and_block_diagonal_tile():
         assert np.abs(out[g] - ref).max() < 1e-12
 
 
+
+def test_joint_attn_pins():
+    """One softmax over [context keys ; the row's beam prefix] (shared-prefix
+    beam attention; GR-Decode-Attention K1 + K2 merged by K3)."""
+    r = np.random.default_rng(21)
+    B, M, H, T, Tb, d = 2, 3, 2, 6, 4, 8
+    R = B * M
+    q = r.standard_normal((R, H, d))
+    K = r.standard_normal((B, H, T, d))
+    Vv = r.standard_normal((B, H, T, d))
+    hk = r.standard_normal((R, Tb, H, d))
+    hv = r.standard_normal((R, Tb, H, d))
+    # no beam position: the context attention alone
+    none = np.zeros((R, Tb), np.uint8)
+    assert np.abs(oracle.joint_attn(q, K, Vv, hk, hv, none, B, M)
+                  - oracle.cross_attn(q, K, Vv, B, M)).max() < 1e-12
+    # log-sum-exp merge of the two separately pinned attentions: the joint
+    # output is the convex combination of the context-only and beam-only
+    # outputs weighted by their partition functions
+    valid = (r.random((R, Tb)) < 0.7).astype(np.uint8)
+    valid[:, 0] = 1
+    joint = oracle.joint_attn(q, K, Vv, hk, hv, valid, B, M)
+    o1 = oracle.cross_attn(q, K, Vv, B, M)
+    o2 = oracle.self_attn(q, hk, hv, valid)
+    for row in range(R):
+        b = row // M
+        for h in range(H):
+            s1 = K[b, h] @ q[row, h] / math.sqrt(d)
+            s2 = hk[row, valid[row].astype(bool), h] @ q[row, h] / math.sqrt(d)
+            mx = max(s1.max(), s2.max())
+            z1, z2 = np.exp(s1 - mx).sum(), np.exp(s2 - mx).sum()
+            ref = (z1 * o1[row, h] + z2 * o2[row, h]) / (z1 + z2)
+            assert np.abs(joint[row, h] - ref).max() < 1e-12
+    # identical keys everywhere: the mean of every value taken part
+    k0 = r.standard_normal(d)
+    Ks = np.broadcast_to(k0, K.shape).copy()
+    hks = np.broadcast_to(k0, hk.shape).copy()
+    out = oracle.joint_attn(q, Ks, Vv, hks, hv, valid, B, M)
+    for row in range(R):
+        b = row // M
+        allv = np.concatenate([Vv[b].transpose(1, 0, 2), hv[row][valid[row].astype(bool)]], axis=0)
+        assert np.abs(out[row] - allv.mean(axis=0)).max() < 1e-13
+    # q = 0: uniform weights as well
+    out = oracle.joint_attn(np.zeros_like(q), K, Vv, hk, hv, valid, B, M)
+    for row in range(R):
+        b = row // M
+        allv = np.concatenate([Vv[b].transpose(1, 0, 2), hv[row][valid[row].astype(bool)]], axis=0)
+        assert np.abs(out[row] - allv.mean(axis=0)).max() < 1e-13
+
 # --------------------------------------------------------------------------
 # The decode walk end to end (tiny workload)
 # --------------------------------------------------------------------------
