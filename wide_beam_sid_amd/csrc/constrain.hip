@@ -43,6 +43,7 @@ constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw
 constexpr int SEL_THREADS = 1024;
 constexpr int BND_CAP = 2048;         // threshold-bin entries buffered in LDS
 constexpr uint32_t BIN_SCAN_MIN = 16 * SEL_THREADS;   // survivors from which select reads bins first
+constexpr uint32_t CAND_CAP = 4096;   // candidates (bins up to the threshold) listed in LDS
 
 struct TailParams {
     const int32_t *off;
@@ -864,6 +865,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     __shared__ uint32_t s_segpre[MAX_GX + 1];  // prefix sums of the segments' survivors
     __shared__ uint32_t s_wsum2[SEL_THREADS / 64];
     __shared__ int s_thr, s_below, s_nbnd, s_ncol, s_digit, s_rem;
+    __shared__ uint32_t s_cand[CAND_CAP];     // survivors in bins up to the threshold bin
+    __shared__ uint32_t s_ncand, s_ncl;
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_ub[SEL_THREADS / 64];
@@ -925,6 +928,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         s_thr = NBINS;
         s_nbnd = 0;
         s_ncol = 0;
+        s_ncand = 0xFFFFFFFFu;   // every survivor (no threshold bin)
     }
     __syncthreads();
     uint32_t pre = 0, total = 0;
@@ -940,10 +944,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         if (total > (uint32_t)k && cum < (uint32_t)k && (uint32_t)k <= cum + c[i]) {
             s_thr = tid * PER + i;
             s_below = (int)cum;
+            s_ncand = cum + c[i];   // survivors in bins up to and including this one
         }
         cum += c[i];
     }
     if (tid == 0 && total <= (uint32_t)k) s_below = (int)total;
+    if (tid == 0) s_ncl = 0u;
     __syncthreads();
     const int thr = s_thr, below = s_below;
     const uint32_t n_surv = s_segpre[gx];
@@ -978,10 +984,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             }
         }
     };
-    if (n_surv >= BIN_SCAN_MIN) {
+    if (n_surv >= BIN_SCAN_MIN && s_ncand <= CAND_CAP) {
         // Many survivors: their bins are read 8 at a time (16 bytes, 4 groups
-        // in flight per thread) and only the keys of bins at or below the
-        // threshold bin are fetched; pads carry bin 0xFFFF.
+        // in flight per thread); the positions of bins at or below the
+        // threshold bin go to an LDS list, whose keys are then fetched all at
+        // once.  Pads carry bin 0xFFFF.
         const uint16_t *bins = p.sbin + (size_t)b * gx * seg_cap;
         const uint32_t n_oct = n_surv >> 3;
         for (uint32_t o0 = 0; o0 < n_oct; o0 += 4 * SEL_THREADS) {
@@ -996,14 +1003,36 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (src[u] == 0xFFFFFFFFu) continue;
                 const uint32_t wv[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int bn = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                    if (bn <= thr) take(keys[src[u] + e], src[u] + e);
+                    const bool in = src[u] != 0xFFFFFFFFu && bn <= thr;
+                    const uint64_t bal = __ballot(in);
+                    if (bal) {
+                        uint32_t base = 0;
+                        if (lane == 0) base = atomicAdd(&s_ncl, (uint32_t)__popcll(bal));
+                        base = __shfl(base, 0, 64);
+                        const uint32_t ci = base + lanes_below(bal);
+                        if (in && ci < CAND_CAP) s_cand[ci] = src[u] + e;
+                    }
                 }
             }
+        }
+        __syncthreads();
+        const uint32_t nc = min(s_ncl, (uint32_t)CAND_CAP);
+        for (uint32_t c0 = 0; c0 < nc; c0 += 4 * SEL_THREADS) {
+            uint32_t src[4];
+            uint64_t kk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t ci = c0 + u * SEL_THREADS + tid;
+                src[u] = ci < nc ? s_cand[ci] : 0xFFFFFFFFu;
+                kk[u] = ci < nc ? keys[src[u]] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (src[u] != 0xFFFFFFFFu) take(kk[u], src[u]);
         }
     } else {
         // Pairs are read coalesced (consecutive threads take consecutive
