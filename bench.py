@@ -88,7 +88,7 @@ def measured_traffic(kernel: str, steps, workload: str):
 # ---------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, w, seed: int, n_sets: int, stream):
+    def __init__(self, w, seed: int, n_sets: int, stream, slice_min: int = 0):
         import torch
 
         import wide_beam_sid_amd as gr
@@ -106,7 +106,7 @@ class Bench:
             f"({time.time() - t0:.1f} s)")
         t0 = time.time()
         self.trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads],
-                                  keep_host=True)
+                                  keep_host=True, bloom_slice_min=slice_min)
         self.view = self.trie.host_view()
         log(f"[bench] trie {self.trie.info()} ({time.time() - t0:.1f} s)")
         self.sids, self.ads = sids, ads
@@ -161,7 +161,7 @@ class Bench:
         for t in range(w.L):
             a = self.args[s][t]
             R = w.rows(t)
-            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(6)]
             e[0].record(self.stream)
             st = self.L.gr_cross_attn(a.qx, a.k_ctx, a.v_ctx, a.cross_out, w.B, d.M[t], w.H,
                                       w.T_ctx, w.d_h, gdt, self.sp)
@@ -174,6 +174,13 @@ class Bench:
             e[3].record(self.stream)
             st |= self.L.gr_topk_reorder(self.h, ctypes.byref(a.tail), self.sp)
             e[4].record(self.stream)
+            # the joint (context + beam prefix) attention on the same step's
+            # inputs; it rewrites the same pool blocks and table column
+            st |= self.L.gr_joint_attn(a.q, a.k_ctx, a.v_ctx, a.k_new, a.v_new, a.k_pool,
+                                       a.v_pool, a.pool_blocks, a.tail.table_in, a.fresh_base,
+                                       w.B, d.M[t], w.H, w.T_ctx, w.d_h, t, w.L, gdt,
+                                       a.cross_out, self.sp)
+            e[5].record(self.stream)
             if st != 0:
                 raise RuntimeError(self.L.gr_last_error().decode())
             out.append(e)
@@ -319,6 +326,9 @@ def main():
                     help="decodes issued per entry point for the event breakdown")
     ap.add_argument("--cpu-requests", type=int, default=-1,
                     help="requests in the oracle's sample (-1: the whole batch, 0: skip)")
+    ap.add_argument("--slice-min", type=int, default=0,
+                    help="trie builder: fewest children of a node with a bit-sliced matcher "
+                         "block (0: the library default, -1: none)")
     ap.add_argument("--n-sids", type=int, default=0,
                     help="catalog size override (0: the workload's own); per-step shapes stay")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -341,7 +351,7 @@ def main():
     if args.n_sids:
         w = dataclasses.replace(w, n_sids=args.n_sids)
     stream = torch.cuda.Stream()
-    b = Bench(w, args.seed, args.sets, stream)
+    b = Bench(w, args.seed, args.sets, stream, args.slice_min)
     rows_per_decode = w.total_rows
     log(f"[bench] rows per decode {rows_per_decode}, {args.sets} input sets "
         f"({b.set_bytes / 2**20:.0f} MiB)")
@@ -423,7 +433,8 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
 
-    names = ["gr_cross_attn", "gr_self_attn_paged", "gr_constrain", "gr_topk_reorder"]
+    names = ["gr_cross_attn", "gr_self_attn_paged", "gr_constrain", "gr_topk_reorder",
+             "gr_joint_attn"]
     per = {n: [[] for _ in range(w.L)] for n in names}
     for dec in split:
         for t, e in enumerate(dec):
@@ -441,6 +452,7 @@ def main():
             rows_per_s=u["R"] / (float(np.mean(x)) * 1e-6),
             cross_us=mean_us["gr_cross_attn"][t], self_us=mean_us["gr_self_attn_paged"][t],
             constrain_us=mean_us["gr_constrain"][t], topk_us=mean_us["gr_topk_reorder"][t],
+            joint_us=mean_us["gr_joint_attn"][t],
             cross_tflops=u["cross_flops"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e12,
             cross_gbs=u["cross_bytes"] / (mean_us["gr_cross_attn"][t] * 1e-6) / 1e9,
             self_gbs=u["self_bytes"] / (mean_us["gr_self_attn_paged"][t] * 1e-6) / 1e9,
@@ -448,7 +460,9 @@ def main():
             topk_gbs=u["topk_bytes"] / (mean_us["gr_topk_reorder"][t] * 1e-6) / 1e9))
 
     # Dominant entry point: largest total time over the decode.
-    tot = {n: sum(mean_us[n]) for n in names}
+    # the decode's own entry points (the joint attention is an alternative to
+    # the first two, timed beside them)
+    tot = {n: sum(mean_us[n]) for n in names if n != "gr_joint_attn"}
     dom = max(tot, key=tot.get)
     wide = [t for t in range(w.L) if w.rows(t) == max(w.rows(s) for s in range(w.L))]
     if dom == "gr_cross_attn":
@@ -494,6 +508,7 @@ def main():
                    "V": w.V, "T_ctx": w.T_ctx, "heads": w.H, "head_dim": w.d_h,
                    "n_sids": w.n_sids, "bloom_bits": w.bloom_bits, "bloom_k": w.bloom_k,
                    "n_loc": w.n_loc, "rows_per_decode": rows_per_decode,
+                   "slice_words": int(b.trie.info()["slice_words"]),
                    "input_sets": args.sets, "input_set_mib": round(b.set_bytes / 2**20)},
         "step_latency_us": {"p50": float(np.percentile(wide_steps, 50)),
                             "p99": float(np.percentile(wide_steps, 99)),

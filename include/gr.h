@@ -78,7 +78,7 @@ typedef struct {
     int32_t bloom_slice_min; /* nodes with at least this many children also get */
                          /* a bit-sliced (column-major) copy of their children's */
                          /* Bloom and bitmask rows, which answers eqs 5 and 8   */
-                         /* for all children at once (0: 16, -1: none); see      */
+                         /* for all children at once (0: 48, -1: none); see      */
                          /* gr_trie_view.slice_words                             */
 } gr_trie_params;
 
@@ -147,7 +147,7 @@ typedef struct {
  * Validates: offsets non-decreasing from 0 to num_entries, child ids in
  * [1, num_nodes), tokens in [0, V), matcher ids in range, tokens of one node
  * strictly increasing.  GR_E_INVALID names the first violation.
- * Nodes with at least 16 children also get the bit-sliced copy described at
+ * Nodes with at least 48 children also get the bit-sliced copy described at
  * gr_trie_params.bloom_slice_min.
  */
 gr_status gr_trie_create(const gr_trie_view *arrays, gr_trie **out);
@@ -210,6 +210,35 @@ gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new
                              int32_t *table, int64_t fresh_base, int32_t R, int32_t t,
                              int32_t L, int32_t H, int32_t d_h, gr_dtype dtype,
                              void *out, void *stream);
+
+/* ===================================================================== */
+/* Joint attention: one softmax over the request's context and the row's */
+/* own beam prefix (the shared-prefix beam attention of the Meituan       */
+/* engine article; GR-Inference's GR-Decode-Attention, whose context and   */
+/* beam parts are merged with a log-sum-exp, computes the same output).    */
+/* ===================================================================== */
+/*
+ * For row r = b*M + m (R = B*M rows) and head h:
+ *   out[r,h] = softmax_j(q[r,h] . key_j / sqrt(d_h)) . value_j over the keys
+ *              k_ctx[b,h,0..T_ctx-1], then the row's prefix blocks
+ *              k_pool[table[r,j],h] for j < t (a block id outside
+ *              [0, pool_blocks) is skipped), then the current token k_new[r,h]
+ *              (position t), with the matching values.
+ * Like gr_self_attn_paged it writes k_new[r], v_new[r] to block
+ * fresh_base + r of the pools and sets table[r, t] = fresh_base + r; the
+ * prefix blocks it reads must lie outside [fresh_base, fresh_base + R).
+ * Layouts: q, k_new, v_new, out [R, H, d_h]; k_ctx, v_ctx [B, H, T_ctx, d_h];
+ * pools [pool_blocks, H, d_h]; table [R, L] int32 (L <= 16, 0 <= t < L).
+ * bf16 (d_h in {32, 64, 128}, fp32 accumulation, context on MFMA) or fp32
+ * (d_h <= 64).  All pointers are caller-owned device memory; no allocation,
+ * no host synchronisation; argument errors return before any launch.
+ */
+gr_status gr_joint_attn(const void *q, const void *k_ctx, const void *v_ctx, const void *k_new,
+                        const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                        int32_t *block_table, int64_t fresh_base, int32_t B, int32_t M,
+                        int32_t H, int32_t T_ctx, int32_t d_h, int32_t t, int32_t L,
+                        gr_dtype dtype, void *out, void *stream);
+
 
 /* ===================================================================== */
 /* A3-A6: CD + GTM mask, log-softmax, scores, top-k, reorder.            */

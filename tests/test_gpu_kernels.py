@@ -76,6 +76,70 @@ def test_cross_attn_parity(B, M, H, T, d, dt):
 
 
 # ---------------------------------------------------------------------------
+# Joint attention: context + the row's beam prefix in one softmax
+# ---------------------------------------------------------------------------
+
+JOINT_CASES = [
+    # B, M, H, T, d, L, t, dtype
+    (1, 8, 2, 16, 32, 3, 0, "f32"),
+    (2, 5, 2, 7, 64, 4, 3, "f32"),
+    (2, 37, 2, 70, 64, 4, 2, "bf16"),     # ragged beams and keys
+    (3, 129, 4, 64, 32, 4, 3, "bf16"),    # two row tiles + 1
+    (1, 300, 2, 2048, 128, 3, 2, "bf16"), # long context
+    (4, 256, 4, 64, 64, 4, 1, "bf16"),
+    (2, 200, 2, 333, 64, 4, 3, "bf16"),   # 128-row workgroups, ragged last tile
+    (1, 20, 16, 1, 128, 3, 0, "bf16"),    # T_ctx = 1, no prefix
+]
+
+
+@pytest.mark.parametrize("B,M,H,T,d,L,t,dt", JOINT_CASES)
+def test_joint_attn_parity(B, M, H, T, d, L, t, dt):
+    gr = _gr()
+    rng = np.random.default_rng(B * 7 + M + T + t)
+    R = B * M
+    q = _rand((R, H, d), dt, rng)
+    K = _rand((B, H, T, d), dt, rng)
+    Vv = _rand((B, H, T, d), dt, rng)
+    kn = _rand((R, H, d), dt, rng)
+    vn = _rand((R, H, d), dt, rng)
+    old = 2 * R + 3
+    pool_blocks = old + R
+    kp = _rand((pool_blocks, H, d), dt, rng)
+    vp = _rand((pool_blocks, H, d), dt, rng)
+    table = rng.integers(0, old, size=(R, L)).astype(np.int32)
+    table[rng.random((R, L)) < 0.15] = -1          # missing past (dead rows)
+    table[:, t:] = -1
+    dkp, dvp, dtab = to_dev(kp, dt), to_dev(vp, dt), to_dev(table)
+    out = torch.empty(to_dev(q, dt).shape, dtype=dkp.dtype, device="cuda")
+    gr.joint_attn(to_dev(q, dt), to_dev(K, dt), to_dev(Vv, dt), to_dev(kn, dt), to_dev(vn, dt),
+                  dkp, dvp, dtab, old, t, B, M, out)
+    torch.cuda.synchronize()
+    # oracle: the row's history gathered from the (input) pool, then the current token
+    hk = np.zeros((R, t + 1, H, d))
+    hv = np.zeros((R, t + 1, H, d))
+    valid = np.zeros((R, t + 1), np.uint8)
+    kpf, vpf = _as_f(kp, dt), _as_f(vp, dt)
+    for j in range(t):
+        ok = table[:, j] >= 0
+        hk[ok, j] = kpf[table[ok, j]]
+        hv[ok, j] = vpf[table[ok, j]]
+        valid[ok, j] = 1
+    hk[:, t], hv[:, t], valid[:, t] = _as_f(kn, dt), _as_f(vn, dt), 1
+    ref = oracle.joint_attn(_as_f(q, dt), _as_f(K, dt), _as_f(Vv, dt), hk, hv, valid, B, M)
+    attn_close(to_np64(out), ref, dt, f"joint {B}x{M}x{H}x{T}x{d} t={t}")
+    # the current token went to its fresh block, the table names it
+    got_tab = dtab.cpu().numpy()
+    assert np.array_equal(got_tab[:, t], old + np.arange(R))
+    assert np.array_equal(got_tab[:, :t], table[:, :t])
+    kview = dkp[old:].view(torch.int16 if dt == "bf16" else torch.int32).cpu().numpy()
+    kin = kn.view(np.int16) if dt == "bf16" else kn.view(np.int32)
+    assert np.array_equal(kview, kin)
+    vview = dvp[old:].view(torch.int16 if dt == "bf16" else torch.int32).cpu().numpy()
+    vin = vn.view(np.int16) if dt == "bf16" else vn.view(np.int32)
+    assert np.array_equal(vview, vin)
+
+
+# ---------------------------------------------------------------------------
 # A2: paged self-attention
 # ---------------------------------------------------------------------------
 

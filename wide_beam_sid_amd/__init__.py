@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import GR_BF16, GR_F32, GrError, StepArgs, TailArgs, TrieParams, TrieView, check
 
 __all__ = [
-    "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged",
+    "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged", "joint_attn",
     "constrain_topk_workspace", "constrain_topk", "constrain", "topk_reorder", "decode_step",
     "DecodeGraph", "version",
 ]
@@ -185,6 +185,20 @@ def self_attn_paged(q, k_new, v_new, k_pool, v_pool, table, fresh_base: int, t: 
     check(_lib.lib().gr_self_attn_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                         _ptr(v_pool), k_pool.shape[0], _ptr(table), fresh_base,
                                         R, t, L, H, d, _dtype(q), _ptr(out), _stream(stream)))
+
+
+def joint_attn(q, k_ctx, v_ctx, k_new, v_new, k_pool, v_pool, table, fresh_base: int, t: int,
+               B: int, M: int, out, stream=None) -> None:
+    """Joint context + beam-prefix attention on torch tensors (see
+    gr_joint_attn): q/k_new/v_new/out [B*M, H, d_h], k_ctx/v_ctx
+    [B, H, T_ctx, d_h], pools [N, H, d_h], table int32 [B*M, L]."""
+    R, H, d = q.shape
+    T = k_ctx.shape[2]
+    L = table.shape[1]
+    check(_lib.lib().gr_joint_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(table),
+                                   fresh_base, B, M, H, T, d, t, L, _dtype(q), _ptr(out),
+                                   _stream(stream)))
 
 
 def constrain_topk_workspace(B: int, M_in: int, V: int, k_out: int) -> int:

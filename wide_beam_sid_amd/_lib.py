@@ -21,7 +21,7 @@ EXPORTS = [
     "gr_last_error", "gr_version", "gr_bloom_probes",
     "gr_trie_builder_create", "gr_trie_builder_add_ads", "gr_trie_builder_finish",
     "gr_trie_builder_destroy", "gr_trie_create", "gr_trie_host_view", "gr_trie_info",
-    "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged",
+    "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged", "gr_joint_attn",
     "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
     "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
     "gr_decode_graph_destroy",
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.gr_cross_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P]
     L.gr_self_attn_paged.argtypes = [P, P, P, P, P, i64, P, i64, i32, i32, i32, i32, i32,
                                      ctypes.c_int, P, P]
+    L.gr_joint_attn.argtypes = [P, P, P, P, P, P, P, i64, P, i64, i32, i32, i32, i32, i32, i32,
+                                i32, ctypes.c_int, P, P]
     L.gr_constrain_topk_workspace.argtypes = [i32, i32, i32, i32]
     L.gr_constrain_topk_workspace.restype = sz
     L.gr_constrain_topk.argtypes = [P, ctypes.POINTER(TailArgs), P]

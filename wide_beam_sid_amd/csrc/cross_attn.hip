@@ -38,17 +38,34 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
+// The beam-prefix part of the joint attention: the current token's k, v
+// (written to block fresh_base + r) and the row's earlier blocks P[r, j < t].
+struct JointArgs {
+    const uint16_t *k_new, *v_new;
+    uint16_t *k_pool, *v_pool;
+    int32_t *table;
+    int64_t pool_blocks, fresh_base;
+    int t, L;
+};
+
 // One workgroup = (request b, head h, 64 * RB beam rows); wavefront w takes
 // RB blocks of 16 rows.  The K / V tiles of 64 keys are double-buffered in
 // LDS: the global loads of tile i + 1 are in flight (in registers) while
 // tile i is computed, then written to the other buffer, one barrier per
 // tile.  K is stored row-major; V transposed, two keys per 32-bit store.
-template <int D, int RB>
+//
+// JOINT: after the context tiles, the same online softmax continues over the
+// row's own beam positions j = 0..t (shared-prefix beam attention): lane
+// (g, a) dots its quarter of row a's query with the position's key, the four
+// lanes of the row sum their parts, and the lane's output columns take the
+// weighted value; position t is the current token, which also goes to the
+// pool.  One output, no partial results leave the kernel.
+template <int D, int RB, bool JOINT>
 __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ K,
                                                        const uint16_t *__restrict__ Vv,
                                                        uint16_t *__restrict__ out, int M, int H,
-                                                       int T, float scale_log2) {
+                                                       int T, float scale_log2, JointArgs jn) {
     constexpr int NDC = D / 32;   // k steps of S = Q K^T
     constexpr int NDB = D / 16;   // 16-wide blocks of d in O^T
     constexpr int ROWS = 4 * RB * 16;
@@ -205,6 +222,71 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
         __syncthreads();
     }
 
+    if constexpr (JOINT) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int m = mbase + rb * 16 + a;
+            const bool rv = m < M;
+            const size_t r = (size_t)b * M + (rv ? m : 0);
+            const int64_t fblk = jn.fresh_base + (int64_t)r;
+            for (int j = 0; j <= jn.t; ++j) {
+                // position j < t: block P[r, j] (skipped when missing); j = t:
+                // the current token
+                int64_t blk = fblk;
+                bool use = rv;
+                if (j < jn.t) {
+                    blk = rv ? jn.table[r * jn.L + j] : -1;
+                    use = rv && blk >= 0 && blk < jn.pool_blocks;
+                }
+                const uint16_t *kr = j < jn.t ? jn.k_pool + ((size_t)(use ? blk : 0) * H + h) * D
+                                              : jn.k_new + (r * H + h) * D;
+                const uint16_t *vr = j < jn.t ? jn.v_pool + ((size_t)(use ? blk : 0) * H + h) * D
+                                              : jn.v_new + (r * H + h) * D;
+                uint4 kc[NDC], vc[NDB / 2];
+#pragma unroll
+                for (int c = 0; c < NDC; ++c)
+                    kc[c] = use ? *(const uint4 *)(kr + c * 32 + g * 8) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int c = 0; c < NDB / 2; ++c)
+                    vc[c] = use ? *(const uint4 *)(vr + g * 4 * NDB + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+                if (j == jn.t && rv) {   // the current token's k, v to its fresh block
+#pragma unroll
+                    for (int c = 0; c < NDC; ++c)
+                        *(uint4 *)(jn.k_pool + ((size_t)fblk * H + h) * D + c * 32 + g * 8) = kc[c];
+#pragma unroll
+                    for (int c = 0; c < NDB / 2; ++c)
+                        *(uint4 *)(jn.v_pool + ((size_t)fblk * H + h) * D + g * 4 * NDB + c * 8) = vc[c];
+                    if (h == 0 && g == 0) jn.table[r * jn.L + jn.t] = (int32_t)fblk;
+                }
+                float dot = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NDC; ++c) {
+                    V8 kk;
+                    kk.u = kc[c];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dot += (float)qf[rb][c][e] * (float)kk.b[e];
+                }
+                dot += __shfl_xor(dot, 16, 64);
+                dot += __shfl_xor(dot, 32, 64);
+                const float sj = use ? dot * scale_log2 : -INFINITY;
+                const float mn = fmaxf(mrow[rb], sj);
+                const float al = __builtin_amdgcn_exp2f(mrow[rb] - mn);
+                const float pj = __builtin_amdgcn_exp2f(sj - mn);
+                mrow[rb] = mn;
+                lpart[rb] = lpart[rb] * al + (g == 0 ? pj : 0.0f);   // counted once per row
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const uint32_t w0 = ((const uint32_t *)&vc[(db * 4) >> 3])[((db * 4) & 7) >> 1];
+                    const uint32_t w1 = ((const uint32_t *)&vc[(db * 4) >> 3])[(((db * 4) & 7) >> 1) + 1];
+                    const float vv[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                                         __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[rb][db][i] = o[rb][db][i] * al + pj * vv[i];
+                }
+            }
+        }
+    }
+
     // Lane (g, a) holds O[row a][d = g*4*NDB + db*4 + i].
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -254,6 +336,56 @@ __global__ __launch_bounds__(256) void k_cross_f32(const float *__restrict__ q,
     if (act) out[((size_t)r * H + h) * D + lane] = o / l;
 }
 
+// fp32 joint attention: one wavefront per (row, head), lane x holds
+// element x; the context keys, then the row's beam positions j = 0..t, in
+// one online softmax.
+__global__ __launch_bounds__(256) void k_joint_f32(const float *__restrict__ q,
+                                                   const float *__restrict__ K,
+                                                   const float *__restrict__ Vv,
+                                                   const float *__restrict__ k_new,
+                                                   const float *__restrict__ v_new, float *k_pool,
+                                                   float *v_pool, int32_t *table,
+                                                   int64_t pool_blocks, int64_t fresh_base,
+                                                   float *__restrict__ out, int M, int H, int T,
+                                                   int D, int rows, int t, int L, float scale) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int idx = blockIdx.x * 4 + wave;
+    if (idx >= rows * H) return;
+    const int r = idx / H, h = idx % H, b = r / M;
+    const bool act = lane < D;
+    const float qx = act ? q[((size_t)r * H + h) * D + lane] : 0.0f;
+    const float *Kb = K + ((size_t)b * H + h) * (size_t)T * D;
+    const float *Vb = Vv + ((size_t)b * H + h) * (size_t)T * D;
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    auto push = [&](float s, float v) {
+        const float mn = fmaxf(m, s);
+        const float alpha = expf(m - mn);
+        const float pe = expf(s - mn);
+        l = l * alpha + pe;
+        o = o * alpha + pe * v;
+        m = mn;
+    };
+    for (int tau = 0; tau < T; ++tau)
+        push(wave_sum(act ? qx * Kb[(size_t)tau * D + lane] : 0.0f) * scale,
+             act ? Vb[(size_t)tau * D + lane] : 0.0f);
+    const int64_t fblk = fresh_base + r;
+    for (int j = 0; j < t; ++j) {
+        const int64_t blk = table[(size_t)r * L + j];
+        if (blk < 0 || blk >= pool_blocks) continue;   // a dead row's missing past
+        const size_t o2 = ((size_t)blk * H + h) * D + lane;
+        push(wave_sum(act ? qx * k_pool[o2] : 0.0f) * scale, act ? v_pool[o2] : 0.0f);
+    }
+    const float kx = act ? k_new[((size_t)r * H + h) * D + lane] : 0.0f;
+    const float vx = act ? v_new[((size_t)r * H + h) * D + lane] : 0.0f;
+    if (act) {
+        k_pool[((size_t)fblk * H + h) * D + lane] = kx;
+        v_pool[((size_t)fblk * H + h) * D + lane] = vx;
+    }
+    if (h == 0 && lane == 0) table[(size_t)r * L + t] = (int32_t)fblk;
+    push(wave_sum(qx * kx) * scale, vx);
+    if (act) out[((size_t)r * H + h) * D + lane] = o / l;
+}
+
 }  // namespace
 
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out, int B, int M,
@@ -274,17 +406,57 @@ hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *
     // per SIMD)
     const bool big = T > 2 * TT && d <= 64;
     dim3 grid((M + (big ? 127 : 63)) / (big ? 128 : 64), H, B);
+    const JointArgs nj{};
 #define GR_CROSS(DD)                                                                          \
-    if (big) k_cross_bf16<DD, 2><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);          \
-    else k_cross_bf16<DD, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
+    if (big) k_cross_bf16<DD, 2, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj); \
+    else k_cross_bf16<DD, 1, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj);
     if (d == 32) {
         GR_CROSS(32)
     } else if (d == 64) {
         GR_CROSS(64)
     } else {
-        k_cross_bf16<128, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2);
+        k_cross_bf16<128, 1, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj);
     }
 #undef GR_CROSS
+    return hipGetLastError();
+}
+
+hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const void *k_new,
+                             const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                             int32_t *table, int64_t fresh_base, int B, int M, int H, int T, int d,
+                             int t, int L, gr_dtype dt, void *out, hipStream_t s) {
+    if (dt == GR_F32) {
+        const int waves = B * M * H;
+        k_joint_f32<<<(waves + 3) / 4, 256, 0, s>>>(
+            (const float *)q, (const float *)k, (const float *)v, (const float *)k_new,
+            (const float *)v_new, (float *)k_pool, (float *)v_pool, table, pool_blocks, fresh_base,
+            (float *)out, M, H, T, d, B * M, t, L, 1.0f / sqrtf((float)d));
+        return hipGetLastError();
+    }
+    const float sl2 = 1.4426950408889634f / sqrtf((float)d);
+    const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
+    uint16_t *oo = (uint16_t *)out;
+    JointArgs jn;
+    jn.k_new = (const uint16_t *)k_new;
+    jn.v_new = (const uint16_t *)v_new;
+    jn.k_pool = (uint16_t *)k_pool;
+    jn.v_pool = (uint16_t *)v_pool;
+    jn.table = table;
+    jn.pool_blocks = pool_blocks;
+    jn.fresh_base = fresh_base;
+    jn.t = t;
+    jn.L = L;
+    const bool big = T > 2 * TT && d <= 64;
+    dim3 grid((M + (big ? 127 : 63)) / (big ? 128 : 64), H, B);
+    if (d == 32) {
+        if (big) k_cross_bf16<32, 2, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
+        else k_cross_bf16<32, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
+    } else if (d == 64) {
+        if (big) k_cross_bf16<64, 2, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
+        else k_cross_bf16<64, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
+    } else {
+        k_cross_bf16<128, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
+    }
     return hipGetLastError();
 }
 

@@ -361,8 +361,11 @@ static void free_trie_dev(gr_trie *t) {
 // is set.  One block answers eqs 5 and 8 for all of a node's children at
 // once: AND the columns of the user's bitmask bits, AND the columns of a
 // location's probe positions and OR over locations.  The total is kept
-// under MAX_SLICE_WORDS by raising min_c.
-constexpr int DEFAULT_SLICE_MIN = 16;
+// under MAX_SLICE_WORDS by raising min_c.  A block answers a probe with one
+// column of ceil(c / 64) words but moves a whole cache line for it, so it
+// pays off over the per-child rows only for wide nodes: 48 children was the
+// fastest threshold measured on the main workload (16, 48, 96 and 160 tried).
+constexpr int DEFAULT_SLICE_MIN = 48;
 constexpr int64_t MAX_SLICE_WORDS = (int64_t)4 << 30;  // 32 GiB
 
 static void build_slices(int64_t num_nodes, const int32_t *off, const int32_t *bmi,
@@ -801,6 +804,33 @@ gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new
     hipError_t e = launch_self_attn(q, k_new, v_new, k_pool, v_pool, pool_blocks, table, fresh_base, R, t, L, H, d_h,
                                     dtype, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_self_attn_paged launch");
+    return GR_OK;
+}
+
+gr_status gr_joint_attn(const void *q, const void *k_ctx, const void *v_ctx, const void *k_new,
+                        const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                        int32_t *table, int64_t fresh_base, int32_t B, int32_t M, int32_t H,
+                        int32_t T_ctx, int32_t d_h, int32_t t, int32_t L, gr_dtype dtype,
+                        void *out, void *stream) {
+    gr_status st = check_attn_common("gr_joint_attn", B, M, H, d_h, dtype);
+    if (st) return st;
+    if (!q || !k_ctx || !v_ctx || !k_new || !v_new || !k_pool || !v_pool || !table || !out)
+        return fail(GR_E_INVALID, "gr_joint_attn: null pointer");
+    if (T_ctx < 1) return fail(GR_E_INVALID, "gr_joint_attn: T_ctx %d < 1", T_ctx);
+    if ((int64_t)B * M * H > INT32_MAX) return fail(GR_E_INVALID, "gr_joint_attn: too many rows");
+    if (L < 1 || L > 16 || t < 0 || t >= L) return fail(GR_E_INVALID, "gr_joint_attn: t %d / L %d invalid", t, L);
+    const int64_t R = (int64_t)B * M;
+    if (fresh_base < 0 || pool_blocks < 0 || fresh_base + R > pool_blocks || fresh_base + R > INT32_MAX)
+        return fail(GR_E_INVALID, "gr_joint_attn: blocks [%lld, %lld) exceed pool of %lld",
+                    (long long)fresh_base, (long long)(fresh_base + R), (long long)pool_blocks);
+    if (dtype == GR_BF16 && d_h != 32 && d_h != 64 && d_h != 128)
+        return fail(GR_E_UNSUPPORTED, "gr_joint_attn: bf16 d_h %d not in {32, 64, 128}", d_h);
+    if (dtype == GR_F32 && d_h > 64)
+        return fail(GR_E_UNSUPPORTED, "gr_joint_attn: f32 d_h %d > 64", d_h);
+    hipError_t e = launch_joint_attn(q, k_ctx, v_ctx, k_new, v_new, k_pool, v_pool, pool_blocks, table,
+                                     fresh_base, B, M, H, T_ctx, d_h, t, L, dtype, out,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_joint_attn launch");
     return GR_OK;
 }
 

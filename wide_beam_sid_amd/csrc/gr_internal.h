@@ -86,6 +86,10 @@ hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t pool_blocks, int32_t *table,
                             int64_t fresh_base, int R, int t, int L, int H, int d,
                             gr_dtype dt, void *out, hipStream_t s);
+hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const void *k_new,
+                             const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                             int32_t *table, int64_t fresh_base, int B, int M, int H, int T, int d,
+                             int t, int L, gr_dtype dt, void *out, hipStream_t s);
 hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 
