@@ -19,6 +19,8 @@ Parity status per function (pins live in tests/test_oracle_*.py):
                     T_ctx = 1, q = 0, identical keys
   self_attn         pinned: T_self = 1, coalesced block-diagonal tile of
                     Section 5.2, torch SDPA fp64 per row
+  post.post_filter  pinned: hand-worked example, brute-force properties
+                    (tests/test_oracle_post.py)
   joint_attn        pinned: no beam positions = cross_attn; the log-sum-exp
                     merge of the pinned cross_attn and self_attn results;
                     identical keys (mean of every value); q = 0
