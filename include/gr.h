@@ -362,6 +362,44 @@ gr_status gr_decode_graph_create(const gr_trie *trie, const gr_step_args *steps,
 gr_status gr_decode_graph_launch(const gr_graph *graph, void *stream);
 void gr_decode_graph_destroy(gr_graph *graph);
 
+/* ===================================================================== */
+/* Post stage (GRACE Section 2.1 steps 3-4, Section 2.2): the SID-to-ad    */
+/* index expands finished SIDs into ads, and the exact ad-level matcher   */
+/* (the ads targeting index) filters them.  Host memory and host threads, */
+/* as the pages place this stage on the CPU.                               */
+/* ===================================================================== */
+/*
+ * gr_ad_index_create takes the catalog (sids [n_sids, sid_length] int32,
+ * distinct rows, tokens in [0, vocab_size)); gr_ad_index_add_ads appends
+ * ads in id order (ad_sid [n] = catalog row, rules [n, w_bm] u64,
+ * geo_offsets [n + 1] into geo_ids, as for gr_trie_builder_add_ads);
+ * gr_ad_index_finish freezes it.  The index copies what it needs.
+ *
+ * gr_post_filter expands each row of tokens [n_rows, sid_length] (rows of
+ * request b = r / rows_per_request; a row with a token outside [0, V), such
+ * as a dead slot's -1, or a SID not in the catalog expands to nothing) and
+ * tests every ad: it passes the bitmask part when each bit of
+ * user_bm[b, :w_bm] is set in its rule words, the location part when one of
+ * user_locs[b, :n_loc] is in its geo list (always, if n_loc = 0), and the
+ * matcher when both do.  counts [n_rows, 4] int64 receive, per row: ads
+ * expanded, bitmask passes, location passes, passes.  If pass_ids is not
+ * NULL it receives the ids of the passing ads row by row (offsets = prefix
+ * sums of counts[:, 3]); GR_E_WORKSPACE if they exceed pass_cap (counts are
+ * still written).  n_threads <= 0: all hardware threads.
+ */
+typedef struct gr_ad_index gr_ad_index;
+gr_status gr_ad_index_create(const int32_t *sids, int64_t n_sids, int32_t sid_length,
+                             int32_t vocab_size, int32_t w_bm, gr_ad_index **out);
+gr_status gr_ad_index_add_ads(gr_ad_index *index, int64_t n_ads, const int64_t *ad_sid,
+                              const uint64_t *rules, const int64_t *geo_offsets,
+                              const int32_t *geo_ids);
+gr_status gr_ad_index_finish(gr_ad_index *index);
+gr_status gr_post_filter(const gr_ad_index *index, const int32_t *tokens, int64_t n_rows,
+                         int64_t rows_per_request, const uint64_t *user_bm,
+                         const int32_t *user_locs, int32_t n_loc, int64_t *counts,
+                         int64_t *pass_ids, int64_t pass_cap, int32_t n_threads);
+void gr_ad_index_destroy(gr_ad_index *index);
+
 #ifdef __cplusplus
 }
 #endif

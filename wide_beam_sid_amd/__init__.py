@@ -20,7 +20,7 @@ from ._lib import GR_BF16, GR_F32, GrError, StepArgs, TailArgs, TrieParams, Trie
 __all__ = [
     "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged", "joint_attn",
     "constrain_topk_workspace", "constrain_topk", "constrain", "topk_reorder", "decode_step",
-    "DecodeGraph", "version",
+    "DecodeGraph", "AdIndex", "version",
 ]
 
 
@@ -259,6 +259,62 @@ class DecodeGraph:
         h = getattr(self, "h", None)
         if h is not None and h.value:
             _lib.lib().gr_decode_graph_destroy(h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class AdIndex:
+    """SID-to-ad index plus the ads' targeting (host), for the post stage
+    (see gr_ad_index_create / gr_post_filter)."""
+
+    def __init__(self, sids: np.ndarray, vocab_size: int, w_bm: int, ad_chunks):
+        L = _lib.lib()
+        sids = np.ascontiguousarray(sids, dtype=np.int32)
+        h = ctypes.c_void_p()
+        check(L.gr_ad_index_create(_ptr(sids), sids.shape[0], sids.shape[1], vocab_size, w_bm,
+                                   ctypes.byref(h)))
+        self.h = h
+        self.sid_length = sids.shape[1]
+        try:
+            for ch in ad_chunks:
+                ad_sid = np.ascontiguousarray(ch.ad_sid, dtype=np.int64)
+                rules = np.ascontiguousarray(ch.rules, dtype=np.uint64)
+                go = np.ascontiguousarray(ch.geo_offsets, dtype=np.int64)
+                gi = np.ascontiguousarray(ch.geo_ids, dtype=np.int32)
+                check(L.gr_ad_index_add_ads(h, ad_sid.size, _ptr(ad_sid), _ptr(rules), _ptr(go),
+                                            _ptr(gi) if gi.size else None))
+            check(L.gr_ad_index_finish(h))
+        except Exception:
+            self.close()
+            raise
+
+    def post_filter(self, tokens: np.ndarray, rows_per_request: int, user_bm: np.ndarray,
+                    user_locs: Optional[np.ndarray], n_threads: int = 0):
+        """Per row [ads, bitmask passes, location passes, passes] (int64
+        [n, 4]) and the passing ad ids row by row."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1, self.sid_length)
+        ubm = np.ascontiguousarray(user_bm, dtype=np.uint64)
+        n_loc = 0 if user_locs is None else int(user_locs.shape[1])
+        locs = None if not n_loc else np.ascontiguousarray(user_locs, dtype=np.int32)
+        counts = np.zeros((tokens.shape[0], 4), np.int64)
+        L = _lib.lib()
+        check(L.gr_post_filter(self.h, _ptr(tokens), tokens.shape[0], rows_per_request, _ptr(ubm),
+                               _ptr(locs), n_loc, _ptr(counts), None, 0, n_threads))
+        total = int(counts[:, 3].sum())
+        ids = np.zeros(max(total, 1), np.int64)
+        check(L.gr_post_filter(self.h, _ptr(tokens), tokens.shape[0], rows_per_request, _ptr(ubm),
+                               _ptr(locs), n_loc, _ptr(counts), _ptr(ids), ids.size, n_threads))
+        return counts, ids[:total]
+
+    def close(self) -> None:
+        h = getattr(self, "h", None)
+        if h is not None and h.value:
+            _lib.lib().gr_ad_index_destroy(h)
         self.h = None
 
     def __del__(self):

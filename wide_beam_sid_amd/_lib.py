@@ -24,7 +24,8 @@ EXPORTS = [
     "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged", "gr_joint_attn",
     "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
     "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
-    "gr_decode_graph_destroy",
+    "gr_decode_graph_destroy", "gr_ad_index_create", "gr_ad_index_add_ads",
+    "gr_ad_index_finish", "gr_post_filter", "gr_ad_index_destroy",
 ]
 
 
@@ -109,10 +110,16 @@ def lib() -> ctypes.CDLL:
     L.gr_decode_graph_launch.argtypes = [P, P]
     L.gr_decode_graph_destroy.argtypes = [P]
     L.gr_decode_graph_destroy.restype = None
+    L.gr_ad_index_create.argtypes = [P, i64, i32, i32, i32, ctypes.POINTER(P)]
+    L.gr_ad_index_add_ads.argtypes = [P, i64, P, P, P, P]
+    L.gr_ad_index_finish.argtypes = [P]
+    L.gr_post_filter.argtypes = [P, P, i64, i64, P, P, i32, P, P, i64, i32]
+    L.gr_ad_index_destroy.argtypes = [P]
+    L.gr_ad_index_destroy.restype = None
     for name in EXPORTS:
         if name not in ("gr_last_error", "gr_version", "gr_trie_builder_destroy",
                         "gr_trie_destroy", "gr_constrain_topk_workspace",
-                        "gr_decode_graph_destroy"):
+                        "gr_decode_graph_destroy", "gr_ad_index_destroy"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgr.so")
-SOURCES = ["gr_host.cpp", "cross_attn.hip", "self_attn.hip", "constrain.hip"]
+SOURCES = ["gr_host.cpp", "post.cpp", "cross_attn.hip", "self_attn.hip", "constrain.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -37,6 +37,12 @@ gr_status hip_fail(hipError_t e, const char *what) {
     return fail(GR_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+gr_status gr::report(gr_status st, const char *msg) { return fail(st, "%s", msg); }
+
+namespace {
+
 int hw_threads(int req) {
     if (req > 0) return req;
     unsigned n = std::thread::hardware_concurrency();
@@ -952,15 +958,13 @@ static gr_status check_step(const gr_trie *trie, const gr_step_args *s) {
 
 static gr_status launch_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
     const gr_tail_args &a = s->tail;
-    const int R = a.B * a.M_in;
     hipStream_t hs = (hipStream_t)stream;
-    hipError_t e = launch_cross_attn(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
-                                     s->d_h, a.dtype, hs);
-    if (e != hipSuccess) return hip_fail(e, "gr_decode_step cross-attention launch");
-    e = launch_self_attn(s->q, s->k_new, s->v_new, s->k_pool, s->v_pool, s->pool_blocks,
-                         const_cast<int32_t *>(a.table_in),
-                         s->fresh_base, R, a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs);
-    if (e != hipSuccess) return hip_fail(e, "gr_decode_step self-attention launch");
+    // A1 and A2 are independent: one launch runs both
+    hipError_t e = launch_attn_pair(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H,
+                                    s->T_ctx, s->d_h, s->q, s->k_new, s->v_new, s->k_pool,
+                                    s->v_pool, s->pool_blocks, const_cast<int32_t *>(a.table_in),
+                                    s->fresh_base, a.t, a.L, a.dtype, s->self_out, hs);
+    if (e != hipSuccess) return hip_fail(e, "gr_decode_step attention launch");
     e = launch_constrain(trie->d, a, hs);
     if (e == hipSuccess) e = launch_topk_reorder(trie->d, a, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");

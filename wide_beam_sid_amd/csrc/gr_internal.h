@@ -86,11 +86,19 @@ hipError_t launch_self_attn(const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t pool_blocks, int32_t *table,
                             int64_t fresh_base, int R, int t, int L, int H, int d,
                             gr_dtype dt, void *out, hipStream_t s);
+hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx, void *cross_out,
+                            int B, int M, int H, int T, int d, const void *q, const void *k_new,
+                            const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                            int32_t *table, int64_t fresh_base, int t, int L, gr_dtype dt,
+                            void *self_out, hipStream_t s);
 hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const void *k_new,
                              const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
                              int32_t *table, int64_t fresh_base, int B, int M, int H, int T, int d,
                              int t, int L, gr_dtype dt, void *out, hipStream_t s);
 hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
+
+// Records msg as the message gr_last_error returns and returns st.
+gr_status report(gr_status st, const char *msg);
 hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 
 }  // namespace gr
