@@ -18,6 +18,7 @@
 // fp32 path (small heads): one wavefront per (row, head), lanes over d.
 #include "gr_device.h"
 #include "gr_internal.h"
+#include "self_attn_body.h"
 
 namespace gr {
 namespace {
@@ -61,11 +62,12 @@ struct JointArgs {
 // weighted value; position t is the current token, which also goes to the
 // pool.  One output, no partial results leave the kernel.
 template <int D, int RB, bool JOINT>
-__global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restrict__ q,
-                                                       const uint16_t *__restrict__ K,
-                                                       const uint16_t *__restrict__ Vv,
-                                                       uint16_t *__restrict__ out, int M, int H,
-                                                       int T, float scale_log2, JointArgs jn) {
+__device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
+                                           const uint16_t *__restrict__ K,
+                                           const uint16_t *__restrict__ Vv,
+                                           uint16_t *__restrict__ out, int M, int H, int T,
+                                           float scale_log2, const JointArgs &jn, int bx, int h,
+                                           int b) {
     constexpr int NDC = D / 32;   // k steps of S = Q K^T
     constexpr int NDB = D / 16;   // 16-wide blocks of d in O^T
     constexpr int ROWS = 4 * RB * 16;
@@ -77,8 +79,7 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, a = lane & 15;
-    const int b = blockIdx.z, h = blockIdx.y;
-    const int mbase = blockIdx.x * ROWS + wave * RB * 16;
+    const int mbase = bx * ROWS + wave * RB * 16;
     const size_t kvbase = ((size_t)b * H + h) * (size_t)T * D;
 
     uint4 kr[KU], vr[VU][2];
@@ -309,6 +310,38 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
     }
 }
 
+template <int D, int RB, bool JOINT>
+__global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ K,
+                                                       const uint16_t *__restrict__ Vv,
+                                                       uint16_t *__restrict__ out, int M, int H,
+                                                       int T, float scale_log2, JointArgs jn) {
+    cross_rows<D, RB, JOINT>(q, K, Vv, out, M, H, T, scale_log2, jn, blockIdx.x, blockIdx.y,
+                             blockIdx.z);
+}
+
+// Cross- and self-attention of one decode step in one launch (they are
+// independent): the first n_cross workgroups take the cross-attention tiles
+// (x fastest, then head, then request), the rest take four self-attention
+// rows each.  Saves a launch and lets the MFMA-bound tiles and the
+// gather-bound rows share the machine.
+template <int D, int RB, int NCH>
+__global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict__ q,
+                                                      const uint16_t *__restrict__ K,
+                                                      const uint16_t *__restrict__ Vv,
+                                                      uint16_t *__restrict__ out, int M, int H,
+                                                      int T, float scale_log2, int gxc,
+                                                      int n_cross, SelfParams sp) {
+    const int blk = blockIdx.x;
+    if (blk < n_cross) {
+        const int bx = blk % gxc, rest = blk / gxc;
+        const JointArgs nj{};
+        cross_rows<D, RB, false>(q, K, Vv, out, M, H, T, scale_log2, nj, bx, rest % H, rest / H);
+    } else {
+        self_attn_rows<true, NCH>(sp, blk - n_cross);
+    }
+}
+
 // fp32: one wavefront per (row, head), lane x holds q[x], online softmax.
 __global__ __launch_bounds__(256) void k_cross_f32(const float *__restrict__ q,
                                                    const float *__restrict__ K,
@@ -457,6 +490,53 @@ hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const 
     } else {
         k_cross_bf16<128, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx, void *cross_out,
+                            int B, int M, int H, int T, int d, const void *q, const void *k_new,
+                            const void *v_new, void *k_pool, void *v_pool, int64_t pool_blocks,
+                            int32_t *table, int64_t fresh_base, int t, int L, gr_dtype dt,
+                            void *self_out, hipStream_t s) {
+    const int R = B * M;
+    const SelfParams sp = self_params(q, k_new, v_new, k_pool, v_pool, pool_blocks, table,
+                                      fresh_base, R, t, L, H, d, dt, self_out);
+    const int nch = self_chunks(sp, dt == GR_BF16);
+    if (dt != GR_BF16 || nch > 4) {   // two launches
+        hipError_t e = launch_cross_attn(qx, k_ctx, v_ctx, cross_out, B, M, H, T, d, dt, s);
+        if (e != hipSuccess) return e;
+        return launch_self_attn(q, k_new, v_new, k_pool, v_pool, pool_blocks, table, fresh_base,
+                                R, t, L, H, d, dt, self_out, s);
+    }
+    const float sl2 = 1.4426950408889634f / sqrtf((float)d);
+    const uint16_t *qq = (const uint16_t *)qx, *kk = (const uint16_t *)k_ctx,
+                   *vv = (const uint16_t *)v_ctx;
+    uint16_t *oo = (uint16_t *)cross_out;
+    const bool big = T > 2 * TT && d <= 64;
+    const int rows = big ? 128 : 64;
+    const int gxc = (M + rows - 1) / rows;
+    const int n_cross = gxc * H * B;
+    const dim3 grid(n_cross + (R + 3) / 4);
+#define GR_PAIR(DD, RBB)                                                                        \
+    {                                                                                           \
+        if (nch <= 1)                                                                           \
+            k_attn_pair<DD, RBB, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
+                                                         n_cross, sp);                          \
+        else if (nch <= 2)                                                                      \
+            k_attn_pair<DD, RBB, 2><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
+                                                         n_cross, sp);                          \
+        else                                                                                    \
+            k_attn_pair<DD, RBB, 4><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
+                                                         n_cross, sp);                          \
+    }
+    if (d == 32) {
+        if (big) GR_PAIR(32, 2) else GR_PAIR(32, 1)
+    } else if (d == 64) {
+        if (big) GR_PAIR(64, 2) else GR_PAIR(64, 1)
+    } else {
+        GR_PAIR(128, 1)
+    }
+#undef GR_PAIR
     return hipGetLastError();
 }
 
