@@ -49,8 +49,8 @@ def log(*a):
 
 
 KERNEL_SOURCES = ["wide_beam_sid_amd/csrc/constrain.hip", "wide_beam_sid_amd/csrc/cross_attn.hip",
-                  "wide_beam_sid_amd/csrc/self_attn.hip", "wide_beam_sid_amd/csrc/gr_device.h",
-                  "wide_beam_sid_amd/csrc/gr_internal.h"]
+                  "wide_beam_sid_amd/csrc/self_attn.hip", "wide_beam_sid_amd/csrc/self_attn_body.h",
+                  "wide_beam_sid_amd/csrc/gr_device.h", "wide_beam_sid_amd/csrc/gr_internal.h"]
 TRAFFIC_FILE = "profiles/traffic_main_b16_m1024.json"
 
 
@@ -107,6 +107,7 @@ class Bench:
         t0 = time.time()
         self.trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads],
                                   keep_host=True, bloom_slice_min=slice_min)
+        self.slice_min = slice_min
         self.view = self.trie.host_view()
         log(f"[bench] trie {self.trie.info()} ({time.time() - t0:.1f} s)")
         self.sids, self.ads = sids, ads
@@ -250,7 +251,11 @@ def algorithmic_units(b: Bench):
         # the parents' token / block-table rows
         sel_b = 8 * surv[t] + 4 * n_sel + w.B * k * (16 + 2 * w.L * 4) + n_sel * 2 * t * 4
         tail_b = con_b + sel_b
+        # rows whose node has a bit-sliced block (48 children: the library default)
+        smin = {0: 48, -1: 1 << 30}.get(b.slice_min, b.slice_min)
+        wide_rows = cnt >= smin
         res.append(dict(t=t, R=R, live_in=int(live.sum()), cross_bytes=int(cross_b),
+                        sliced_rows=int(wide_rows.sum()), sliced_entries=int(cnt[wide_rows].sum()),
                         cross_flops=int(cross_f), self_bytes=int(self_b),
                         uniq_prefix_blocks=int(uniq_blk), tail_bytes=int(tail_b),
                         constrain_bytes=int(con_b), topk_bytes=int(sel_b), survivors=surv[t],
@@ -275,10 +280,10 @@ def cpu_model() -> str:
     return platform.machine()
 
 
-def cpu_baseline(b: Bench, n_req: int):
-    """The oracle's decode of the first n_req requests (all L SID steps,
-    attention, masks, top-k, reorder), timed on the host; index build
-    excluded."""
+def cpu_baseline(b: Bench, n_req: int, min_seconds: float = 10.0):
+    """The oracle's decodes of the first n_req requests (all L SID steps,
+    attention, masks, top-k, reorder), repeated on fresh step inputs until
+    about min_seconds of host time; index build excluded."""
     import oracle
     from oracle.decode import initial_state, step as oracle_step
     W, w = b.W, b.w
@@ -291,23 +296,27 @@ def cpu_baseline(b: Bench, n_req: int):
     req = W.Requests(b.req.attrs[:n_req], b.req.user_bm[:n_req], b.req.locs[:n_req])
     kc, vc = W.make_context(w, b.seed)
     ctx = (kc[:n_req], vc[:n_req])
-    st = initial_state(w1)
     rows = 0
     spent = 0.0
-    for t in range(w.L):
-        full = W.make_step(w, b.seed, t)
-        R1 = w1.rows(t)
-        inp = {k: v[:R1] for k, v in full.items()}
-        t0 = time.perf_counter()
-        ref = oracle_step(w1, ix, req, ctx, t, st, inp, lambda a: W.as_float(w, a))
-        spent += time.perf_counter() - t0
-        rows += R1
-        st = ref.next_state
-        log(f"[cpu] t={t} rows={R1} cumulative {spent:.2f} s")
+    decodes = 0
+    # whole decodes of fresh seeded step inputs until about 10 s of CPU work
+    while decodes < 8 and (decodes == 0 or spent < min_seconds):
+        st = initial_state(w1)
+        for t in range(w.L):
+            full = W.make_step(w, b.seed + decodes, t)
+            R1 = w1.rows(t)
+            inp = {k: v[:R1] for k, v in full.items()}
+            t0 = time.perf_counter()
+            ref = oracle_step(w1, ix, req, ctx, t, st, inp, lambda a: W.as_float(w, a))
+            spent += time.perf_counter() - t0
+            rows += R1
+            st = ref.next_state
+        decodes += 1
+        log(f"[cpu] decode {decodes}: cumulative {spent:.2f} s")
     return dict(value=rows / spent, unit="beam-rows/s", cores=threads, kind="oracle",
-                sample=(f"first {n_req} of {w.B} requests, all {w.L} SID steps "
-                        f"({rows} beam rows): cross/self attention in fp64, CD+GTM masks, "
-                        f"log-softmax, top-k, reorder; index build excluded; "
+                sample=(f"{decodes} decodes of the first {n_req} of {w.B} requests, all {w.L} "
+                        f"SID steps ({rows} beam rows): cross/self attention in fp64, CD+GTM "
+                        f"masks, log-softmax, top-k, reorder; index build excluded; "
                         f"{spent:.1f} s on {cpu_model()}"),
                 seconds=spent)
 
