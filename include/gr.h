@@ -80,6 +80,20 @@ typedef struct {
                          /* Bloom and bitmask rows, which answers eqs 5 and 8   */
                          /* for all children at once (0: 48, -1: none); see      */
                          /* gr_trie_view.slice_words                             */
+    /* k-way partitioned matchers (GRACE Section 4.2 and Figure 3; the      */
+    /* modes of Section 6): each child entry keeps up to k partition unions */
+    /* instead of one subtree union, and passes when one partition passes   */
+    /* both the bitmask and the Bloom test.  The descendants of a node are  */
+    /* its SIDs in ascending order; each goes to the partition whose union  */
+    /* has the fewest set bits (bitmask and Bloom words together) after     */
+    /* adding it, the lowest index on a tie; empty partitions are dropped.  */
+    int32_t kway_mode;   /* 0: one union per entry (CD + GTM); 1: static, k =   */
+                         /* kway_k[depth - 1]; 2: dynamic, k = 1, 2, ... until  */
+                         /* the mean fill of the partitions is at most          */
+                         /* kway_target_fill or k = kway_kmax                   */
+    int32_t kway_k[16];  /* static: partitions per decoding position (>= 1)    */
+    int32_t kway_kmax;   /* dynamic: largest k (>= 1)                           */
+    float kway_target_fill; /* dynamic: fill target in (0, 1]                  */
 } gr_trie_params;
 
 /*
@@ -140,6 +154,13 @@ typedef struct {
     const int16_t *node_token;     /* [num_nodes] (view only)                    */
     int64_t slice_words;           /* 8-byte words of bit-sliced matcher blocks   */
                                    /* on the device (info only)                   */
+    /* k-way partitioned matchers (NULL / 0 without them): entry e's       */
+    /* partitions are kway_bitmask_index / kway_bloom_index [kway_offsets[e] */
+    /* .. kway_offsets[e + 1]), rows of the same deduplicated tables.       */
+    const int32_t *kway_offsets;   /* [num_entries + 1]                           */
+    const int32_t *kway_bitmask_index; /* [kway_rows]                             */
+    const int32_t *kway_bloom_index;   /* [kway_rows] (or NULL)                   */
+    int64_t kway_rows;
 } gr_trie_view;
 
 /*

@@ -72,15 +72,21 @@ class Trie:
     @classmethod
     def build(cls, sids: np.ndarray, vocab_size: int, w_bm: int, bloom_bits: int,
               bloom_k: int, ad_chunks, keep_host: bool = False, n_threads: int = 0,
-              host_only: bool = False, bloom_slice_min: int = 0) -> "Trie":
+              host_only: bool = False, bloom_slice_min: int = 0, kway_mode: int = 0,
+              kway_k=(), kway_kmax: int = 0, kway_target_fill: float = 0.0) -> "Trie":
         """Build from the catalog and an iterable of ad chunks (objects with
-        ad_sid, rules, geo_offsets, geo_ids)."""
+        ad_sid, rules, geo_offsets, geo_ids).  kway_mode 1 (static, kway_k per
+        decoding position) or 2 (dynamic, kway_kmax, kway_target_fill) keeps
+        k-way partitioned matchers (see gr_trie_params)."""
         L = _lib.lib()
         sids = np.ascontiguousarray(sids, dtype=np.int32)
         p = TrieParams(sid_length=sids.shape[1], vocab_size=vocab_size, w_bm=w_bm,
                        bloom_bits=bloom_bits, bloom_k=bloom_k, n_threads=n_threads,
                        keep_host=int(keep_host), host_only=int(host_only),
-                       bloom_slice_min=bloom_slice_min)
+                       bloom_slice_min=bloom_slice_min, kway_mode=kway_mode,
+                       kway_kmax=kway_kmax, kway_target_fill=kway_target_fill)
+        for i, k in enumerate(kway_k):
+            p.kway_k[i] = k
         b = ctypes.c_void_p()
         check(L.gr_trie_builder_create(ctypes.byref(p), _ptr(sids), sids.shape[0], ctypes.byref(b)))
         try:
@@ -123,7 +129,7 @@ class Trie:
         check(_lib.lib().gr_trie_info(self.h, ctypes.byref(v)))
         return {k: getattr(v, k) for k in ("vocab_size", "sid_length", "w_bm", "bloom_bits",
                                            "bloom_k", "num_nodes", "num_entries", "bm_rows",
-                                           "bl_rows", "slice_words")}
+                                           "bl_rows", "slice_words", "kway_rows")}
 
     def host_view(self) -> dict:
         """Copies of the host arrays (trie built with keep_host=True)."""
@@ -152,6 +158,11 @@ class Trie:
             "node_parent": arr(v.node_parent, ctypes.c_int32, n, np.int32),
             "node_token": arr(v.node_token, ctypes.c_int16, n, np.int16),
         }
+        if v.kway_offsets:
+            kr = arr(v.kway_offsets, ctypes.c_int32, e + 1, np.int32)
+            out["kway_offsets"] = kr
+            out["kway_bitmask_index"] = arr(v.kway_bitmask_index, ctypes.c_int32, int(kr[-1]), np.int32)
+            out["kway_bloom_index"] = arr(v.kway_bloom_index, ctypes.c_int32, int(kr[-1]), np.int32)
         out.update({k: getattr(v, k) for k in ("vocab_size", "sid_length", "w_bm", "bloom_bits",
                                                 "bloom_k", "num_nodes", "num_entries",
                                                 "bm_rows", "bl_rows")})

@@ -38,7 +38,9 @@ class GrError(RuntimeError):
 class TrieParams(ctypes.Structure):
     _fields_ = [("sid_length", i32), ("vocab_size", i32), ("w_bm", i32),
                 ("bloom_bits", i32), ("bloom_k", i32), ("n_threads", i32),
-                ("keep_host", i32), ("host_only", i32), ("bloom_slice_min", i32)]
+                ("keep_host", i32), ("host_only", i32), ("bloom_slice_min", i32),
+                ("kway_mode", i32), ("kway_k", i32 * 16), ("kway_kmax", i32),
+                ("kway_target_fill", ctypes.c_float)]
 
 
 class TrieView(ctypes.Structure):
@@ -49,7 +51,8 @@ class TrieView(ctypes.Structure):
                 ("bitmask_index", P), ("bloom_index", P),
                 ("bitmask_table", P), ("bloom_table", P),
                 ("node_depth", P), ("node_parent", P), ("node_token", P),
-                ("slice_words", i64)]
+                ("slice_words", i64), ("kway_offsets", P), ("kway_bitmask_index", P),
+                ("kway_bloom_index", P), ("kway_rows", i64)]
 
 
 class TailArgs(ctypes.Structure):

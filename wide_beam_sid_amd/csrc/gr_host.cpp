@@ -165,6 +165,7 @@ struct gr_trie {
     std::vector<int32_t> h_off, h_child, h_bmi, h_bli, h_depth, h_parent;
     std::vector<int16_t> h_tok, h_ntok;
     std::vector<uint64_t> h_bm, h_bl;
+    std::vector<int32_t> h_kw_off, h_kw_bmi, h_kw_bli;
     bool host_only = false;
 };
 
@@ -212,6 +213,13 @@ gr_status gr_trie_builder_create(const gr_trie_params *params, const int32_t *si
     }
     if (p.bloom_slice_min < -1)
         return fail(GR_E_INVALID, "bloom_slice_min %d is not -1, 0 or a child count", p.bloom_slice_min);
+    if (p.kway_mode < 0 || p.kway_mode > 2)
+        return fail(GR_E_INVALID, "kway_mode %d not in {0, 1, 2}", p.kway_mode);
+    if (p.kway_mode == 1)
+        for (int l = 0; l < p.sid_length; ++l)
+            if (p.kway_k[l] < 1) return fail(GR_E_INVALID, "kway_k[%d] = %d < 1", l, p.kway_k[l]);
+    if (p.kway_mode == 2 && (p.kway_kmax < 1 || !(p.kway_target_fill > 0.0f) || p.kway_target_fill > 1.0f))
+        return fail(GR_E_INVALID, "dynamic k-way needs kway_kmax >= 1 and kway_target_fill in (0, 1]");
     if (n_sids < 1 || n_sids > (int64_t)1 << 30)
         return fail(GR_E_INVALID, "n_sids %lld not in [1, 2^30]", (long long)n_sids);
     int bpt = 1;
@@ -356,6 +364,9 @@ static void free_trie_dev(gr_trie *t) {
     hipFree((void *)t->d.node_slice);
     hipFree((void *)t->d.slice_table);
     hipFree((void *)t->d.entry_bitmask);
+    hipFree((void *)t->d.kway_offsets);
+    hipFree((void *)t->d.kway_bmi);
+    hipFree((void *)t->d.kway_bli);
     t->d = TrieDev{};
 }
 
@@ -428,10 +439,167 @@ static void build_slices(int64_t num_nodes, const int32_t *off, const int32_t *b
     });
 }
 
+// k-way partitioned matchers (GRACE Section 4.2 and Figure 3).  A node's
+// descendant SIDs are the sorted leaves below it (a contiguous range); each
+// goes, in ascending order, to the partition whose union has the fewest set
+// bits after adding it (bitmask and Bloom words together; the lowest index
+// on a tie); empty partitions are dropped.  Static: k = kway_k[depth - 1].
+// Dynamic: k = 1, 2, 4, ... until the partitions' mean fill is at most the
+// target or k reaches kway_kmax.  k never exceeds the node's SID count.  The
+// partition unions go to the same deduplicated tables as the other rows.
+struct KwayOut {
+    std::vector<int32_t> off, bmi, bli;
+};
+
+static void kway_partitions(const gr_trie_params &p, int depth, const uint64_t *const *leaf_bm,
+                            const uint64_t *const *leaf_bl, int64_t lo, int64_t hi, int wbm,
+                            int wbl, std::vector<uint64_t> &out_rows, int &out_n) {
+    const int W = wbm + wbl;
+    const int64_t n = hi - lo;
+    auto greedy = [&](int k, std::vector<uint64_t> &P, std::vector<int64_t> &ones,
+                      std::vector<int> &used) {
+        P.assign((size_t)k * W, 0ull);
+        ones.assign(k, 0);
+        used.assign(k, 0);
+        for (int64_t i = lo; i < hi; ++i) {
+            const uint64_t *bm = leaf_bm[i - lo], *bl = wbl ? leaf_bl[i - lo] : nullptr;
+            int best = 0;
+            int64_t best_c = INT64_MAX;
+            for (int j = 0; j < k; ++j) {
+                const uint64_t *r = &P[(size_t)j * W];
+                int64_t c = 0;
+                for (int w = 0; w < wbm; ++w) c += __builtin_popcountll(r[w] | bm[w]);
+                for (int w = 0; w < wbl; ++w) c += __builtin_popcountll(r[wbm + w] | bl[w]);
+                if (c < best_c) {
+                    best_c = c;
+                    best = j;
+                }
+            }
+            uint64_t *r = &P[(size_t)best * W];
+            for (int w = 0; w < wbm; ++w) r[w] |= bm[w];
+            for (int w = 0; w < wbl; ++w) r[wbm + w] |= bl[w];
+            ones[best] = best_c;
+            used[best] = 1;
+        }
+    };
+    std::vector<uint64_t> P;
+    std::vector<int64_t> ones;
+    std::vector<int> used;
+    if (p.kway_mode == 1) {
+        greedy((int)std::min<int64_t>(p.kway_k[depth - 1], n), P, ones, used);
+    } else {
+        const int kcap = (int)std::min<int64_t>(p.kway_kmax, n);
+        for (int k = 1;; k = std::min(2 * k, kcap)) {
+            greedy(k, P, ones, used);
+            int64_t tot = 0, nu = 0;
+            for (int j = 0; j < k; ++j) {
+                tot += ones[j];
+                nu += used[j];
+            }
+            const double fill = (double)tot / ((double)nu * 64.0 * W);
+            if (fill <= p.kway_target_fill || k >= kcap) break;
+        }
+    }
+    out_rows.clear();
+    out_n = 0;
+    for (size_t j = 0; j < used.size(); ++j)
+        if (used[j]) {
+            out_rows.insert(out_rows.end(), P.begin() + (ptrdiff_t)(j * W), P.begin() + (ptrdiff_t)((j + 1) * W));
+            ++out_n;
+        }
+}
+
+// Appends row r to table T (deduplicated); returns its id.
+static int32_t table_add(RowTable &T, const uint64_t *r) {
+    if ((size_t)(T.n + 1) * T.w > T.rows.size()) T.rows.resize(((size_t)T.n + 1) * T.w * 2);
+    std::memcpy(&T.rows[(size_t)T.n * T.w], r, sizeof(uint64_t) * T.w);
+    return T.insert(&T.rows[(size_t)T.n * T.w]);
+}
+
+static void build_kway(const gr_trie_params &p, int L, int bpt, int wbm, int wbl,
+                       const std::vector<uint64_t> &leaf_key,
+                       const std::vector<std::vector<uint64_t>> &pk, const std::vector<int64_t> &base,
+                       int64_t num_entries, const std::vector<int32_t> &bmi,
+                       const std::vector<int32_t> &bli, std::vector<uint64_t> &bm_store,
+                       int64_t &bm_rows, std::vector<uint64_t> &bl_store, int64_t &bl_rows,
+                       int threads, KwayOut &o) {
+    const int64_t n_leaf = (int64_t)leaf_key.size();
+    // the tables as they stand, then the partition unions appended
+    auto reopen = [](RowTable &T, std::vector<uint64_t> &store, int w, int64_t n) {
+        T.rows.swap(store);
+        T.init(w, n * 2);
+        for (int64_t r = 0; r < n; ++r) T.insert(&T.rows[(size_t)r * w]);
+    };
+    RowTable tbm, tbl;
+    reopen(tbm, bm_store, wbm, bm_rows);
+    if (wbl) reopen(tbl, bl_store, wbl, bl_rows);
+    // each leaf's own rows (pointers into the tables, stable while rows only
+    // get appended in the serial merge: copied up front)
+    std::vector<uint64_t> lbm((size_t)n_leaf * wbm), lbl((size_t)n_leaf * wbl);
+    for (int64_t i = 0; i < n_leaf; ++i) {
+        const int64_t e = base[L] + i - 1;
+        std::memcpy(&lbm[(size_t)i * wbm], &tbm.rows[(size_t)bmi[e] * wbm], sizeof(uint64_t) * wbm);
+        if (wbl) std::memcpy(&lbl[(size_t)i * wbl], &tbl.rows[(size_t)bli[e] * wbl], sizeof(uint64_t) * wbl);
+    }
+    std::vector<const uint64_t *> pbm((size_t)n_leaf), pbl((size_t)n_leaf);
+    for (int64_t i = 0; i < n_leaf; ++i) {
+        pbm[i] = &lbm[(size_t)i * wbm];
+        pbl[i] = wbl ? &lbl[(size_t)i * wbl] : nullptr;
+    }
+    o.off.assign((size_t)num_entries + 1, 0);
+    o.bmi.clear();
+    o.bli.clear();
+    const int W = wbm + wbl;
+    for (int l = 1; l <= L; ++l) {
+        const int sh = (L - l) * bpt;
+        const int64_t nn = (int64_t)pk[l].size();
+        std::vector<int64_t> lo((size_t)nn), hi((size_t)nn);
+        for (int64_t i = 0, j = 0; i < nn; ++i) {
+            lo[i] = j;
+            while (j < n_leaf && (leaf_key[j] >> sh) == pk[l][i]) ++j;
+            hi[i] = j;
+        }
+        const int64_t CH = 4096;   // nodes per parallel batch, merged serially
+        std::vector<std::vector<uint64_t>> rows((size_t)CH);
+        std::vector<int> cnt((size_t)CH);
+        for (int64_t c0 = 0; c0 < nn; c0 += CH) {
+            const int64_t c1 = std::min(nn, c0 + CH);
+            parallel_for(c1 - c0, threads, [&](int64_t a, int64_t b2) {
+                for (int64_t q = a; q < b2; ++q) {
+                    const int64_t i = c0 + q;
+                    kway_partitions(p, l, pbm.data() + lo[i], pbl.data() + lo[i], lo[i], hi[i], wbm,
+                                    wbl, rows[(size_t)q], cnt[(size_t)q]);
+                }
+            });
+            for (int64_t q = 0; q < c1 - c0; ++q) {
+                const int64_t e = base[l] + c0 + q - 1;   // entry of node base[l] + i
+                for (int j = 0; j < cnt[(size_t)q]; ++j) {
+                    const uint64_t *r = &rows[(size_t)q][(size_t)j * W];
+                    o.bmi.push_back(table_add(tbm, r));
+                    if (wbl) o.bli.push_back(table_add(tbl, r + wbm));
+                }
+                o.off[(size_t)e + 1] = (int32_t)o.bmi.size();
+            }
+        }
+    }
+    for (int64_t e = 1; e <= num_entries; ++e)   // entries are filled in order
+        if (o.off[(size_t)e] < o.off[(size_t)e - 1]) o.off[(size_t)e] = o.off[(size_t)e - 1];
+    tbm.rows.resize((size_t)tbm.n * wbm);
+    bm_store.swap(tbm.rows);
+    bm_rows = tbm.n;
+    if (wbl) {
+        tbl.rows.resize((size_t)tbl.n * wbl);
+        bl_store.swap(tbl.rows);
+        bl_rows = tbl.n;
+    }
+}
+
 static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *child,
                              const int16_t *tok, const int32_t *bmi, const int32_t *bli,
                              const uint64_t *bm, const uint64_t *bl, int slice_min,
-                             int threads) {
+                             int threads, const int32_t *kw_off = nullptr,
+                             const int32_t *kw_bmi = nullptr, const int32_t *kw_bli = nullptr,
+                             int64_t kw_rows = 0) {
     hipError_t e;
     int32_t *d_off, *d_child, *d_bmi, *d_bli = nullptr;
     int16_t *d_tok;
@@ -471,6 +639,19 @@ static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *chil
         d.bloom_index = d_bli;
         if ((e = upload(&d_bl, bl, (size_t)d.bl_rows * d.w_bl)) != hipSuccess) goto err;
         d.bloom_table = d_bl;
+    }
+    if (kw_off) {   // k-way partitions replace the one-union rows in the kernels
+        int32_t *d_kwo, *d_kwb, *d_kwl = nullptr;
+        if ((e = upload(&d_kwo, kw_off, (size_t)d.num_entries + 1)) != hipSuccess) goto err;
+        d.kway_offsets = d_kwo;
+        if ((e = upload(&d_kwb, kw_bmi, (size_t)kw_rows)) != hipSuccess) goto err;
+        d.kway_bmi = d_kwb;
+        if (d.w_bl) {
+            if ((e = upload(&d_kwl, kw_bli, (size_t)kw_rows)) != hipSuccess) goto err;
+            d.kway_bli = d_kwl;
+        }
+        d.kway_rows = kw_rows;
+        slice_min = -1;   // the bit-sliced blocks hold one-union rows only
     }
     if (slice_min >= 0) {
         std::vector<int64_t> ns;
@@ -615,8 +796,13 @@ gr_status gr_trie_builder_finish(gr_trie_builder *b, gr_trie **out) {
         int64_t bm_rows = build_rows(b->leaf_bm, wbm, bmi);
         int64_t bl_rows = 0;
         if (wbl) bl_rows = build_rows(b->leaf_bl, wbl, bli);
+        KwayOut kw;
+        if (b->p.kway_mode)
+            build_kway(b->p, L, bpt, wbm, wbl, b->leaf_key, pk, base, num_entries, bmi, bli,
+                       b->leaf_bm, bm_rows, b->leaf_bl, bl_rows, b->threads, kw);
 
         TrieDev &d = t->d;
+        d.kway_rows = (int64_t)kw.bmi.size();
         d.V = b->p.vocab_size;
         d.L = L;
         d.w_bm = wbm;
@@ -631,7 +817,9 @@ gr_status gr_trie_builder_finish(gr_trie_builder *b, gr_trie **out) {
         if (!t->host_only)
             st = upload_trie(t, off.data(), child.data(), tok.data(), bmi.data(),
                              wbl ? bli.data() : nullptr, b->leaf_bm.data(),
-                             wbl ? b->leaf_bl.data() : nullptr, b->p.bloom_slice_min, b->threads);
+                             wbl ? b->leaf_bl.data() : nullptr, b->p.bloom_slice_min, b->threads,
+                             b->p.kway_mode ? kw.off.data() : nullptr, kw.bmi.data(),
+                             wbl ? kw.bli.data() : nullptr, (int64_t)kw.bmi.size());
         if (st == GR_OK && (b->p.keep_host || t->host_only)) {
             t->has_host = true;
             t->h_off.swap(off);
@@ -644,6 +832,9 @@ gr_status gr_trie_builder_finish(gr_trie_builder *b, gr_trie **out) {
             t->h_depth.swap(depth);
             t->h_parent.swap(parent);
             t->h_ntok.swap(ntok);
+            t->h_kw_off.swap(kw.off);
+            t->h_kw_bmi.swap(kw.bmi);
+            t->h_kw_bli.swap(kw.bli);
         }
     } catch (const std::bad_alloc &) {
         st = fail(GR_E_NOMEM, "out of host memory finishing the trie");
@@ -694,6 +885,18 @@ gr_status gr_trie_create(const gr_trie_view *a, gr_trie **out) {
                 return fail(GR_E_INVALID, "bloom_index[%d] = %d out of range", j, a->bloom_index[j]);
         }
     }
+    if (a->kway_offsets) {   // optional k-way partitions
+        if (a->kway_offsets[0] != 0 || a->kway_offsets[a->num_entries] != a->kway_rows ||
+            a->kway_rows < 0 || !a->kway_bitmask_index || (bloom && !a->kway_bloom_index))
+            return fail(GR_E_INVALID, "k-way offsets do not span [0, kway_rows) or an index is missing");
+        for (int64_t e = 0; e < a->num_entries; ++e)
+            if (a->kway_offsets[e + 1] < a->kway_offsets[e])
+                return fail(GR_E_INVALID, "kway_offsets decreases at entry %lld", (long long)e);
+        for (int64_t q = 0; q < a->kway_rows; ++q)
+            if (a->kway_bitmask_index[q] < 0 || a->kway_bitmask_index[q] >= a->bm_rows ||
+                (bloom && (a->kway_bloom_index[q] < 0 || a->kway_bloom_index[q] >= a->bl_rows)))
+                return fail(GR_E_INVALID, "k-way matcher id %lld out of range", (long long)q);
+    }
     gr_trie *t = new (std::nothrow) gr_trie;
     if (!t) return fail(GR_E_NOMEM, "out of host memory");
     TrieDev &d = t->d;
@@ -708,7 +911,9 @@ gr_status gr_trie_create(const gr_trie_view *a, gr_trie **out) {
     d.bm_rows = a->bm_rows;
     d.bl_rows = bloom ? a->bl_rows : 0;
     gr_status st = upload_trie(t, a->node_offsets, a->child_nodes, a->tokens, a->bitmask_index,
-                               a->bloom_index, a->bitmask_table, a->bloom_table, 0, hw_threads(0));
+                               a->bloom_index, a->bitmask_table, a->bloom_table, 0, hw_threads(0),
+                               a->kway_offsets, a->kway_bitmask_index,
+                               bloom ? a->kway_bloom_index : nullptr, a->kway_rows);
     if (st != GR_OK) {
         delete t;
         return st;
@@ -729,6 +934,7 @@ static void fill_sizes(const gr_trie *t, gr_trie_view *o) {
     o->bm_rows = t->d.bm_rows;
     o->bl_rows = t->d.bl_rows;
     o->slice_words = t->d.slice_words;
+    o->kway_rows = t->d.kway_rows;
 }
 
 gr_status gr_trie_info(const gr_trie *t, gr_trie_view *o) {
@@ -751,6 +957,9 @@ gr_status gr_trie_host_view(const gr_trie *t, gr_trie_view *o) {
     o->node_depth = t->h_depth.data();
     o->node_parent = t->h_parent.data();
     o->node_token = t->h_ntok.data();
+    o->kway_offsets = t->h_kw_off.empty() ? nullptr : t->h_kw_off.data();
+    o->kway_bitmask_index = t->h_kw_bmi.empty() ? nullptr : t->h_kw_bmi.data();
+    o->kway_bloom_index = t->h_kw_bli.empty() ? nullptr : t->h_kw_bli.data();
     return GR_OK;
 }
 

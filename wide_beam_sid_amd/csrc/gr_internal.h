@@ -33,6 +33,12 @@ struct TrieDev {
     // null when w_bm > ENTRY_BM_MAX_W): one contiguous read with the entry
     // instead of a dependent gather through bitmask_index.
     const uint64_t *entry_bitmask;
+    // k-way partitioned matchers (null without them): entry e's partitions
+    // are kway_bmi / kway_bli [kway_offsets[e], kway_offsets[e + 1]).
+    const int32_t *kway_offsets;
+    const int32_t *kway_bmi;
+    const int32_t *kway_bli;
+    int64_t kway_rows;
 };
 constexpr int ENTRY_BM_MAX_W = 2;
 
