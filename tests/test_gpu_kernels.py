@@ -212,14 +212,14 @@ def _workspace(nbytes):
     return _WS["ws"]
 
 
-def _trie_case(w, seed, slice_min=0):
-    key = (w, seed, slice_min)
+def _trie_case(w, seed, slice_min=0, kway=None):
+    key = (w, seed, slice_min, None if kway is None else repr(kway))
     if key not in _TRIES:
         gr = _gr()
         sids = W.make_catalog(w, seed)
         ads = W.make_ads(w, seed, W.ad_counts(w, seed))
         trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True,
-                             bloom_slice_min=slice_min)
+                             bloom_slice_min=slice_min, **(kway or {}))
         view = trie.host_view()
         ix = oracle.build_index(w, sids, ads)
         n = view["num_nodes"]
@@ -231,12 +231,12 @@ def _trie_case(w, seed, slice_min=0):
 
 
 def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mode="normal",
-             B=None, slice_min=0, staged=False):
+             B=None, slice_min=0, staged=False, kway=None):
     """Run gr_constrain_topk on synthetic beam rows at depth t and check every
     output against the oracle."""
     gr = _gr()
     B = B or w.B
-    trie, view, ix, prefix = _trie_case(w, seed, slice_min)
+    trie, view, ix, prefix = _trie_case(w, seed, slice_min, kway)
     rng = np.random.default_rng(seed * 31 + M_in + t)
     R = B * M_in
     depth_nodes = np.nonzero(view["node_depth"] == t)[0]
@@ -286,26 +286,55 @@ def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mo
         gr.constrain_topk(trie, args)
     torch.cuda.synchronize()
     o = {k: v.cpu().numpy() for k, v in out.items()}
+    exp_mask = None
+    if kway is not None:   # k-way decisions from the partition oracle
+        from oracle import kway as okway
+        sids = W.make_catalog(w, seed)
+        ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+        rows = okway.leaf_rows(sids, ads, w.w_bm, w.bloom_bits, w.bloom_k)
+        okw = (dict(k_static=kway["kway_k"]) if kway["kway_mode"] == 1
+               else dict(k_max=kway["kway_kmax"], target=kway["kway_target_fill"]))
+        blooms = [[oracle.bloom_row(int(l), w.bloom_bits, w.bloom_k) for l in req.locs[b]]
+                  for b in range(B)] if w.bloom_bits else [[] for _ in range(B)]
+        children = {}
+        for sid in rows:
+            children.setdefault(sid[:t], set()).add(sid[t])
+        memo = {}
+        exp_mask = np.zeros((R, (w.V + 63) // 64), np.uint64)
+        for r in range(R):
+            if node_in[r] < 0:
+                continue
+            b = r // M_in
+            pre = tuple(prefix[node_in[r]])
+            for v in sorted(children.get(pre, ())):
+                key = (b, pre + (v,))
+                if key not in memo:
+                    parts = okway.node_partitions(rows, pre + (v,), kway["kway_mode"], **okw)
+                    memo[key] = okway.passes(parts, req.user_bm[b], blooms[b], w.w_bm)
+                if memo[key]:
+                    exp_mask[r, v // 64] |= np.uint64(1) << np.uint64(v % 64)
+        exp_mask = exp_mask.view(np.uint64)
     check_tail(w, ix, view, prefix, req, node_in, acc_in, W.as_float(w, logits).astype(np.float64),
-               M_in, k_out, t, o, tokens_in, table_in, B)
+               M_in, k_out, t, o, tokens_in, table_in, B, exp_mask=exp_mask)
     return o
 
 
 def check_tail(w, ix, view, prefix, req, node_in, acc_in, logits64, M_in, k_out, t, o,
-               tokens_in=None, table_in=None, B=None):
+               tokens_in=None, table_in=None, B=None, exp_mask=None):
     B = B or w.B
     V, L = w.V, w.L
     R = B * M_in
     mask = o["dbg_mask"].view(np.uint64)
     scores = o["dbg_scores"]
     # A3: masks bit-exact
-    blooms = [ix.user_blooms(req.locs[b]) for b in range(B)]
-    exp_mask = np.zeros_like(mask)
-    for r in range(R):
-        b = r // M_in
-        live = node_in[r] >= 0
-        exp_mask[r] = ix.mask_row(list(prefix[node_in[r]]) if live else [], t if live else -1,
-                                  req.user_bm[b], req.locs[b], blooms[b])
+    if exp_mask is None:
+        blooms = [ix.user_blooms(req.locs[b]) for b in range(B)]
+        exp_mask = np.zeros_like(mask)
+        for r in range(R):
+            b = r // M_in
+            live = node_in[r] >= 0
+            exp_mask[r] = ix.mask_row(list(prefix[node_in[r]]) if live else [], t if live else -1,
+                                      req.user_bm[b], req.locs[b], blooms[b])
     assert np.array_equal(mask, exp_mask), "mask mismatch"
     # A4: scores within tolerance of acc + fp64 log-softmax
     keep = oracle.mask_bits_to_bool(mask, V)
@@ -410,6 +439,21 @@ def test_constrain_topk_k_at_survivor_count(name, seed, M_in, t):
     assert 2 <= n < 1024, n
     for k in (n, n - 1, n + 1):
         run_tail(w, seed, M_in, k, t, 0.0, B=1)
+
+
+_KWAY_W = W.WORKLOADS["main_b16_m1024"].scaled(n_sids=600, B=2, V=16)
+
+
+@pytest.mark.parametrize("kw,t", [
+    (dict(kway_mode=1, kway_k=(8, 4, 3, 2)), 1),
+    (dict(kway_mode=1, kway_k=(8, 4, 3, 2)), 2),
+    (dict(kway_mode=2, kway_kmax=8, kway_target_fill=0.1), 1),
+    (dict(kway_mode=2, kway_kmax=8, kway_target_fill=0.1), 3),
+])
+def test_constrain_topk_kway(kw, t):
+    """k-way partitioned matchers: the GPU's masks equal the partition
+    oracle's decisions; scores, top-k and reorder as for one-union tries."""
+    run_tail(_KWAY_W, 11, 40, 30, t, 0.1, B=2, kway=kw)
 
 
 @pytest.mark.parametrize("slice_min", [-1, 1])

@@ -88,6 +88,7 @@ struct TailParams {
     int vec_logits;     // bf16 logits readable 8 at a time (V % 8 == 0, 16-byte base)
     const uint64_t *ent_bm;   // entry-ordered bitmask rows (null: gather through bmi)
     int vec_rows;             // token / block-table rows movable as 16-byte pieces
+    const int32_t *kw_off, *kw_bmi, *kw_bli;   // k-way partitions (null: one union per entry)
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -254,6 +255,8 @@ void k_expand(TailParams p) {
     __shared__ int32_t s_lc[2][EXP_THREADS];       //   child node,
     __shared__ int32_t s_lb[2][EXP_THREADS];       //   Bloom row (-1 once the test fails)
     __shared__ uint32_t s_nl[2];                   // entries listed so far, per parity
+    __shared__ uint32_t s_kn;                      // k-way: partitions listed this sub-round
+    __shared__ uint8_t s_kok[EXP_THREADS];         // k-way: entry kept (a partition passed)
 
     const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gx = gridDim.x, x = blockIdx.x;
@@ -279,6 +282,7 @@ void k_expand(TailParams p) {
         s_nsurv = 0u;
         s_nl[0] = 0u;
         s_nl[1] = 0u;
+        s_kn = 0u;
     }
     {
         const float ub = bound_part(p, b);
@@ -612,93 +616,10 @@ void k_expand(TailParams p) {
     }
     __syncthreads();
 
-    // The entries of rows without a bit-sliced block: rounds of EXP_THREADS
-    // entries, one per thread (the round count is the same for every thread).  Entries that pass eq 5 and still need eq 8
-    // go to a round list; the list's Bloom tests are then shared by all
-    // wavefronts.  Lists and their counters alternate between rounds, so a
-    // round's list is never written while the previous one is read.
-    uint32_t nlb0 = 0u, nlb1 = 0u;   // list entries consumed, per parity
-    const int n_ent = s_nstart[nrows];
-    for (int c0 = 0, round = 0; c0 < n_ent; c0 += EXP_THREADS, ++round) {
-        const int par = round & 1;
-        const int e = c0 + tid;
-        const bool valid = e < n_ent;
-        int i = 0;
-        if (valid) {  // row of entry e: the largest i with s_nstart[i] <= e
-            int lo = 0, hi = nrows;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_nstart[mid] <= e) lo = mid;
-                else hi = mid;
-            }
-            i = lo;
-        }
-        // One round of loads for the entry (token, child, matcher rows or
-        // ids), then the logit.
-        int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
-        uint64_t bw0 = 0ull, bw1 = 0ull;
-        if (valid) {
-            j = s_roff[i] + (e - s_nstart[i]);
-            v = p.tok[j];
-            child = p.child[j];
-            if (p.ent_bm) {
-                bw0 = p.ent_bm[(size_t)j * p.w_bm];
-                if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
-            } else {
-                bmi = p.bmi[j];
-            }
-            if (wq) bli = p.bli[j];
-            m = s_rm[i];
-        }
-        bool ok = false;
-        float xv = 0.0f;
-        if (valid) {
-            xv = logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
-            if (p.ent_bm) {
-                // eq 5: every user attribute bit present in the entry's row
-                ok = (bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (bw1 & s_ubm[1]) == s_ubm[1]);
-            } else {
-                const uint64_t *bmr = p.bm_tab + (size_t)bmi * p.w_bm;
-                ok = true;
-                for (int w = 0; w < p.w_bm; ++w) {
-                    const uint64_t u = s_ubm[w];
-                    if ((bmr[w] & u) != u) {
-                        ok = false;
-                        break;
-                    }
-                }
-            }
-        }
-        const float score = ok ? s_acc[i] + (xv - s_lse[i]) : -INFINITY;
-        const uint32_t f = (uint32_t)(m * V + v);
-        const bool defer = wq && ok;   // eq 8 still to test
-        if (ok && !defer && p.mask_words) mark(i, v);
-        emit(ok && !defer && score > -INFINITY, score, f, child);
-        if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
-
-        const uint64_t dm = __ballot(defer);
-        if (dm) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_nl[par], (uint32_t)__popcll(dm));
-            base = __shfl(base, 0, 64) - (par ? nlb1 : nlb0);
-            if (defer) {
-                const uint32_t q = base + lanes_below(dm);
-                s_ls[par][q] = score;
-                s_lf[par][q] = f;
-                s_lc[par][q] = child;
-                s_lb[par][q] = bli;
-            }
-        }
-        __syncthreads();
-        const uint32_t tot = s_nl[par];
-        const int n_bl = (int)(tot - (par ? nlb1 : nlb0));
-        if (par) nlb1 = tot;
-        else nlb0 = tot;
-        if (n_bl == 0) continue;   // uniform
-
-        // eq 8 for the round's list: ANY user location whose probe bits are
-        // all set in the entry's Bloom row.  A failed entry's row id becomes -1.
-        int32_t *lb = s_lb[par];
+    // eq 8 for a list of n_bl Bloom row ids lb[0 .. n_bl): ANY user location
+    // whose probe bits are all set in the row.  The wavefronts share the
+    // list; a row that fails becomes -1.  Called by the whole workgroup.
+    auto bloom_list = [&](int32_t *lb, int n_bl) {
         if (WIDE) {
             // CH rows per wavefront batch, loaded into registers in one round
             // (register q holds 8-byte word ((q * 64) mod w_bl) + lane of row
@@ -775,6 +696,153 @@ void k_expand(TailParams p) {
                 if (lane < nq && !((pm >> lane) & 1ull)) lb[g0 + lane] = -1;
             }
         }
+    };
+
+    // The entries of rows without a bit-sliced block: rounds of EXP_THREADS
+    // entries, one per thread (the round count is the same for every thread).  Entries that pass eq 5 and still need eq 8
+    // go to a round list; the list's Bloom tests are then shared by all
+    // wavefronts.  Lists and their counters alternate between rounds, so a
+    // round's list is never written while the previous one is read.
+    uint32_t nlb0 = 0u, nlb1 = 0u;   // list entries consumed, per parity
+    const int n_ent = s_nstart[nrows];
+    for (int c0 = 0, round = 0; c0 < n_ent; c0 += EXP_THREADS, ++round) {
+        const int par = round & 1;
+        const int e = c0 + tid;
+        const bool valid = e < n_ent;
+        int i = 0;
+        if (valid) {  // row of entry e: the largest i with s_nstart[i] <= e
+            int lo = 0, hi = nrows;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_nstart[mid] <= e) lo = mid;
+                else hi = mid;
+            }
+            i = lo;
+        }
+        // One round of loads for the entry (token, child, matcher rows or
+        // ids), then the logit.
+        int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
+        uint64_t bw0 = 0ull, bw1 = 0ull;
+        if (valid) {
+            j = s_roff[i] + (e - s_nstart[i]);
+            v = p.tok[j];
+            child = p.child[j];
+            if (p.ent_bm) {
+                bw0 = p.ent_bm[(size_t)j * p.w_bm];
+                if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
+            } else {
+                bmi = p.bmi[j];
+            }
+            if (wq) bli = p.bli[j];
+            m = s_rm[i];
+        }
+        if (p.kw_off) {
+            // k-way partitioned matchers (uniform branch): the entry is kept
+            // when one of its partitions passes eq 5 and, with a Bloom
+            // matcher, eq 8.  Sub-rounds: every entry still undecided offers
+            // its next partition that passes eq 5; the offered Bloom rows
+            // are tested together by all wavefronts.
+            const float xk = valid ? logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v) : 0.0f;
+            int cur = valid ? p.kw_off[j] : 0;
+            const int q1 = valid ? p.kw_off[j + 1] : 0;
+            auto bm_pass = [&](int q) {
+                const uint64_t *r = p.bm_tab + (size_t)p.kw_bmi[q] * p.w_bm;
+                for (int w = 0; w < p.w_bm; ++w)
+                    if ((r[w] & s_ubm[w]) != s_ubm[w]) return false;
+                return true;
+            };
+            bool kept = false;
+            if (!wq) {
+                while (!kept && cur < q1) kept = bm_pass(cur++);
+            } else {
+                s_kok[tid] = 0;
+                int32_t *lb = s_lb[0];
+                for (;;) {   // the same number of sub-rounds for every thread
+                    int32_t blr = -1;
+                    while (!kept && cur < q1) {
+                        const int q = cur++;
+                        if (bm_pass(q)) {
+                            blr = p.kw_bli[q];
+                            break;
+                        }
+                    }
+                    const uint64_t dm = __ballot(blr >= 0);
+                    if (dm) {
+                        uint32_t base = 0;
+                        if (lane == 0) base = atomicAdd(&s_kn, (uint32_t)__popcll(dm));
+                        base = __shfl(base, 0, 64);
+                        if (blr >= 0) {
+                            const uint32_t qi = base + lanes_below(dm);
+                            lb[qi] = blr;
+                            s_lf[0][qi] = (uint32_t)tid;
+                        }
+                    }
+                    __syncthreads();
+                    const int n_k = (int)s_kn;
+                    if (n_k == 0) break;   // uniform
+                    bloom_list(lb, n_k);
+                    __syncthreads();
+                    if (tid < n_k && lb[tid] >= 0) s_kok[s_lf[0][tid]] = 1;
+                    __syncthreads();
+                    kept = kept || s_kok[tid] != 0;
+                    if (tid == 0) s_kn = 0u;
+                    __syncthreads();
+                }
+            }
+            const float sk = kept ? s_acc[i] + (xk - s_lse[i]) : -INFINITY;
+            if (kept && p.mask_words) mark(i, v);
+            emit(kept && sk > -INFINITY, sk, (uint32_t)(m * V + v), child);
+            continue;
+        }
+        bool ok = false;
+        float xv = 0.0f;
+        if (valid) {
+            xv = logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
+            if (p.ent_bm) {
+                // eq 5: every user attribute bit present in the entry's row
+                ok = (bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (bw1 & s_ubm[1]) == s_ubm[1]);
+            } else {
+                const uint64_t *bmr = p.bm_tab + (size_t)bmi * p.w_bm;
+                ok = true;
+                for (int w = 0; w < p.w_bm; ++w) {
+                    const uint64_t u = s_ubm[w];
+                    if ((bmr[w] & u) != u) {
+                        ok = false;
+                        break;
+                    }
+                }
+            }
+        }
+        const float score = ok ? s_acc[i] + (xv - s_lse[i]) : -INFINITY;
+        const uint32_t f = (uint32_t)(m * V + v);
+        const bool defer = wq && ok;   // eq 8 still to test
+        if (ok && !defer && p.mask_words) mark(i, v);
+        emit(ok && !defer && score > -INFINITY, score, f, child);
+        if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
+
+        const uint64_t dm = __ballot(defer);
+        if (dm) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nl[par], (uint32_t)__popcll(dm));
+            base = __shfl(base, 0, 64) - (par ? nlb1 : nlb0);
+            if (defer) {
+                const uint32_t q = base + lanes_below(dm);
+                s_ls[par][q] = score;
+                s_lf[par][q] = f;
+                s_lc[par][q] = child;
+                s_lb[par][q] = bli;
+            }
+        }
+        __syncthreads();
+        const uint32_t tot = s_nl[par];
+        const int n_bl = (int)(tot - (par ? nlb1 : nlb0));
+        if (par) nlb1 = tot;
+        else nlb0 = tot;
+        if (n_bl == 0) continue;   // uniform
+
+        // eq 8 for the round's list (a failed entry's row id becomes -1)
+        int32_t *lb = s_lb[par];
+        bloom_list(lb, n_bl);
         __syncthreads();
         {   // the list's survivors (n_bl <= EXP_THREADS: one entry per thread)
             const bool in = tid < n_bl;
@@ -1268,6 +1336,9 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.wmax = tr.node_slice ? (a.V + 63) / 64 : 0;
     p.vec_logits = a.dtype == GR_BF16 && (a.V & 7) == 0 && ((uintptr_t)a.logits & 15) == 0;
     p.ent_bm = tr.entry_bitmask;
+    p.kw_off = tr.kway_offsets;
+    p.kw_bmi = tr.kway_bmi;
+    p.kw_bli = tr.kway_bli;
     auto al16 = [](const void *x) { return ((uintptr_t)x & 15) == 0; };
     p.vec_rows = (a.L & 3) == 0 && al16(a.tokens_in) && al16(a.tokens_out) && al16(a.table_in) &&
                  al16(a.table_out);
