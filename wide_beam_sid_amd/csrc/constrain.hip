@@ -111,6 +111,40 @@ __device__ __forceinline__ uint32_t key_flat(uint64_t k) { return 0xFFFFFFFFu - 
 // request is at most the full max (log-probabilities are <= 0), so the score
 // histogram bins hang below it.  The same rows and the same max (exact in
 // floating point) give expand and select the same bound.
+// The first chunk's loads of bound_part, issued early: the reduction
+// (bound_finish) runs after other loads, so they share a round trip.
+struct BoundLoads {
+    int32_t n4[4];
+    float a4[4];
+};
+__device__ __forceinline__ BoundLoads bound_load(const TailParams &p, int b) {
+    BoundLoads o;
+    const int32_t *nd = p.node_in + (size_t)b * p.M_in;
+    const float *ac = p.acc_in + (size_t)b * p.M_in;
+    const int nt = blockDim.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = (int)threadIdx.x + q * nt;
+        o.n4[q] = m < p.M_in ? nd[m] : -1;
+        o.a4[q] = m < p.M_in ? ac[m] : -INFINITY;
+    }
+    return o;
+}
+__device__ __forceinline__ float bound_finish(const TailParams &p, int b, const BoundLoads &f) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (f.n4[q] >= 0 && f.n4[q] < p.num_nodes) mx = fmaxf(mx, f.a4[q]);
+    const int32_t *nd = p.node_in + (size_t)b * p.M_in;
+    const float *ac = p.acc_in + (size_t)b * p.M_in;
+    const int nt = blockDim.x;
+    for (int m = (int)threadIdx.x + 4 * nt; m < p.M_in; m += nt) {   // rows past the first chunk
+        const int32_t n = nd[m];
+        if (n >= 0 && n < p.num_nodes) mx = fmaxf(mx, ac[m]);
+    }
+    return wave_max(mx);
+}
+
 __device__ __forceinline__ float bound_part(const TailParams &p, int b) {
     float mx = -INFINITY;
     const int32_t *nd = p.node_in + (size_t)b * p.M_in;
@@ -250,11 +284,11 @@ void k_expand(TailParams p) {
     __shared__ int s_nsl;
     __shared__ float s_ub[EXP_WAVES];
     __shared__ int s_nub;
-    __shared__ float s_ls[2][EXP_THREADS];         // round lists of entries awaiting eq 8:
-    __shared__ uint32_t s_lf[2][EXP_THREADS];      //   score, flat index m * V + v,
-    __shared__ int32_t s_lc[2][EXP_THREADS];       //   child node,
-    __shared__ int32_t s_lb[2][EXP_THREADS];       //   Bloom row (-1 once the test fails)
-    __shared__ uint32_t s_nl[2];                   // entries listed so far, per parity
+    __shared__ float s_ls[2][EXP_THREADS];         // the round's list of entries awaiting
+    __shared__ uint32_t s_lf[2][EXP_THREADS];      //   eq 8 (2 * EXP_THREADS): score, flat
+    __shared__ int32_t s_lc[2][EXP_THREADS];       //   index m * V + v, child node, Bloom
+    __shared__ int32_t s_lb[2][EXP_THREADS];       //   row (-1 once the test fails)
+    __shared__ uint32_t s_nl[2];                   // entries in the list
     __shared__ uint32_t s_kn;                      // k-way: partitions listed this sub-round
     __shared__ uint8_t s_kok[EXP_THREADS];         // k-way: entry kept (a partition passed)
 
@@ -284,10 +318,7 @@ void k_expand(TailParams p) {
         s_nl[1] = 0u;
         s_kn = 0u;
     }
-    {
-        const float ub = bound_part(p, b);
-        if (lane == 0) s_ub[wave] = ub;
-    }
+    const BoundLoads bl0 = bound_load(p, b);   // reduced just before the barrier
     if (p.wmax && wave == 1) {  // list the user's attribute bits (eq 5 columns)
         const uint64_t u = lane < p.w_bm ? p.user_bm[(size_t)b * p.w_bm + lane] : 0ull;
         const int n = __popcll(u);
@@ -347,58 +378,24 @@ void k_expand(TailParams p) {
         if (lane < nrows) s_nstart[lane + 1] = inc2;
         if (lane == 0) s_nstart[0] = 0;
     }
-    __syncthreads();
-    const float U = fmaxf(fmaxf(s_ub[0], s_ub[1]), fmaxf(s_ub[2], s_ub[3]));
-    // this workgroup's survivor segment: slots come from an LDS counter
-    uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
-    int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
-    uint16_t *sbin = p.sbin + ((size_t)b * gx + x) * p.seg_cap;
-    const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
-    const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
-
-    // A candidate that passed CD + TM with a finite score: its bin in the
-    // workgroup histogram and its (key, child) in the segment.  Called by
-    // whole wavefronts.
-    auto emit = [&](bool sel, float score, uint32_t f, int32_t ch) {
-        const int bin = score_bin(score, U);
-        if (sel) atomicAdd(&s_hist[bin], 1u);
-        const uint64_t bal = __ballot(sel);
-        if (bal) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
-            base = __shfl(base, 0, 64);
-            if (sel) {
-                const uint32_t idx = base + lanes_below(bal);
-                if (idx < (uint32_t)p.seg_cap) {
-                    skey[idx] = make_key(score, f);
-                    schild[idx] = ch;
-                    sbin[idx] = (uint16_t)bin;
-                }
-            }
-        }
-    };
-    auto mark = [&](int i, int v) {   // debug mask bit of row i, token v
-        atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
-    };
-
-    // lane l's location l: its probe positions, kept in registers
-    uint4 pr0[MAX_KP / 4];
-#pragma unroll
-    for (int q = 0; q < MAX_KP / 4; ++q) {
-        pr0[q] = make_uint4(0u, 0u, 0u, 0u);
-        if (q * 4 < kp && lane < p.n_loc && p.w_bl) pr0[q] = ((const uint4 *)(s_probe + lane * kp))[q];
-    }
-
-    // Full-vocabulary log-sum-exp of every row with candidates (eq 3 masks
+    // Full-vocabulary log-sum-exp of every live row (eq 3 masks
     // log-probabilities, so the normaliser runs over all V tokens): TPR
     // threads per row, each with a running (max, sum) over its share.
     {
         const int tpr = p.tpr, sh_tpr = p.log2_tpr;
         const int i = tid >> sh_tpr, part = tid & (tpr - 1);
         float m = -INFINITY, s = 0.0f;
-        const bool has = i < nrows && s_rstart[i + 1] > s_rstart[i];
+        // the row's node decides whether it is live; its logits are read
+        // while wavefront 0 is still resolving the rows' CSR ranges
+        bool has = false;
+        size_t rowoff = 0;
+        if (i < nrows) {
+            const int r = b * p.M_in + x + i * gx;
+            const int nd = p.node_in[r];
+            has = nd >= 0 && nd < p.num_nodes;
+            rowoff = (size_t)r * V;
+        }
         if (has) {
-            const size_t rowoff = (size_t)(b * p.M_in + s_rm[i]) * V;
             if (BF16 && p.vec_logits) {
                 // 8 logits per 16-byte load and up to 8 loads in flight per
                 // thread; then one max and one rescaled sum per batch
@@ -447,7 +444,52 @@ void k_expand(TailParams p) {
         }
         if (i < nrows && part == 0) s_lse[i] = has ? m + __logf(s) : 0.0f;
     }
+    {
+        const float ub = bound_finish(p, b, bl0);
+        if (lane == 0) s_ub[wave] = ub;
+    }
     __syncthreads();
+    const float U = fmaxf(fmaxf(s_ub[0], s_ub[1]), fmaxf(s_ub[2], s_ub[3]));
+    // this workgroup's survivor segment: slots come from an LDS counter
+    uint64_t *skey = p.skey + ((size_t)b * gx + x) * p.seg_cap;
+    int32_t *schild = p.schild + ((size_t)b * gx + x) * p.seg_cap;
+    uint16_t *sbin = p.sbin + ((size_t)b * gx + x) * p.seg_cap;
+    const int G = p.G, wq = p.w_bl, sh_wq = p.log2_wq;
+    const int row_dw = 2 * wq + 1;   // staged row stride in dwords (odd: spreads banks)
+
+    // A candidate that passed CD + TM with a finite score: its bin in the
+    // workgroup histogram and its (key, child) in the segment.  Called by
+    // whole wavefronts.
+    auto emit = [&](bool sel, float score, uint32_t f, int32_t ch) {
+        const int bin = score_bin(score, U);
+        if (sel) atomicAdd(&s_hist[bin], 1u);
+        const uint64_t bal = __ballot(sel);
+        if (bal) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
+            base = __shfl(base, 0, 64);
+            if (sel) {
+                const uint32_t idx = base + lanes_below(bal);
+                if (idx < (uint32_t)p.seg_cap) {
+                    skey[idx] = make_key(score, f);
+                    schild[idx] = ch;
+                    sbin[idx] = (uint16_t)bin;
+                }
+            }
+        }
+    };
+    auto mark = [&](int i, int v) {   // debug mask bit of row i, token v
+        atomicOr((unsigned long long *)&s_mask[i * p.mask_words + (v >> 6)], 1ull << (v & 63));
+    };
+
+    // lane l's location l: its probe positions, kept in registers
+    uint4 pr0[MAX_KP / 4];
+#pragma unroll
+    for (int q = 0; q < MAX_KP / 4; ++q) {
+        pr0[q] = make_uint4(0u, 0u, 0u, 0u);
+        if (q * 4 < kp && lane < p.n_loc && p.w_bl) pr0[q] = ((const uint4 *)(s_probe + lane * kp))[q];
+    }
+
 
     // eqs 5 and 8 for every child of a node with a bit-sliced block, one
     // wavefront per row.  Eq 5: AND of the columns of the user's attribute
@@ -698,53 +740,66 @@ void k_expand(TailParams p) {
         }
     };
 
-    // The entries of rows without a bit-sliced block: rounds of EXP_THREADS
-    // entries, one per thread (the round count is the same for every thread).  Entries that pass eq 5 and still need eq 8
-    // go to a round list; the list's Bloom tests are then shared by all
-    // wavefronts.  Lists and their counters alternate between rounds, so a
-    // round's list is never written while the previous one is read.
-    uint32_t nlb0 = 0u, nlb1 = 0u;   // list entries consumed, per parity
+    // The entries of rows without a bit-sliced block, one per thread per
+    // round (two with one-union matchers), the round count the same for
+    // every thread.
     const int n_ent = s_nstart[nrows];
-    for (int c0 = 0, round = 0; c0 < n_ent; c0 += EXP_THREADS, ++round) {
-        const int par = round & 1;
-        const int e = c0 + tid;
-        const bool valid = e < n_ent;
-        int i = 0;
-        if (valid) {  // row of entry e: the largest i with s_nstart[i] <= e
-            int lo = 0, hi = nrows;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_nstart[mid] <= e) lo = mid;
-                else hi = mid;
-            }
-            i = lo;
+    // entry e's row, CSR position, token, child and matcher ids / rows, in
+    // one round of loads
+    struct Ent {
+        bool valid;
+        int i, j, v, bmi, bli, child, m;
+        uint64_t bw0, bw1;
+    };
+    auto load_entry = [&](int e) {
+        Ent t{};
+        t.valid = e < n_ent;
+        t.bli = -1;
+        if (!t.valid) return t;
+        int lo = 0, hi = nrows;   // the largest i with s_nstart[i] <= e
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_nstart[mid] <= e) lo = mid;
+            else hi = mid;
         }
-        // One round of loads for the entry (token, child, matcher rows or
-        // ids), then the logit.
-        int j = 0, v = 0, bmi = 0, bli = -1, child = 0, m = 0;
-        uint64_t bw0 = 0ull, bw1 = 0ull;
-        if (valid) {
-            j = s_roff[i] + (e - s_nstart[i]);
-            v = p.tok[j];
-            child = p.child[j];
-            if (p.ent_bm) {
-                bw0 = p.ent_bm[(size_t)j * p.w_bm];
-                if (p.w_bm > 1) bw1 = p.ent_bm[(size_t)j * p.w_bm + 1];
-            } else {
-                bmi = p.bmi[j];
-            }
-            if (wq) bli = p.bli[j];
-            m = s_rm[i];
+        t.i = lo;
+        t.j = s_roff[lo] + (e - s_nstart[lo]);
+        t.v = p.tok[t.j];
+        t.child = p.child[t.j];
+        if (p.ent_bm) {
+            t.bw0 = p.ent_bm[(size_t)t.j * p.w_bm];
+            if (p.w_bm > 1) t.bw1 = p.ent_bm[(size_t)t.j * p.w_bm + 1];
+        } else {
+            t.bmi = p.bmi[t.j];
         }
-        if (p.kw_off) {
-            // k-way partitioned matchers (uniform branch): the entry is kept
-            // when one of its partitions passes eq 5 and, with a Bloom
-            // matcher, eq 8.  Sub-rounds: every entry still undecided offers
-            // its next partition that passes eq 5; the offered Bloom rows
-            // are tested together by all wavefronts.
-            const float xk = valid ? logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v) : 0.0f;
-            int cur = valid ? p.kw_off[j] : 0;
-            const int q1 = valid ? p.kw_off[j + 1] : 0;
+        if (wq) t.bli = p.bli[t.j];
+        t.m = s_rm[lo];
+        return t;
+    };
+    // eq 5: every user attribute bit present in the entry's row
+    auto bitmask_ok = [&](const Ent &t) {
+        if (p.ent_bm)
+            return (t.bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (t.bw1 & s_ubm[1]) == s_ubm[1]);
+        const uint64_t *bmr = p.bm_tab + (size_t)t.bmi * p.w_bm;
+        for (int w = 0; w < p.w_bm; ++w)
+            if ((bmr[w] & s_ubm[w]) != s_ubm[w]) return false;
+        return true;
+    };
+    auto logit_of = [&](const Ent &t) {
+        return t.valid ? logit_at<BF16>(p.logits, (size_t)(b * p.M_in + t.m) * V + t.v) : 0.0f;
+    };
+
+    if (p.kw_off) {
+        // k-way partitioned matchers: an entry is kept when one of its
+        // partitions passes eq 5 and, with a Bloom matcher, eq 8.
+        // Sub-rounds: every entry still undecided offers its next partition
+        // that passes eq 5; the offered Bloom rows are tested together by
+        // all wavefronts.
+        for (int c0 = 0; c0 < n_ent; c0 += EXP_THREADS) {
+            const Ent t = load_entry(c0 + tid);
+            const float xk = logit_of(t);
+            int cur = t.valid ? p.kw_off[t.j] : 0;
+            const int q1 = t.valid ? p.kw_off[t.j + 1] : 0;
             auto bm_pass = [&](int q) {
                 const uint64_t *r = p.bm_tab + (size_t)p.kw_bmi[q] * p.w_bm;
                 for (int w = 0; w < p.w_bm; ++w)
@@ -789,71 +844,69 @@ void k_expand(TailParams p) {
                     __syncthreads();
                 }
             }
-            const float sk = kept ? s_acc[i] + (xk - s_lse[i]) : -INFINITY;
-            if (kept && p.mask_words) mark(i, v);
-            emit(kept && sk > -INFINITY, sk, (uint32_t)(m * V + v), child);
-            continue;
+            const float sk = kept ? s_acc[t.i] + (xk - s_lse[t.i]) : -INFINITY;
+            if (kept && p.mask_words) mark(t.i, t.v);
+            emit(kept && sk > -INFINITY, sk, (uint32_t)(t.m * V + t.v), t.child);
         }
-        bool ok = false;
-        float xv = 0.0f;
-        if (valid) {
-            xv = logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
-            if (p.ent_bm) {
-                // eq 5: every user attribute bit present in the entry's row
-                ok = (bw0 & s_ubm[0]) == s_ubm[0] && (p.w_bm < 2 || (bw1 & s_ubm[1]) == s_ubm[1]);
-            } else {
-                const uint64_t *bmr = p.bm_tab + (size_t)bmi * p.w_bm;
-                ok = true;
-                for (int w = 0; w < p.w_bm; ++w) {
-                    const uint64_t u = s_ubm[w];
-                    if ((bmr[w] & u) != u) {
-                        ok = false;
-                        break;
+    } else {
+        // One-union matchers: two entries per thread per round, both
+        // entries' loads issued before either is used.  Entries that pass
+        // eq 5 and still need eq 8 go to the round's list (up to 2 *
+        // EXP_THREADS), whose Bloom rows all wavefronts test together.
+        float *Ls = &s_ls[0][0];
+        uint32_t *Lf = &s_lf[0][0];
+        int32_t *Lc = &s_lc[0][0], *Lb = &s_lb[0][0];
+        for (int c0 = 0; c0 < n_ent; c0 += 2 * EXP_THREADS) {
+            const Ent t0 = load_entry(c0 + tid), t1 = load_entry(c0 + EXP_THREADS + tid);
+            const float x0 = logit_of(t0), x1 = logit_of(t1);
+            const Ent *ts[2] = {&t0, &t1};
+            const float xs[2] = {x0, x1};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const Ent &t = *ts[u];
+                const bool ok = t.valid && bitmask_ok(t);
+                const float score = ok ? s_acc[t.i] + (xs[u] - s_lse[t.i]) : -INFINITY;
+                const uint32_t f = (uint32_t)(t.m * V + t.v);
+                const bool defer = wq && ok;   // eq 8 still to test
+                if (ok && !defer && p.mask_words) mark(t.i, t.v);
+                emit(ok && !defer && score > -INFINITY, score, f, t.child);
+                const uint64_t dm = __ballot(defer);
+                if (dm) {
+                    uint32_t base = 0;
+                    if (lane == 0) base = atomicAdd(&s_nl[0], (uint32_t)__popcll(dm));
+                    base = __shfl(base, 0, 64);
+                    if (defer) {
+                        const uint32_t q = base + lanes_below(dm);
+                        Ls[q] = score;
+                        Lf[q] = f;
+                        Lc[q] = t.child;
+                        Lb[q] = t.bli;
                     }
                 }
             }
-        }
-        const float score = ok ? s_acc[i] + (xv - s_lse[i]) : -INFINITY;
-        const uint32_t f = (uint32_t)(m * V + v);
-        const bool defer = wq && ok;   // eq 8 still to test
-        if (ok && !defer && p.mask_words) mark(i, v);
-        emit(ok && !defer && score > -INFINITY, score, f, child);
-        if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
-
-        const uint64_t dm = __ballot(defer);
-        if (dm) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_nl[par], (uint32_t)__popcll(dm));
-            base = __shfl(base, 0, 64) - (par ? nlb1 : nlb0);
-            if (defer) {
-                const uint32_t q = base + lanes_below(dm);
-                s_ls[par][q] = score;
-                s_lf[par][q] = f;
-                s_lc[par][q] = child;
-                s_lb[par][q] = bli;
+            if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
+            __syncthreads();
+            const int n_bl = (int)s_nl[0];
+            if (n_bl) {   // uniform
+                // eq 8 for the round's list (a failed entry's row id becomes -1)
+                bloom_list(Lb, n_bl);
+                __syncthreads();
+                if (tid == 0) s_nl[0] = 0u;   // every thread has read the count
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {   // the list's survivors, two per thread
+                    const int q = u * EXP_THREADS + tid;
+                    const bool in = q < n_bl;
+                    const bool okq = in && Lb[q] >= 0;
+                    const float sc = in ? Ls[q] : -INFINITY;
+                    const uint32_t fq = in ? Lf[q] : 0u;
+                    if (okq && p.mask_words) {
+                        const int mq = (int)(fq / (uint32_t)V);
+                        mark((mq - x) / gx, (int)(fq % (uint32_t)V));
+                    }
+                    emit(okq && sc > -INFINITY, sc, fq, in ? Lc[q] : 0);
+                }
             }
-        }
-        __syncthreads();
-        const uint32_t tot = s_nl[par];
-        const int n_bl = (int)(tot - (par ? nlb1 : nlb0));
-        if (par) nlb1 = tot;
-        else nlb0 = tot;
-        if (n_bl == 0) continue;   // uniform
-
-        // eq 8 for the round's list (a failed entry's row id becomes -1)
-        int32_t *lb = s_lb[par];
-        bloom_list(lb, n_bl);
-        __syncthreads();
-        {   // the list's survivors (n_bl <= EXP_THREADS: one entry per thread)
-            const bool in = tid < n_bl;
-            const bool okq = in && lb[tid] >= 0;
-            const float sc = in ? s_ls[par][tid] : -INFINITY;
-            const uint32_t fq = in ? s_lf[par][tid] : 0u;
-            if (okq && p.mask_words) {
-                const int mq = (int)(fq / (uint32_t)V);
-                mark((mq - x) / gx, (int)(fq % (uint32_t)V));
-            }
-            emit(okq && sc > -INFINITY, sc, fq, in ? s_lc[par][tid] : 0);
+            __syncthreads();   // the list is rewritten by the next round
         }
     }
 
