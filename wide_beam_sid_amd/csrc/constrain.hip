@@ -257,6 +257,85 @@ __device__ __forceinline__ bool bloom_row_test(const uint32_t *row, const uint4 
     return any;
 }
 
+// Bitonic sort of n2 (power of two) keys in LDS, descending, with payload.
+__device__ void bitonic_desc(uint64_t *key, int32_t *idx, int n2) {
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool desc = (i & size) == 0;
+                    const uint64_t a = key[i], c = key[j];
+                    if (desc ? (a < c) : (a > c)) {
+                        key[i] = c;
+                        key[j] = a;
+                        const int32_t t = idx[i];
+                        idx[i] = idx[j];
+                        idx[j] = t;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ int next_pow2(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+// Reorder writes of output slot sl (GRACE Section 3.3, Section 5.3): a live
+// slot takes the key's parent row, token, score and child node and copies
+// the parent's token and block-table rows (block ids only); a dead slot is
+// -1 / -inf throughout.
+__device__ __forceinline__ void write_slot(const TailParams &p, int b, size_t sl, bool live,
+                                           uint64_t key, int32_t child) {
+    const int V = p.V, L = p.L, t = p.t;
+    if (live) {
+        const uint32_t f = key_flat(key);
+        const int m = (int)(f / (uint32_t)V), v = (int)(f % (uint32_t)V);
+        const int parent = b * p.M_in + m;
+        p.parent_out[sl] = parent;
+        p.token_out[sl] = v;
+        p.node_out[sl] = child;
+        p.acc_out[sl] = key_score(key);
+        if (p.vec_rows) {   // rows of L int32 as 16-byte pieces
+            for (int l0 = 0; l0 < L; l0 += 4) {
+                int4 tk = make_int4(-1, -1, -1, -1), tb = tk;
+                if (p.tokens_out && l0 < t) tk = *(const int4 *)(p.tokens_in + (size_t)parent * L + l0);
+                if (p.table_out && l0 <= t) tb = *(const int4 *)(p.table_in + (size_t)parent * L + l0);
+                int *tkv = (int *)&tk, *tbv = (int *)&tb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int l = l0 + e;
+                    tkv[e] = l < t ? tkv[e] : (l == t ? v : -1);
+                    tbv[e] = l <= t ? tbv[e] : -1;
+                }
+                if (p.tokens_out) *(int4 *)(p.tokens_out + sl * L + l0) = tk;
+                if (p.table_out) *(int4 *)(p.table_out + sl * L + l0) = tb;
+            }
+        } else {
+            if (p.tokens_out)
+                for (int l = 0; l < L; ++l)
+                    p.tokens_out[sl * L + l] = l < t ? p.tokens_in[(size_t)parent * L + l] : (l == t ? v : -1);
+            if (p.table_out)
+                for (int l = 0; l < L; ++l)
+                    p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
+        }
+    } else {
+        p.parent_out[sl] = -1;
+        p.token_out[sl] = -1;
+        p.node_out[sl] = -1;
+        p.acc_out[sl] = -INFINITY;
+        if (p.tokens_out)
+            for (int l = 0; l < L; ++l) p.tokens_out[sl * L + l] = -1;
+        if (p.table_out)
+            for (int l = 0; l < L; ++l) p.table_out[sl * L + l] = -1;
+    }
+}
+
 // One workgroup = up to rows_wg beam rows of one request, taken with a stride
 // of gridDim.x (row m = blockIdx.x + i * gridDim.x) so that the live rows,
 // which sit at the front of a request after a top-k, spread over the grid.
@@ -946,35 +1025,6 @@ void k_expand(TailParams p) {
     }
 }
 
-// Bitonic sort of n2 (power of two) keys in LDS, descending, with payload.
-__device__ void bitonic_desc(uint64_t *key, int32_t *idx, int n2) {
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n2; i += blockDim.x) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool desc = (i & size) == 0;
-                    const uint64_t a = key[i], c = key[j];
-                    if (desc ? (a < c) : (a > c)) {
-                        key[i] = c;
-                        key[j] = a;
-                        const int32_t t = idx[i];
-                        idx[i] = idx[j];
-                        idx[j] = t;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-__device__ __forceinline__ int next_pow2(int n) {
-    int p = 1;
-    while (p < n) p <<= 1;
-    return p;
-}
-
 __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     __shared__ uint32_t s_seg[NBINS];     // bin starts, then (after the scatter) bin ends
     __shared__ uint64_t s_key[MAX_K];     // winners, grouped by bin
@@ -1259,67 +1309,25 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     // 4. Output.  A winner of a bin below the threshold takes slot
     //    (start of its bin) + (number of better keys in its bin); the
     //    threshold-bin winners are already in order.  Slots past n_sel are dead.
-    const int V = p.V, L = p.L, t = p.t;
+    const int V = p.V;
     for (int pos = tid; pos < k; pos += SEL_THREADS) {
-        const size_t base = (size_t)b * k;
         const uint64_t keyp = pos < n_sel ? s_key[pos] : 0ull;
         const uint32_t fp = key_flat(keyp);
         const uint32_t srcp = (uint32_t)s_src[pos];
         // a zero key or an out-of-range survivor (only with a workspace that
         // was not zero-filled) gives a dead slot instead of a wild read
-        if (keyp != 0ull && fp < (uint32_t)p.M_in * (uint32_t)V && srcp < (uint32_t)(gx * seg_cap)) {
-            const uint64_t key = keyp;
-            int slot = pos;
-            if (pos < below) {
-                const int bin = score_bin(key_score(key), U);
-                const int end = (int)s_seg[bin], start = bin ? (int)s_seg[bin - 1] : 0;
-                int r = 0;
-                for (int q = start; q < end; ++q) r += s_key[q] > key;
-                slot = start + r;
-            }
-            const size_t sl = base + slot;
-            const uint32_t f = key_flat(key);
-            const int m = (int)(f / (uint32_t)V), v = (int)(f % (uint32_t)V);
-            const int parent = b * p.M_in + m;
-            p.parent_out[sl] = parent;
-            p.token_out[sl] = v;
-            p.node_out[sl] = p.schild[(size_t)b * gx * seg_cap + srcp];
-            p.acc_out[sl] = key_score(key);
-            if (p.vec_rows) {   // rows of L int32 as 16-byte pieces
-                for (int l0 = 0; l0 < L; l0 += 4) {
-                    int4 tk = make_int4(-1, -1, -1, -1), tb = tk;
-                    if (p.tokens_out && l0 < t) tk = *(const int4 *)(p.tokens_in + (size_t)parent * L + l0);
-                    if (p.table_out && l0 <= t) tb = *(const int4 *)(p.table_in + (size_t)parent * L + l0);
-                    int *tkv = (int *)&tk, *tbv = (int *)&tb;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int l = l0 + e;
-                        tkv[e] = l < t ? tkv[e] : (l == t ? v : -1);
-                        tbv[e] = l <= t ? tbv[e] : -1;
-                    }
-                    if (p.tokens_out) *(int4 *)(p.tokens_out + sl * L + l0) = tk;
-                    if (p.table_out) *(int4 *)(p.table_out + sl * L + l0) = tb;
-                }
-            } else {
-                if (p.tokens_out)
-                    for (int l = 0; l < L; ++l)
-                        p.tokens_out[sl * L + l] =
-                            l < t ? p.tokens_in[(size_t)parent * L + l] : (l == t ? v : -1);
-                if (p.table_out)
-                    for (int l = 0; l < L; ++l)
-                        p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
-            }
-        } else {
-            const size_t sl = base + pos;
-            p.parent_out[sl] = -1;
-            p.token_out[sl] = -1;
-            p.node_out[sl] = -1;
-            p.acc_out[sl] = -INFINITY;
-            if (p.tokens_out)
-                for (int l = 0; l < L; ++l) p.tokens_out[sl * L + l] = -1;
-            if (p.table_out)
-                for (int l = 0; l < L; ++l) p.table_out[sl * L + l] = -1;
+        const bool live = keyp != 0ull && fp < (uint32_t)p.M_in * (uint32_t)V &&
+                          srcp < (uint32_t)(gx * seg_cap);
+        int slot = pos;
+        if (live && pos < below) {
+            const int bin = score_bin(key_score(keyp), U);
+            const int end = (int)s_seg[bin], start = bin ? (int)s_seg[bin - 1] : 0;
+            int r = 0;
+            for (int q = start; q < end; ++q) r += s_key[q] > keyp;
+            slot = start + r;
         }
+        write_slot(p, b, (size_t)b * k + slot, live, keyp,
+                   live ? p.schild[(size_t)b * gx * seg_cap + srcp] : -1);
     }
 }
 
