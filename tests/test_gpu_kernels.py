@@ -151,6 +151,13 @@ SELF_CASES = [
     (1000, 4, 64, 4, 1, "bf16"),
     (301, 16, 128, 3, 2, "bf16"),
     (130, 8, 64, 4, 3, "bf16"),
+    # 16 lanes per row (16 rows per workgroup), ragged
+    (29, 2, 64, 4, 2, "bf16"),
+    # 24 pieces per row on 32 lanes (8 lanes idle), ragged
+    (45, 3, 64, 4, 3, "bf16"),
+    # heads narrower than 16 bytes: 8-byte pieces
+    (19, 4, 4, 3, 2, "bf16"),
+    (11, 3, 2, 3, 2, "f32"),
 ]
 
 

@@ -322,10 +322,10 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
 
 // Cross- and self-attention of one decode step in one launch (they are
 // independent): the first n_cross workgroups take the cross-attention tiles
-// (x fastest, then head, then request), the rest take four self-attention
-// rows each.  Saves a launch and lets the MFMA-bound tiles and the
+// (x fastest, then head, then request), the rest take the self-attention
+// rows (4 to 16 per workgroup, by row width).  Saves a launch and lets the MFMA-bound tiles and the
 // gather-bound rows share the machine.
-template <int D, int RB, int NCH>
+template <int D, int RB, int LPR, int NCH>
 __global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ K,
                                                       const uint16_t *__restrict__ Vv,
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict
         const JointArgs nj{};
         cross_rows<D, RB, false>(q, K, Vv, out, M, H, T, scale_log2, nj, bx, rest % H, rest / H);
     } else {
-        self_attn_rows<true, NCH>(sp, blk - n_cross);
+        self_attn_rows<true, 16, LPR, NCH>(sp, blk - n_cross);
     }
 }
 
@@ -501,8 +501,8 @@ hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx
     const int R = B * M;
     const SelfParams sp = self_params(q, k_new, v_new, k_pool, v_pool, pool_blocks, table,
                                       fresh_base, R, t, L, H, d, dt, self_out);
-    const int nch = self_chunks(sp, dt == GR_BF16);
-    if (dt != GR_BF16 || nch > 4) {   // two launches
+    const SelfLayout ly = self_layout(sp, dt == GR_BF16);
+    if (dt != GR_BF16 || sp.CB != 16 || ly.nch > 4) {   // two launches
         hipError_t e = launch_cross_attn(qx, k_ctx, v_ctx, cross_out, B, M, H, T, d, dt, s);
         if (e != hipSuccess) return e;
         return launch_self_attn(q, k_new, v_new, k_pool, v_pool, pool_blocks, table, fresh_base,
@@ -516,18 +516,17 @@ hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx
     const int rows = big ? 128 : 64;
     const int gxc = (M + rows - 1) / rows;
     const int n_cross = gxc * H * B;
-    const dim3 grid(n_cross + (R + 3) / 4);
+    const int srows = 4 * (64 / ly.lpr);
+    const dim3 grid(n_cross + (R + srows - 1) / srows);
+#define GR_PAIR_K(DD, RBB, LL, NN)                                                              \
+    k_attn_pair<DD, RBB, LL, NN><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc, n_cross, sp)
 #define GR_PAIR(DD, RBB)                                                                        \
     {                                                                                           \
-        if (nch <= 1)                                                                           \
-            k_attn_pair<DD, RBB, 1><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
-                                                         n_cross, sp);                          \
-        else if (nch <= 2)                                                                      \
-            k_attn_pair<DD, RBB, 2><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
-                                                         n_cross, sp);                          \
-        else                                                                                    \
-            k_attn_pair<DD, RBB, 4><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc,     \
-                                                         n_cross, sp);                          \
+        if (ly.lpr == 16) GR_PAIR_K(DD, RBB, 16, 1);                                            \
+        else if (ly.lpr == 32) GR_PAIR_K(DD, RBB, 32, 1);                                       \
+        else if (ly.nch <= 1) GR_PAIR_K(DD, RBB, 64, 1);                                        \
+        else if (ly.nch <= 2) GR_PAIR_K(DD, RBB, 64, 2);                                        \
+        else GR_PAIR_K(DD, RBB, 64, 4);                                                         \
     }
     if (d == 32) {
         if (big) GR_PAIR(32, 2) else GR_PAIR(32, 1)
@@ -537,6 +536,7 @@ hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx
         GR_PAIR(128, 1)
     }
 #undef GR_PAIR
+#undef GR_PAIR_K
     return hipGetLastError();
 }
 

@@ -9,11 +9,11 @@
 // (K2) makes the same choice of plain FMA over matrix units for such short,
 // gathered sequences.
 //
-// One wavefront per beam row.  A row's H*d_h elements are spread over the 64
-// lanes in 8-byte chunks (4 bf16 or 2 fp32 per lane per chunk), so every load
-// and store of q, k, v, out and of a gathered pool block is one fully
-// coalesced wavefront access; the d_h/VEC lanes of a head reduce their dot
-// products with xor shuffles.  The prefix block ids are read in one load,
+// A beam row's H*d_h elements are spread over 16, 32 or 64 lanes in 16-byte
+// pieces (8 bf16 or 4 fp32 per lane; 8-byte pieces when a head is narrower
+// than 16 bytes), so a wavefront holds one to four rows and every load and
+// store of q, k, v, out and of a gathered pool block is a coalesced access;
+// the lanes of a head reduce their dot products with xor shuffles.  The prefix block ids are read in one load,
 // the blocks' K/V are gathered in batches with all loads of a batch in
 // flight, and positions are consumed with an online softmax.
 #include "self_attn_body.h"
@@ -21,22 +21,34 @@
 namespace gr {
 namespace {
 
-template <bool BF16, int NCH>
+template <bool BF16, int CB, int LPR, int NCH>
 __global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
-    self_attn_rows<BF16, NCH>(p, blockIdx.x);
+    self_attn_rows<BF16, CB, LPR, NCH>(p, blockIdx.x);
+}
+
+template <bool BF16, int CB, int LPR, int NCH>
+hipError_t go(const SelfParams &p, hipStream_t s) {
+    constexpr int rows = self_rows_wg<LPR>();
+    k_self_attn<BF16, CB, LPR, NCH><<<(p.R + rows - 1) / rows, 256, 0, s>>>(p);
+    return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t dispatch(const SelfParams &p, hipStream_t s) {
-    constexpr int VEC = Chunk<BF16>::VEC;
-    const int nch = (p.E / VEC + 63) / 64;
-    dim3 grid((p.R + 3) / 4);
-    if (nch <= 1) k_self_attn<BF16, 1><<<grid, 256, 0, s>>>(p);
-    else if (nch <= 2) k_self_attn<BF16, 2><<<grid, 256, 0, s>>>(p);
-    else if (nch <= 4) k_self_attn<BF16, 4><<<grid, 256, 0, s>>>(p);
-    else if (nch <= 8) k_self_attn<BF16, 8><<<grid, 256, 0, s>>>(p);
-    else k_self_attn<BF16, 16><<<grid, 256, 0, s>>>(p);
-    return hipGetLastError();
+    const SelfLayout ly = self_layout(p, BF16);
+    if (p.CB == 8) {
+        if (ly.nch <= 1) return go<BF16, 8, 64, 1>(p, s);
+        if (ly.nch <= 2) return go<BF16, 8, 64, 2>(p, s);
+        if (ly.nch <= 4) return go<BF16, 8, 64, 4>(p, s);
+        if (ly.nch <= 8) return go<BF16, 8, 64, 8>(p, s);
+        return go<BF16, 8, 64, 16>(p, s);
+    }
+    if (ly.lpr == 16) return go<BF16, 16, 16, 1>(p, s);
+    if (ly.lpr == 32) return go<BF16, 16, 32, 1>(p, s);
+    if (ly.nch <= 1) return go<BF16, 16, 64, 1>(p, s);
+    if (ly.nch <= 2) return go<BF16, 16, 64, 2>(p, s);
+    if (ly.nch <= 4) return go<BF16, 16, 64, 4>(p, s);
+    return go<BF16, 16, 64, 8>(p, s);
 }
 
 }  // namespace

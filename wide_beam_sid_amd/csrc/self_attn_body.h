@@ -21,62 +21,112 @@ struct SelfParams {
     int32_t *table;
     void *out;
     int64_t fresh_base, pool_blocks;
-    int R, t, L, H, d, E, G;
+    int R, t, L, H, d, E, G, CB;
     float scale;
 };
 
-template <bool BF16>
+// CB-byte pieces of a row: 4 or 8 bf16, 2 or 4 fp32.
+template <bool BF16, int CB>
 struct Chunk;
 template <>
-struct Chunk<true> {  // 4 x bf16 in 8 bytes
+struct Chunk<true, 8> {
     static constexpr int VEC = 4;
-    __device__ static void unpack(uint2 u, float *f) {
+    using W = uint2;
+    __device__ static W zero() { return make_uint2(0u, 0u); }
+    __device__ static void unpack(W u, float *f) {
         f[0] = __uint_as_float(u.x << 16);
         f[1] = __uint_as_float(u.x & 0xFFFF0000u);
         f[2] = __uint_as_float(u.y << 16);
         f[3] = __uint_as_float(u.y & 0xFFFF0000u);
     }
-    __device__ static uint2 pack(const float *f) {
+    __device__ static W pack(const float *f) {
         return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
     }
 };
 template <>
-struct Chunk<false> {  // 2 x fp32 in 8 bytes
+struct Chunk<false, 8> {
     static constexpr int VEC = 2;
-    __device__ static void unpack(uint2 u, float *f) {
+    using W = uint2;
+    __device__ static W zero() { return make_uint2(0u, 0u); }
+    __device__ static void unpack(W u, float *f) {
         f[0] = __uint_as_float(u.x);
         f[1] = __uint_as_float(u.y);
     }
-    __device__ static uint2 pack(const float *f) {
+    __device__ static W pack(const float *f) {
         return make_uint2(__float_as_uint(f[0]), __float_as_uint(f[1]));
     }
 };
+template <>
+struct Chunk<true, 16> {
+    static constexpr int VEC = 8;
+    using W = uint4;
+    __device__ static W zero() { return make_uint4(0u, 0u, 0u, 0u); }
+    __device__ static void unpack(W u, float *f) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(w[e] << 16);
+            f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+    }
+    __device__ static W pack(const float *f) {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+};
+template <>
+struct Chunk<false, 16> {
+    static constexpr int VEC = 4;
+    using W = uint4;
+    __device__ static W zero() { return make_uint4(0u, 0u, 0u, 0u); }
+    __device__ static void unpack(W u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+    }
+    __device__ static W pack(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+};
 
-// Rows blk * 4 .. blk * 4 + 3, one per wavefront of a 256-thread workgroup.
-template <bool BF16, int NCH>
+// Beam rows of one workgroup (256 threads): LPR lanes per row, so 64 / LPR
+// rows per wavefront.
+template <int LPR>
+constexpr int self_rows_wg() {
+    return 4 * (64 / LPR);
+}
+
+// Rows blk * self_rows_wg<LPR>() onwards.  A row's H*d_h elements are spread
+// over LPR lanes in CB-byte pieces, NCH pieces per lane (NCH > 1 only with
+// LPR = 64), so every load and store of a row is one coalesced access.
+template <bool BF16, int CB, int LPR, int NCH>
 __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
-    using C = Chunk<BF16>;
+    using C = Chunk<BF16, CB>;
+    using W = typename C::W;
     constexpr int VEC = C::VEC;
     constexpr int JB = NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1);   // prefix blocks per load batch
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int i = blk * 4 + wave;
-    if (i >= p.R) return;
-    const int E2 = p.E / VEC;  // 8-byte chunks per row
+    const int lr = lane & (LPR - 1);
+    const int i = blk * self_rows_wg<LPR>() + wave * (64 / LPR) + lane / LPR;
+    if (i >= p.R) return;   // whole rows leave together
+    const int E2 = p.E / VEC;  // pieces per row
     const int64_t f = p.fresh_base + i;
-    const uint2 *q = (const uint2 *)p.q + (size_t)i * E2;
-    const uint2 *kn = (const uint2 *)p.k_new + (size_t)i * E2;
-    const uint2 *vn = (const uint2 *)p.v_new + (size_t)i * E2;
-    uint2 *kp = (uint2 *)p.k_pool;
-    uint2 *vp = (uint2 *)p.v_pool;
+    const W *q = (const W *)p.q + (size_t)i * E2;
+    const W *kn = (const W *)p.k_new + (size_t)i * E2;
+    const W *vn = (const W *)p.v_new + (size_t)i * E2;
+    W *kp = (W *)p.k_pool;
+    W *vp = (W *)p.v_pool;
 
     float qf[NCH][VEC], kc[NCH][VEC], vc[NCH][VEC];
     float o[NCH][VEC], mrun[NCH], lrun[NCH];
     bool act[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int e = c * 64 + lane;
+        const int e = c * LPR + lr;
         act[c] = e < E2;
-        uint2 uq = make_uint2(0, 0), uk = uq, uv = uq;
+        W uq = C::zero(), uk = uq, uv = uq;
         if (act[c]) {
             uq = q[e];
             uk = kn[e];
@@ -92,36 +142,40 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
 #pragma unroll
         for (int x = 0; x < VEC; ++x) o[c][x] = 0.0f;
     }
-    // The row's prefix block ids, lane j holding position j (L <= 64).
-    const int32_t tb = lane < p.t ? p.table[(size_t)i * p.L + lane] : -1;
-    if (lane == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
+    if (lr == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
 
-    // Prefix positions in batches of JB: every block load of a batch is
-    // issued before the first dot product, then the current token.
+    // Prefix positions in batches of JB: the batch's block ids (one load,
+    // the same address for the row's lanes), then every block load of the
+    // batch before the first dot product; position t is the current token.
     for (int j0 = 0; j0 <= p.t; j0 += JB) {
-        uint2 kr[JB][NCH], vr[JB][NCH];
+        int32_t bid[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            bid[jj] = j < p.t ? p.table[(size_t)i * p.L + j] : -1;
+        }
+        W kr[JB][NCH], vr[JB][NCH];
         bool use[JB];
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             const int j = j0 + jj;
-            const int32_t blk = __builtin_amdgcn_readlane(tb, j < 64 ? j : 0);
-            // a dead row's missing past is skipped; position t is the current token
-            use[jj] = j < p.t && blk >= 0 && blk < p.pool_blocks;
+            // a dead row's missing past is skipped
+            use[jj] = j < p.t && bid[jj] >= 0 && bid[jj] < p.pool_blocks;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const int e = c * 64 + lane;
-                kr[jj][c] = vr[jj][c] = make_uint2(0, 0);
+                const int e = c * LPR + lr;
+                kr[jj][c] = vr[jj][c] = C::zero();
                 if (use[jj] && act[c]) {
-                    kr[jj][c] = kp[(size_t)blk * E2 + e];
-                    vr[jj][c] = vp[(size_t)blk * E2 + e];
+                    kr[jj][c] = kp[(size_t)bid[jj] * E2 + e];
+                    vr[jj][c] = vp[(size_t)bid[jj] * E2 + e];
                 }
             }
         }
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             const int j = j0 + jj;
-            if (j > p.t) break;                  // uniform
-            if (j < p.t && !use[jj]) continue;   // uniform
+            if (j > p.t) break;                    // uniform
+            const bool skip = j < p.t && !use[jj];   // the same for a row's lanes
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 float kj[VEC], vj[VEC];
@@ -138,7 +192,9 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
                 float dot = 0.0f;
 #pragma unroll
                 for (int x = 0; x < VEC; ++x) dot += qf[c][x] * kj[x];
+                // the G lanes of a head sit in one aligned group of the row
                 for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
+                if (skip) continue;
                 const float sc = dot * p.scale;
                 const float mn = fmaxf(mrun[c], sc);
                 const float alpha = __expf(mrun[c] - mn);
@@ -150,10 +206,10 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
             }
         }
     }
-    uint2 *out = (uint2 *)p.out + (size_t)i * E2;
+    W *out = (W *)p.out + (size_t)i * E2;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int e = c * 64 + lane;
+        const int e = c * LPR + lr;
         if (!act[c]) continue;
         const float inv = 1.0f / lrun[c];
         float r[VEC];
@@ -184,13 +240,23 @@ inline SelfParams self_params(const void *q, const void *k_new, const void *v_ne
     p.d = d;
     p.E = H * d;
     p.scale = 1.0f / sqrtf((float)d);
-    p.G = dt == GR_BF16 ? d / 4 : d / 2;   // lanes holding one head
+    // 16-byte pieces when a head fills whole ones, else 8-byte pieces
+    const int es = dt == GR_BF16 ? 2 : 4;
+    p.CB = (d * es) % 16 == 0 ? 16 : 8;
+    p.G = d * es / p.CB;   // lanes holding one head
     return p;
 }
 
-// 8-byte chunks of a row (4 bf16 or 2 fp32) per lane, in multiples of 64.
-inline int self_chunks(const SelfParams &p, bool bf16) {
-    return (p.E / (bf16 ? 4 : 2) + 63) / 64;
+// Lanes per row (16, 32 or 64) and pieces per lane of the layout above.
+struct SelfLayout {
+    int lpr, nch;
+};
+inline SelfLayout self_layout(const SelfParams &p, bool bf16) {
+    const int vec = p.CB / (bf16 ? 2 : 4);
+    const int e2 = p.E / vec;
+    if (p.CB == 16 && e2 <= 16) return {16, 1};
+    if (p.CB == 16 && e2 <= 32) return {32, 1};
+    return {64, (e2 + 63) / 64};
 }
 
 }  // namespace
