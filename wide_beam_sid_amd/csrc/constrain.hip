@@ -1172,21 +1172,37 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
                 bv[u] = oo < n_oct ? *(const uint4 *)(bins + src[u])
                                    : make_uint4(~0u, ~0u, ~0u, ~0u);
             }
+            // bit 8u + e: survivor src[u] + e is a candidate; one LDS atomic
+            // per wavefront reserves the wavefront's list positions
+            uint32_t msk = 0u;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t wv[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int bn = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                    const bool in = src[u] != 0xFFFFFFFFu && bn <= thr;
-                    const uint64_t bal = __ballot(in);
-                    if (bal) {
-                        uint32_t base = 0;
-                        if (lane == 0) base = atomicAdd(&s_ncl, (uint32_t)__popcll(bal));
-                        base = __shfl(base, 0, 64);
-                        const uint32_t ci = base + lanes_below(bal);
-                        if (in && ci < CAND_CAP) s_cand[ci] = src[u] + e;
-                    }
+                    if (src[u] != 0xFFFFFFFFu && bn <= thr) msk |= 1u << (8 * u + e);
+                }
+            }
+            const uint32_t nmine = (uint32_t)__popc(msk);
+            uint32_t inc = nmine;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            uint32_t base = 0;
+            if (lane == 63 && inc) base = atomicAdd(&s_ncl, inc);
+            base = __shfl(base, 63, 64);
+            uint32_t ci = base + inc - nmine;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t mm = (msk >> (8 * u)) & 0xFFu;
+                while (mm) {
+                    const int e = __ffs(mm) - 1;
+                    mm &= mm - 1u;
+                    if (ci < CAND_CAP) s_cand[ci] = src[u] + e;
+                    ++ci;
                 }
             }
         }
