@@ -280,6 +280,17 @@ __device__ void bitonic_desc(uint64_t *key, int32_t *idx, int n2) {
     }
 }
 
+// Number of keys in key[lo .. hi) greater than x, four LDS reads in flight.
+__device__ __forceinline__ int count_above(const uint64_t *key, int lo, int hi, uint64_t x) {
+    int r = 0, q = lo;
+    for (; q + 4 <= hi; q += 4) {
+        const uint64_t a0 = key[q], a1 = key[q + 1], a2 = key[q + 2], a3 = key[q + 3];
+        r += (int)(a0 > x) + (int)(a1 > x) + (int)(a2 > x) + (int)(a3 > x);
+    }
+    for (; q < hi; ++q) r += key[q] > x;
+    return r;
+}
+
 __device__ __forceinline__ int next_pow2(int n) {
     int p = 1;
     while (p < n) p <<= 1;
@@ -363,10 +374,9 @@ void k_expand(TailParams p) {
     __shared__ int s_nsl;
     __shared__ float s_ub[EXP_WAVES];
     __shared__ int s_nub;
-    __shared__ float s_ls[2][EXP_THREADS];         // the round's list of entries awaiting
-    __shared__ uint32_t s_lf[2][EXP_THREADS];      //   eq 8 (2 * EXP_THREADS): score, flat
-    __shared__ int32_t s_lc[2][EXP_THREADS];       //   index m * V + v, child node, Bloom
-    __shared__ int32_t s_lb[2][EXP_THREADS];       //   row (-1 once the test fails)
+    __shared__ int32_t s_lb[2 * EXP_THREADS];      // the round's Bloom rows awaiting eq 8
+                                                   //   (-1 once the test fails)
+    __shared__ uint32_t s_lf[EXP_THREADS];         // k-way: the thread that listed a row
     __shared__ uint32_t s_nl[2];                   // entries in the list
     __shared__ uint32_t s_kn;                      // k-way: partitions listed this sub-round
     __shared__ uint8_t s_kok[EXP_THREADS];         // k-way: entry kept (a partition passed)
@@ -890,7 +900,7 @@ void k_expand(TailParams p) {
                 while (!kept && cur < q1) kept = bm_pass(cur++);
             } else {
                 s_kok[tid] = 0;
-                int32_t *lb = s_lb[0];
+                int32_t *lb = s_lb;
                 for (;;) {   // the same number of sub-rounds for every thread
                     int32_t blr = -1;
                     while (!kept && cur < q1) {
@@ -908,7 +918,7 @@ void k_expand(TailParams p) {
                         if (blr >= 0) {
                             const uint32_t qi = base + lanes_below(dm);
                             lb[qi] = blr;
-                            s_lf[0][qi] = (uint32_t)tid;
+                            s_lf[qi] = (uint32_t)tid;
                         }
                     }
                     __syncthreads();
@@ -916,7 +926,7 @@ void k_expand(TailParams p) {
                     if (n_k == 0) break;   // uniform
                     bloom_list(lb, n_k);
                     __syncthreads();
-                    if (tid < n_k && lb[tid] >= 0) s_kok[s_lf[0][tid]] = 1;
+                    if (tid < n_k && lb[tid] >= 0) s_kok[s_lf[tid]] = 1;
                     __syncthreads();
                     kept = kept || s_kok[tid] != 0;
                     if (tid == 0) s_kn = 0u;
@@ -930,36 +940,35 @@ void k_expand(TailParams p) {
     } else {
         // One-union matchers: two entries per thread per round, both
         // entries' loads issued before either is used.  Entries that pass
-        // eq 5 and still need eq 8 go to the round's list (up to 2 *
-        // EXP_THREADS), whose Bloom rows all wavefronts test together.
-        float *Ls = &s_ls[0][0];
-        uint32_t *Lf = &s_lf[0][0];
-        int32_t *Lc = &s_lc[0][0], *Lb = &s_lb[0][0];
+        // eq 5 put their Bloom row on the round's list (up to 2 *
+        // EXP_THREADS), which all wavefronts test together (eq 8); the
+        // owner then emits its entries that passed.  The scores are not
+        // needed before that, so the logit gathers overlap the Bloom loads.
+        int32_t *Lb = s_lb;
         for (int c0 = 0; c0 < n_ent; c0 += 2 * EXP_THREADS) {
             const Ent t0 = load_entry(c0 + tid), t1 = load_entry(c0 + EXP_THREADS + tid);
             const float x0 = logit_of(t0), x1 = logit_of(t1);
             const Ent *ts[2] = {&t0, &t1};
             const float xs[2] = {x0, x1};
+            int qs[2] = {-1, -1};   // the entry's place in the list
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const Ent &t = *ts[u];
                 const bool ok = t.valid && bitmask_ok(t);
-                const float score = ok ? s_acc[t.i] + (xs[u] - s_lse[t.i]) : -INFINITY;
-                const uint32_t f = (uint32_t)(t.m * V + t.v);
-                const bool defer = wq && ok;   // eq 8 still to test
-                if (ok && !defer && p.mask_words) mark(t.i, t.v);
-                emit(ok && !defer && score > -INFINITY, score, f, t.child);
-                const uint64_t dm = __ballot(defer);
+                if (!wq) {   // bitmask-only matcher: decided now
+                    const float score = ok ? s_acc[t.i] + (xs[u] - s_lse[t.i]) : -INFINITY;
+                    if (ok && p.mask_words) mark(t.i, t.v);
+                    emit(ok && score > -INFINITY, score, (uint32_t)(t.m * V + t.v), t.child);
+                    continue;
+                }
+                const uint64_t dm = __ballot(ok);
                 if (dm) {
                     uint32_t base = 0;
                     if (lane == 0) base = atomicAdd(&s_nl[0], (uint32_t)__popcll(dm));
                     base = __shfl(base, 0, 64);
-                    if (defer) {
-                        const uint32_t q = base + lanes_below(dm);
-                        Ls[q] = score;
-                        Lf[q] = f;
-                        Lc[q] = t.child;
-                        Lb[q] = t.bli;
+                    if (ok) {
+                        qs[u] = (int)(base + lanes_below(dm));
+                        Lb[qs[u]] = t.bli;
                     }
                 }
             }
@@ -971,19 +980,14 @@ void k_expand(TailParams p) {
                 bloom_list(Lb, n_bl);
                 __syncthreads();
                 if (tid == 0) s_nl[0] = 0u;   // every thread has read the count
+            }
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {   // the list's survivors, two per thread
-                    const int q = u * EXP_THREADS + tid;
-                    const bool in = q < n_bl;
-                    const bool okq = in && Lb[q] >= 0;
-                    const float sc = in ? Ls[q] : -INFINITY;
-                    const uint32_t fq = in ? Lf[q] : 0u;
-                    if (okq && p.mask_words) {
-                        const int mq = (int)(fq / (uint32_t)V);
-                        mark((mq - x) / gx, (int)(fq % (uint32_t)V));
-                    }
-                    emit(okq && sc > -INFINITY, sc, fq, in ? Lc[q] : 0);
-                }
+            for (int u = 0; u < 2; ++u) {
+                const Ent &t = *ts[u];
+                const bool kept = qs[u] >= 0 && Lb[qs[u]] >= 0;
+                const float score = kept ? s_acc[t.i] + (xs[u] - s_lse[t.i]) : -INFINITY;
+                if (kept && p.mask_words) mark(t.i, t.v);
+                emit(kept && score > -INFINITY, score, (uint32_t)(t.m * V + t.v), t.child);
             }
             __syncthreads();   // the list is rewritten by the next round
         }
@@ -1298,8 +1302,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             // rank by counting: keys are distinct (the flat index is part of it)
             for (int q = tid; q < nb; q += SEL_THREADS) {
                 const uint64_t kq = s_bkey[q];
-                int r = 0;
-                for (int o = 0; o < nb; ++o) r += s_bkey[o] > kq;
+                const int r = count_above(s_bkey, 0, nb, kq);
                 if (r < need) {
                     s_key[below + r] = kq;
                     s_src[below + r] = s_bsrc[q];
@@ -1338,9 +1341,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         if (live && pos < below) {
             const int bin = score_bin(key_score(keyp), U);
             const int end = (int)s_seg[bin], start = bin ? (int)s_seg[bin - 1] : 0;
-            int r = 0;
-            for (int q = start; q < end; ++q) r += s_key[q] > keyp;
-            slot = start + r;
+            slot = start + count_above(s_key, start, end, keyp);
         }
         write_slot(p, b, (size_t)b * k + slot, live, keyp,
                    live ? p.schild[(size_t)b * gx * seg_cap + srcp] : -1);
