@@ -39,6 +39,7 @@ constexpr int EXP_THREADS = 64 * EXP_WAVES;
 constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 4096 bits)
 constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
 constexpr int MAX_KP = 8;             // probes per location held in registers (more: LDS)
+constexpr int LG_BYTES = 8192;        // bf16 logit rows an expand workgroup keeps in LDS
 constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
 constexpr int BND_CAP = 2048;         // threshold-bin entries buffered in LDS
@@ -89,6 +90,7 @@ struct TailParams {
     const uint64_t *ent_bm;   // entry-ordered bitmask rows (null: gather through bmi)
     int vec_rows;             // token / block-table rows movable as 16-byte pieces
     const int32_t *kw_off, *kw_bmi, *kw_bli;   // k-way partitions (null: one union per entry)
+    int lds_lg;         // the rows' bf16 logits are kept in LDS by the log-sum-exp pass
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -389,7 +391,8 @@ void k_expand(TailParams p) {
     const int nprobe = p.w_bl ? p.n_loc * kp : 0;
     uint64_t *s_mask = s_dyn;
     uint64_t *s_pass = s_dyn + (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1);
-    uint32_t *s_probe = (uint32_t *)(s_pass + (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1));
+    uint16_t *s_lg = (uint16_t *)(s_pass + (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1));
+    uint32_t *s_probe = (uint32_t *)(s_lg + (p.lds_lg ? (size_t)p.rows_wg * V : 0));
     int16_t *s_ubit = (int16_t *)(s_probe + nprobe);   // positions of the user's bitmask bits
     uint32_t *s_stage = s_probe + nprobe + (p.wmax ? 32 * p.w_bm : 0) + wave * p.stage_dw;
 
@@ -497,6 +500,12 @@ void k_expand(TailParams p) {
                         const int c = c0 + q * tpr;
                         u[q] = c < nv ? x8[c] : make_uint4(0u, 0u, 0u, 0u);
                     }
+                    if (p.lds_lg)   // kept for the candidates' scores
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int c = c0 + q * tpr;
+                            if (c < nv) *(uint4 *)(s_lg + (size_t)i * V + c * 8) = u[q];
+                        }
                     float mx = m;
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
@@ -579,6 +588,13 @@ void k_expand(TailParams p) {
         if (q * 4 < kp && lane < p.n_loc && p.w_bl) pr0[q] = ((const uint4 *)(s_probe + lane * kp))[q];
     }
 
+
+    // logit of token v of the workgroup's row i (beam m): from LDS when the
+    // log-sum-exp pass kept the rows there, else from memory
+    auto row_logit = [&](int i, int m, int v) -> float {
+        if (p.lds_lg) return bf16_to_f32(s_lg[(size_t)i * V + v]);
+        return logit_at<BF16>(p.logits, (size_t)(b * p.M_in + m) * V + v);
+    };
 
     // eqs 5 and 8 for every child of a node with a bit-sliced block, one
     // wavefront per row.  Eq 5: AND of the columns of the user's attribute
@@ -716,7 +732,6 @@ void k_expand(TailParams p) {
             // per chunk and up to 4 chunks of loads in flight.
             const int off0 = s_roff[i], m = s_rm[i];
             const float acc = s_acc[i], lse = s_lse[i];
-            const size_t lrow = (size_t)(b * p.M_in + m) * V;
             const uint64_t *pw = s_pass + (size_t)i * p.wmax;
             for (int u0 = 0; u0 < wc; u0 += 4) {
                 int tk[4], ch[4];
@@ -734,7 +749,7 @@ void k_expand(TailParams p) {
                 }
                 float xv[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xv[q] = okc[q] ? logit_at<BF16>(p.logits, lrow + tk[q]) : 0.0f;
+                for (int q = 0; q < 4; ++q) xv[q] = okc[q] ? row_logit(i, m, tk[q]) : 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (u0 + q >= wc) break;   // uniform
@@ -875,7 +890,7 @@ void k_expand(TailParams p) {
         return true;
     };
     auto logit_of = [&](const Ent &t) {
-        return t.valid ? logit_at<BF16>(p.logits, (size_t)(b * p.M_in + t.m) * V + t.v) : 0.0f;
+        return t.valid ? row_logit(t.i, t.m, t.v) : 0.0f;
     };
 
     if (p.kw_off) {
@@ -1421,8 +1436,10 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.vec_rows = (a.L & 3) == 0 && al16(a.tokens_in) && al16(a.tokens_out) && al16(a.table_in) &&
                  al16(a.table_out);
     const int nprobe = tr.w_bl ? p.n_loc * ((tr.bloom_k + 3) & ~3) : 0;
+    p.lds_lg = p.vec_logits && (size_t)p.rows_wg * a.V * 2 <= (size_t)LG_BYTES;
     const size_t shm = sizeof(uint64_t) * (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1) +
                        sizeof(uint64_t) * (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1) +
+                       (p.lds_lg ? sizeof(uint16_t) * (size_t)p.rows_wg * a.V : 0) +
                        sizeof(uint32_t) * ((size_t)nprobe + (p.wmax ? 32 * (size_t)tr.w_bm : 0) +
                                            (size_t)EXP_WAVES * p.stage_dw);
 
