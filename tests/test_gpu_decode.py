@@ -164,3 +164,62 @@ def test_decode_chain_stress_full_shape():
     child nodes, token history and block table on every row."""
     run_chain(W.WORKLOADS["stress_b64"].scaled(n_sids=2_000_000), 4, sample_rows=256,
               mask_sample=2048)
+
+
+def _decode_outputs(w, seed, trie, req, probes, kc, vc, debug):
+    """All per-step outputs of one chained decode (attention, selection,
+    reorder), with or without the debug mask and score outputs."""
+    from wide_beam_sid_amd.runner import Decoder
+    dec = Decoder(trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype, debug=debug)
+    ubm, upr = to_dev(req.user_bm), to_dev(probes)
+    kct, vct = to_dev(kc, w.dtype), to_dev(vc, w.dtype)
+    for t in range(w.L):
+        inp = W.make_step(w, seed, t)
+        dinp = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+        dec.step(t, ubm, upr if w.bloom_bits else None, w.n_loc, kct, vct, dinp)
+    torch.cuda.synchronize()
+    def bits(x):   # compared as bit patterns
+        if x.dtype in (torch.bfloat16, torch.float16):
+            x = x.view(torch.int16)
+        elif x.dtype == torch.float32:
+            x = x.view(torch.int32)
+        return x.cpu().numpy()
+    out = {}
+    for t in range(w.L):
+        for name in ("parent", "token", "cross_out", "self_out"):
+            out[f"{name}{t}"] = bits(getattr(dec, name)[t])
+    for t in range(w.L + 1):
+        for name in ("node", "acc", "tokens", "table"):
+            out[f"{name}{t}"] = bits(getattr(dec, name)[t])
+    return out, dec
+
+
+PLAIN = {
+    "main_full": (W.WORKLOADS["main_b16_m1024"], 1),
+    "main_b8_m512": (W.WORKLOADS["main_b16_m1024"].scaled(n_sids=50_000, B=8,
+                                                          schedule=(512, 512, 512, 512)), 5),
+    "stress_small": (W.WORKLOADS["stress_b64"].scaled(n_sids=20_000, B=2, geo_per_ad=(1, 64),
+                                                      T_ctx=130, schedule=(1024, 256, 512, 512)), 4),
+}
+
+
+@pytest.mark.parametrize("name", list(PLAIN))
+def test_decode_without_debug_outputs(name):
+    """The decode as the benchmark runs it, without the debug mask and score
+    outputs, gives bit for bit the outputs of the run with them, which the
+    chain tests check against the oracle."""
+    import wide_beam_sid_amd as gr
+    w, seed = PLAIN[name]
+    print(f"[plain] {name} B={w.B} sched={w.schedule} seed={seed}", flush=True)
+    sids = W.make_catalog(w, seed)
+    ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+    req = W.make_requests(w, seed)
+    kc, vc = W.make_context(w, seed)
+    trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads])
+    probes = (gr.bloom_probes(req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
+              if w.bloom_bits else np.zeros((1, 1), np.uint32))
+    a, dec = _decode_outputs(w, seed, trie, req, probes, kc, vc, debug=True)
+    del dec
+    b, _ = _decode_outputs(w, seed, trie, req, probes, kc, vc, debug=False)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
