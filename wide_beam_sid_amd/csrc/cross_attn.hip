@@ -53,7 +53,9 @@ struct JointArgs {
 // RB blocks of 16 rows.  The K / V tiles of 64 keys are double-buffered in
 // LDS: the global loads of tile i + 1 are in flight (in registers) while
 // tile i is computed, then written to the other buffer, one barrier per
-// tile.  K is stored row-major; V transposed, two keys per 32-bit store.
+// tile.  K is stored row-major; V transposed, two keys per 32-bit store,
+// each row's dword columns XOR-swizzled so the P.V reads are free of bank
+// conflicts.
 //
 // JOINT: after the context tiles, the same online softmax continues over the
 // row's own beam positions j = 0..t (shared-prefix beam attention): lane
@@ -75,10 +77,24 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     constexpr int VIT = (TT / 2) * (D / 8);        // (key pair, 8 d) V pieces per tile
     constexpr int KU = (KIT + 255) / 256, VU = (VIT + 255) / 256;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][TT][D + PAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D][TT + PAD];
+    // V^T as key pairs, row d of TT / 2 dwords.  SWZ (one row block, short
+    // key loops): the dword column is XORed with vsw(d), so the 16 rows a
+    // 16-lane pass of the P.V product reads (d & 3 and d / (D / 4) varying)
+    // fall on distinct banks.  Otherwise rows are padded by 4 dwords, which
+    // leaves 4-way conflicts but measured faster with two row blocks over
+    // long key loops.
+    constexpr bool SWZ = RB == 1;
+    constexpr int VP = TT / 2 + (SWZ ? 0 : PAD / 2);   // dwords per V^T row
+    __shared__ __attribute__((aligned(16))) uint32_t sVt[2][D][VP];
+    static_assert(D == 32 || D == 64 || D == 128, "head size");
+    constexpr int SHV = D == 32 ? 3 : (D == 64 ? 4 : 5);   // log2(D / 4)
+    auto vsw = [](int d) { return SWZ ? 2 * ((d & 3) | (((d >> SHV) & 3) << 2)) : 0; };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, a = lane & 15;
+    // every row d this lane reads in the P.V product has vsw(d) = 2a (SWZ)
+    // or 0, so its four V^T dword columns are vc0 ^ {0, 8, 16, 24}
+    const int vc0 = (2 * g) ^ (RB == 1 ? 2 * a : 0);
     const int mbase = bx * ROWS + wave * RB * 16;
     const size_t kvbase = ((size_t)b * H + h) * (size_t)T * D;
 
@@ -118,8 +134,9 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                 const uint32_t w1[4] = {vr[u][1].x, vr[u][1].y, vr[u][1].z, vr[u][1].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    *(uint32_t *)&sVt[buf][dc * 8 + 2 * e][2 * kp] = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-                    *(uint32_t *)&sVt[buf][dc * 8 + 2 * e + 1][2 * kp] = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+                    const int r0 = dc * 8 + 2 * e, r1 = r0 + 1;
+                    sVt[buf][r0][kp ^ vsw(r0)] = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+                    sVt[buf][r1][kp ^ vsw(r1)] = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
                 }
             }
         }
@@ -211,8 +228,8 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                 for (int db = 0; db < NDB; ++db) {
                     // A row a <-> d = (a/4)*4*NDB + db*4 + a%4
                     const int d = (a >> 2) * (4 * NDB) + db * 4 + (a & 3);
-                    const uint2 lo = *(const uint2 *)&sVt[cur][d][(2 * pc) * 16 + g * 4];
-                    const uint2 hi = *(const uint2 *)&sVt[cur][d][(2 * pc + 1) * 16 + g * 4];
+                    const uint2 lo = *(const uint2 *)&sVt[cur][d][vc0 ^ (pc * 16)];
+                    const uint2 hi = *(const uint2 *)&sVt[cur][d][vc0 ^ (pc * 16 + 8)];
                     V8 va;
                     va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.b, pb.b, o[rb][db], 0, 0, 0);
