@@ -54,14 +54,23 @@ KERNEL_SOURCES = ["wide_beam_sid_amd/csrc/constrain.hip", "wide_beam_sid_amd/csr
 TRAFFIC_FILE = "profiles/traffic_main_b16_m1024.json"
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources: a stored counter reading applies to
-    the kernels it was taken on only."""
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (string
+    literals in these files hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(root: str = None) -> str:
+    """sha256 over the kernel sources' code (comments and layout ignored): a
+    stored counter reading applies to the kernels it was taken on only."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root or ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -12,10 +12,13 @@
 //              request's bound U_b (best live parent score; every candidate
 //              is <= U_b since log-probs are <= 0), each row's log-sum-exp
 //              over all V logits, eqs 5 and 8 for every child of a node with
-//              a bit-sliced matcher block, then the child entries one per
-//              thread: eq 5 from the entry-ordered bitmask row, eq 8 for the
-//              entries still in (their Bloom rows tested by all wavefronts
-//              from a per-round list).  Survivors go to the workgroup's own
+//              a bit-sliced matcher block, then the other rows' child
+//              entries, two per thread per round: eq 5 from the
+//              entry-ordered bitmask row, eq 8 for the entries still in
+//              (their Bloom rows tested by all wavefronts from the round's
+//              list, the owner thread emitting the entries that pass); the
+//              rows' logits stay in LDS when they fit.  Survivors go to the
+//              workgroup's own
 //              segment and a 2048-bin histogram of U_b - score, merged into
 //              the request's histogram.
 //   k_select   one workgroup per request: the bin holding the k-th best
