@@ -192,16 +192,13 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// OR / AND of a 64-bit value over the wavefront (all lanes active)
 __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-    return v;
+    return (uint64_t)wave_or32((uint32_t)v) | ((uint64_t)wave_or32((uint32_t)(v >> 32)) << 32);
 }
 
 __device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v &= __shfl_xor(v, o, 64);
-    return v;
+    return (uint64_t)wave_and32((uint32_t)v) | ((uint64_t)wave_and32((uint32_t)(v >> 32)) << 32);
 }
 
 // Four words w0 .. w0 + 3 of a bit-sliced column, loaded unconditionally
@@ -418,11 +415,7 @@ void k_expand(TailParams p) {
         const uint64_t u = lane < p.w_bm ? p.user_bm[(size_t)b * p.w_bm + lane] : 0ull;
         const int n = __popcll(u);
         int inc = n;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
+        inc = (int)wave_incl_sum((uint32_t)inc);   // inclusive prefix over the lanes
         uint64_t x = u;
         for (int q = inc - n; x; ++q) {
             s_ubit[q] = (int16_t)(lane * 64 + __builtin_ctzll(x));
@@ -453,11 +446,7 @@ void k_expand(TailParams p) {
             s_acc[lane] = acc;
         }
         int inc = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
+        inc = (int)wave_incl_sum((uint32_t)inc);   // inclusive prefix over the lanes
         if (lane < nrows) s_rstart[lane + 1] = inc;
         if (lane == 0) s_rstart[0] = 0;
         const uint64_t sl = __ballot(lane < nrows && cnt > 0 && s_rblk[lane < nrows ? lane : 0] >= 0);
@@ -465,11 +454,7 @@ void k_expand(TailParams p) {
         if (lane == 0) s_nsl = __popcll(sl);
         // prefix over the rows without a block: their entries go through the rounds
         int inc2 = ((sl >> lane) & 1ull) ? 0 : cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc2, o, 64);
-            if (lane >= o) inc2 += y;
-        }
+        inc2 = (int)wave_incl_sum((uint32_t)inc2);   // inclusive prefix over the lanes
         if (lane < nrows) s_nstart[lane + 1] = inc2;
         if (lane == 0) s_nstart[0] = 0;
     }
@@ -568,7 +553,7 @@ void k_expand(TailParams p) {
         if (bal) {
             uint32_t base = 0;
             if (lane == 0) base = atomicAdd(&s_nsurv, (uint32_t)__popcll(bal));
-            base = __shfl(base, 0, 64);
+            base = __builtin_amdgcn_readlane(base, 0);
             if (sel) {
                 const uint32_t idx = base + lanes_below(bal);
                 if (idx < (uint32_t)p.seg_cap) {
@@ -932,7 +917,7 @@ void k_expand(TailParams p) {
                     if (dm) {
                         uint32_t base = 0;
                         if (lane == 0) base = atomicAdd(&s_kn, (uint32_t)__popcll(dm));
-                        base = __shfl(base, 0, 64);
+                        base = __builtin_amdgcn_readlane(base, 0);
                         if (blr >= 0) {
                             const uint32_t qi = base + lanes_below(dm);
                             lb[qi] = blr;
@@ -983,7 +968,7 @@ void k_expand(TailParams p) {
                 if (dm) {
                     uint32_t base = 0;
                     if (lane == 0) base = atomicAdd(&s_nl[0], (uint32_t)__popcll(dm));
-                    base = __shfl(base, 0, 64);
+                    base = __builtin_amdgcn_readlane(base, 0);
                     if (ok) {
                         qs[u] = (int)(base + lanes_below(dm));
                         Lb[qs[u]] = t.bli;
@@ -1085,11 +1070,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     }
     {   // exclusive prefix of the segment counts
         uint32_t sinc = c0 + c1;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(sinc, o, 64);
-            if (lane >= o) sinc += y;
-        }
+        sinc = wave_incl_sum(sinc);   // inclusive prefix over the lanes
         if (lane == 63) s_wsum2[wave] = sinc;
         __syncthreads();
         uint32_t spre = 0;
@@ -1111,11 +1092,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     for (int i = 0; i < PER; ++i) gh[tid * PER + i] = 0u;
     for (int i = tid; i < MAX_K; i += SEL_THREADS) s_key[i] = 0ull;
     uint32_t inc = part;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-    }
+    inc = wave_incl_sum(inc);   // inclusive prefix over the lanes
     if (lane == 63) s_wsum[wave] = inc;
     if (tid == 0) {
         s_thr = NBINS;
@@ -1208,14 +1185,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             }
             const uint32_t nmine = (uint32_t)__popc(msk);
             uint32_t inc = nmine;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(inc, o, 64);
-                if (lane >= o) inc += y;
-            }
+            inc = wave_incl_sum(inc);   // inclusive prefix over the lanes
             uint32_t base = 0;
             if (lane == 63 && inc) base = atomicAdd(&s_ncl, inc);
-            base = __shfl(base, 63, 64);
+            base = __builtin_amdgcn_readlane(base, 63);
             uint32_t ci = base + inc - nmine;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {

@@ -36,6 +36,51 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Cross-lane steps on DPP (data-parallel primitives: an operand read from
+// another lane of the same 16-lane row, no LDS round trip), for a wavefront
+// whose 64 lanes are all active.
+//   0xB1 quad_perm [1,0,3,2] (lane ^ 1)    0x4E quad_perm [2,3,0,1] (lane ^ 2)
+//   0x111.. row_shr:n   0x124 row_ror:4   0x128 row_ror:8
+//   0x142 row_bcast:15 (lane 15 of a row to the next row)
+//   0x143 row_bcast:31 (lane 31 to rows 2 and 3)
+// A lane with no source (or whose row is masked off) gets `ident`.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t ident) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// AND / OR over all 64 lanes, the same value in every lane: within each
+// row by DPP (quad butterflies, then rotations by 4 and 8), then the four
+// rows' values by readlane.
+__device__ __forceinline__ uint32_t wave_and32(uint32_t x) {
+    x &= dpp_u32<0xB1>(x, ~0u);
+    x &= dpp_u32<0x4E>(x, ~0u);
+    x &= dpp_u32<0x124>(x, ~0u);
+    x &= dpp_u32<0x128>(x, ~0u);
+    return __builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
+           __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48);
+}
+__device__ __forceinline__ uint32_t wave_or32(uint32_t x) {
+    x |= dpp_u32<0xB1>(x, 0u);
+    x |= dpp_u32<0x4E>(x, 0u);
+    x |= dpp_u32<0x124>(x, 0u);
+    x |= dpp_u32<0x128>(x, 0u);
+    return __builtin_amdgcn_readlane(x, 0) | __builtin_amdgcn_readlane(x, 16) |
+           __builtin_amdgcn_readlane(x, 32) | __builtin_amdgcn_readlane(x, 48);
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele shifts by 1, 2, 4, 8
+// within each row, then each row adds the totals of the rows before it.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += dpp_u32<0x111>(x, 0u);
+    x += dpp_u32<0x112>(x, 0u);
+    x += dpp_u32<0x114>(x, 0u);
+    x += dpp_u32<0x118>(x, 0u);
+    x += dpp_u32<0x142, 0xA>(x, 0u);
+    x += dpp_u32<0x143, 0xC>(x, 0u);
+    return x;
+}
+
 // Order LDS traffic of one wavefront (lanes exchange data through LDS
 // without a workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
