@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict
         const JointArgs nj{};
         cross_rows<D, RB, false>(q, K, Vv, out, M, H, T, scale_log2, nj, bx, rest % H, rest / H);
     } else {
-        self_attn_rows<true, 16, LPR, NCH>(sp, blk - n_cross);
+        self_attn_rows<true, 16, LPR, NCH, D / 8>(sp, blk - n_cross);   // a head: D * 2 / 16 lanes
     }
 }
 

@@ -9,6 +9,8 @@
 // of one-token blocks addressed through the block table P).
 #pragma once
 
+#include <type_traits>
+
 #include "gr_device.h"
 #include "gr_internal.h"
 
@@ -98,10 +100,30 @@ constexpr int self_rows_wg() {
     return 4 * (64 / LPR);
 }
 
+// Sum over each aligned group of GC lanes (GC a power of two known at
+// compile time): DPP steps within a 16-lane row (lane ^ 1, lane ^ 2, then
+// the mirror image within 8 and 16 lanes, each pairing the two halves of a
+// group), permutes across rows.
+template <int GC>
+__device__ __forceinline__ float group_sum_c(float v) {
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x),
+                                                          decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    if constexpr (GC > 1) v += dpp(v, std::integral_constant<int, 0xB1>{});
+    if constexpr (GC > 2) v += dpp(v, std::integral_constant<int, 0x4E>{});
+    if constexpr (GC > 4) v += dpp(v, std::integral_constant<int, 0x141>{});
+    if constexpr (GC > 8) v += dpp(v, std::integral_constant<int, 0x140>{});
+    if constexpr (GC > 16) v += __shfl_xor(v, 16, 64);
+    if constexpr (GC > 32) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 // Rows blk * self_rows_wg<LPR>() onwards.  A row's H*d_h elements are spread
 // over LPR lanes in CB-byte pieces, NCH pieces per lane (NCH > 1 only with
-// LPR = 64), so every load and store of a row is one coalesced access.
-template <bool BF16, int CB, int LPR, int NCH>
+// LPR = 64), so every load and store of a row is one coalesced access.  GC:
+// the lanes of one head when known at compile time (0: p.G at run time).
+template <bool BF16, int CB, int LPR, int NCH, int GC = 0>
 __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
     using C = Chunk<BF16, CB>;
     using W = typename C::W;
@@ -193,7 +215,11 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
 #pragma unroll
                 for (int x = 0; x < VEC; ++x) dot += qf[c][x] * kj[x];
                 // the G lanes of a head sit in one aligned group of the row
-                for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
+                if constexpr (GC > 0) {
+                    dot = group_sum_c<GC>(dot);
+                } else {
+                    for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
+                }
                 if (skip) continue;
                 const float sc = dot * p.scale;
                 const float mn = fmaxf(mrun[c], sc);
