@@ -522,12 +522,22 @@ void k_expand(TailParams p) {
                 for (int v = part; v < V; v += tpr) lse_push(logit_at<BF16>(p.logits, rowoff + v), m, s);
             }
         }
-        for (int o = 1; o < tpr; o <<= 1) {
-            const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        // merge the (max, sum) pairs of the row's tpr threads, butterfly
+        // fashion: within 16 lanes on DPP when tpr >= 16, by permutes beyond
+        auto merge = [&](float m2, float s2) {
             const float mm = fmaxf(m, m2);
             s = (m == -INFINITY ? 0.0f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.0f : s2 * __expf(m2 - mm));
             m = mm;
+        };
+        int o0 = 1;
+        if (tpr >= 16) {   // uniform
+            merge(dpp_f32<0xB1>(m), dpp_f32<0xB1>(s));     // lane ^ 1
+            merge(dpp_f32<0x4E>(m), dpp_f32<0x4E>(s));     // lane ^ 2
+            merge(dpp_f32<0x141>(m), dpp_f32<0x141>(s));   // mirror within 8
+            merge(dpp_f32<0x140>(m), dpp_f32<0x140>(s));   // mirror within 16
+            o0 = 16;
         }
+        for (int o = o0; o < tpr; o <<= 1) merge(__shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
         if (i < nrows && part == 0) s_lse[i] = has ? m + __logf(s) : 0.0f;
     }
     {

@@ -24,11 +24,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -79,6 +74,27 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
     x += dpp_u32<0x142, 0xA>(x, 0u);
     x += dpp_u32<0x143, 0xC>(x, 0u);
     return x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF,
+                                                      0xF, false));
+}
+
+// Max over all 64 lanes (all active), the same value in every lane: the
+// 16-lane rows on DPP (lane ^ 1, lane ^ 2, mirror within 8, mirror within
+// 16), then the four rows' values by readlane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 // Order LDS traffic of one wavefront (lanes exchange data through LDS
