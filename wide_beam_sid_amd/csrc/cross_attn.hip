@@ -196,8 +196,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                     s[kb][i] = v;
                     tmax = fmaxf(tmax, v);
                 }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = pair32_max(pair16_max(tmax));   // over the row's 4 lanes g
             const float mnew = fmaxf(mrow[rb], tmax);
             const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
             mrow[rb] = mnew;
@@ -284,8 +283,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
 #pragma unroll
                     for (int e = 0; e < 8; ++e) dot += (float)qf[rb][c][e] * (float)kk.b[e];
                 }
-                dot += __shfl_xor(dot, 16, 64);
-                dot += __shfl_xor(dot, 32, 64);
+                dot = pair32_sum(pair16_sum(dot));
                 const float sj = use ? dot * scale_log2 : -INFINITY;
                 const float mn = fmaxf(mrow[rb], sj);
                 const float al = __builtin_amdgcn_exp2f(mrow[rb] - mn);
@@ -309,8 +307,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         float lt = lpart[rb];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        lt = pair32_sum(pair16_sum(lt));
         const float inv = 1.0f / lt;
         const int m = mbase + rb * 16 + a;
         if (m >= M) continue;

@@ -97,6 +97,27 @@ __device__ __forceinline__ float wave_max(float v) {
                        __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
+// Max / sum over the lane pairs (l, l ^ 16) or (l, l ^ 32) on the gfx950
+// row swaps: v_permlane16_swap / v_permlane32_swap hand every lane the
+// values of the even and the odd row of its pair, so each lane of the pair
+// computes op(even, odd), the same in both.  All lanes active.
+__device__ __forceinline__ float pair16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order LDS traffic of one wavefront (lanes exchange data through LDS
 // without a workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
