@@ -21,15 +21,19 @@
 namespace gr {
 namespace {
 
-template <bool BF16, int CB, int LPR, int NCH>
+template <bool BF16, int CB, int LPR, int NCH, int GC>
 __global__ __launch_bounds__(256) void k_self_attn(SelfParams p) {
-    self_attn_rows<BF16, CB, LPR, NCH>(p, blockIdx.x);
+    self_attn_rows<BF16, CB, LPR, NCH, GC>(p, blockIdx.x);
 }
 
+// GC: 8 lanes per head (bf16 heads of 64 in 16-byte pieces) summed with
+// compile-time DPP steps; 0 for any other width, summed by permutes
 template <bool BF16, int CB, int LPR, int NCH>
 hipError_t go(const SelfParams &p, hipStream_t s) {
     constexpr int rows = self_rows_wg<LPR>();
-    k_self_attn<BF16, CB, LPR, NCH><<<(p.R + rows - 1) / rows, 256, 0, s>>>(p);
+    const dim3 grid((p.R + rows - 1) / rows);
+    if (p.G == 8) k_self_attn<BF16, CB, LPR, NCH, 8><<<grid, 256, 0, s>>>(p);
+    else k_self_attn<BF16, CB, LPR, NCH, 0><<<grid, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 
