@@ -48,9 +48,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ["wide_beam_sid_amd/csrc/constrain.hip", "wide_beam_sid_amd/csrc/cross_attn.hip",
-                  "wide_beam_sid_amd/csrc/self_attn.hip", "wide_beam_sid_amd/csrc/self_attn_body.h",
-                  "wide_beam_sid_amd/csrc/gr_device.h", "wide_beam_sid_amd/csrc/gr_internal.h"]
+_CSRC = "wide_beam_sid_amd/csrc/"
+_TAIL = [_CSRC + f for f in ("constrain.hip", "gr_device.h", "gr_internal.h")]
+_ATTN = [_CSRC + f for f in ("cross_attn.hip", "self_attn_body.h", "gr_device.h", "gr_internal.h")]
+# the files each profiled kernel's code comes from
+KERNEL_SOURCES = {
+    "k_expand": _TAIL, "k_select": _TAIL,
+    "k_attn_pair": _ATTN, "k_cross": _ATTN, "k_joint": _ATTN,
+    "k_self": [_CSRC + f for f in ("self_attn.hip", "self_attn_body.h", "gr_device.h",
+                                   "gr_internal.h")],
+}
 TRAFFIC_FILE = "profiles/traffic_main_b16_m1024.json"
 
 
@@ -63,12 +70,13 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash(root: str = None) -> str:
-    """sha256 over the kernel sources' code (comments and layout ignored): a
-    stored counter reading applies to the kernels it was taken on only."""
+def kernel_source_hash(kernel: str, root: str = None) -> str:
+    """sha256 over the code (comments and layout ignored) of the files a
+    kernel comes from: a stored counter reading applies to the code it was
+    taken on only."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(root or ROOT, f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
@@ -84,7 +92,8 @@ def measured_traffic(kernel: str, steps, workload: str):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("workload") != workload or doc.get("source_sha256") != kernel_source_hash():
+    if doc.get("workload") != workload or kernel not in KERNEL_SOURCES or \
+            doc.get("source_sha256", {}).get(kernel) != kernel_source_hash(kernel):
         return None
     rows = doc["per_step"].get(kernel)
     if not rows:
