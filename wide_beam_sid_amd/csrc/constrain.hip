@@ -379,7 +379,7 @@ void k_expand(TailParams p) {
     __shared__ int32_t s_lb[2 * EXP_THREADS];      // the round's Bloom rows awaiting eq 8
                                                    //   (-1 once the test fails)
     __shared__ uint32_t s_lf[EXP_THREADS];         // k-way: the thread that listed a row
-    __shared__ uint32_t s_nl[2];                   // entries in the list
+    __shared__ uint32_t s_nl;                      // entries in the list
     __shared__ uint32_t s_kn;                      // k-way: partitions listed this sub-round
     __shared__ uint8_t s_kok[EXP_THREADS];         // k-way: entry kept (a partition passed)
 
@@ -406,8 +406,7 @@ void k_expand(TailParams p) {
     for (int i = tid; i < p.rows_wg * p.mask_words; i += EXP_THREADS) s_mask[i] = 0ull;
     if (tid == 0) {
         s_nsurv = 0u;
-        s_nl[0] = 0u;
-        s_nl[1] = 0u;
+        s_nl = 0u;
         s_kn = 0u;
     }
     const BoundLoads bl0 = bound_load(p, b);   // reduced just before the barrier
@@ -977,7 +976,7 @@ void k_expand(TailParams p) {
                 const uint64_t dm = __ballot(ok);
                 if (dm) {
                     uint32_t base = 0;
-                    if (lane == 0) base = atomicAdd(&s_nl[0], (uint32_t)__popcll(dm));
+                    if (lane == 0) base = atomicAdd(&s_nl, (uint32_t)__popcll(dm));
                     base = __builtin_amdgcn_readlane(base, 0);
                     if (ok) {
                         qs[u] = (int)(base + lanes_below(dm));
@@ -987,12 +986,12 @@ void k_expand(TailParams p) {
             }
             if (!wq) continue;   // bitmask-only matcher: no Bloom test, no list
             __syncthreads();
-            const int n_bl = (int)s_nl[0];
+            const int n_bl = (int)s_nl;
             if (n_bl) {   // uniform
                 // eq 8 for the round's list (a failed entry's row id becomes -1)
                 bloom_list(Lb, n_bl);
                 __syncthreads();
-                if (tid == 0) s_nl[0] = 0u;   // every thread has read the count
+                if (tid == 0) s_nl = 0u;   // every thread has read the count
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {

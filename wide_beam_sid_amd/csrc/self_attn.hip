@@ -12,10 +12,11 @@
 // A beam row's H*d_h elements are spread over 16, 32 or 64 lanes in 16-byte
 // pieces (8 bf16 or 4 fp32 per lane; 8-byte pieces when a head is narrower
 // than 16 bytes), so a wavefront holds one to four rows and every load and
-// store of q, k, v, out and of a gathered pool block is a coalesced access;
-// the lanes of a head reduce their dot products with xor shuffles.  The prefix block ids are read in one load,
-// the blocks' K/V are gathered in batches with all loads of a batch in
-// flight, and positions are consumed with an online softmax.
+// store of q, k, v, out and of a gathered pool block is a coalesced access.
+// The lanes of a head sum their dot products with DPP butterflies (8-lane
+// heads) or permutes.  A row's prefix block ids are read per batch of
+// positions, the blocks' K/V gathered with all loads of a batch in flight,
+// and the positions consumed with an online softmax.
 #include "self_attn_body.h"
 
 namespace gr {
