@@ -34,6 +34,9 @@ union V8 {
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
+// bf16 pair (1, 1): a dot2 with it sums both halves of a packed pair.
+constexpr bf16x2v kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // Two fp32 values to a bf16 pair (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
@@ -63,7 +66,7 @@ struct JointArgs {
 // lanes of the row sum their parts, and the lane's output columns take the
 // weighted value; position t is the current token, which also goes to the
 // pool.  One output, no partial results leave the kernel.
-template <int D, int RB, bool JOINT>
+template <int D, int RB, bool JOINT, bool RAG>
 __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ K,
                                            const uint16_t *__restrict__ Vv,
@@ -186,17 +189,19 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                     s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[kb], 0, 0, 0);
                 }
             }
+            // The max runs over the raw dot products (the scale is positive);
+            // the running max m is kept in scaled log2 units, and each weight
+            // is exp2(s * scale_log2 - m) with the scale folded into one FMA.
+            // Keys past T exist only in a ragged last tile (RAG).
             float tmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float v = s[kb][i] * scale_log2;
-                    if (t0 + kb * 16 + g * 4 + i >= T) v = -INFINITY;
-                    s[kb][i] = v;
-                    tmax = fmaxf(tmax, v);
+                    if (RAG && t0 + kb * 16 + g * 4 + i >= T) s[kb][i] = -INFINITY;
+                    tmax = fmaxf(tmax, s[kb][i]);
                 }
-            tmax = pair32_max(pair16_max(tmax));   // over the row's 4 lanes g
+            tmax = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
             const float mnew = fmaxf(mrow[rb], tmax);
             const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
             mrow[rb] = mnew;
@@ -206,10 +211,13 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
             for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
                 for (int hp = 0; hp < 2; ++hp) {
-                    const uint32_t w = cvt_bf16x2(__builtin_amdgcn_exp2f(s[kb][2 * hp] - mnew),
-                                                  __builtin_amdgcn_exp2f(s[kb][2 * hp + 1] - mnew));
-                    // the normaliser sums the weights the product uses
-                    lsum += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+                    const uint32_t w = cvt_bf16x2(
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * hp], scale_log2, -mnew)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * hp + 1], scale_log2, -mnew)));
+                    // the normaliser sums the weights the product uses (both
+                    // bf16 halves of w times 1 on one dot2)
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), kOnes2,
+                                                          lsum, false);
                     pk[kb][hp] = w;
                 }
             }
@@ -324,22 +332,36 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     }
 }
 
-template <int D, int RB, bool JOINT>
+// XCD-aware tile order.  The dispatcher hands workgroup w to XCD w mod 8,
+// so workgroup w takes tile (w mod 8) * (n / 8) + w / 8: each XCD gets a
+// contiguous run of tiles, and the row blocks of one (request, head), which
+// are adjacent in the tile order, read their K / V through one L2 instead of
+// eight.  Workgroups past the last multiple of 8 keep their own index.
+__device__ __forceinline__ int xcd_tile(int w, int n) {
+    const int per = n >> 3;
+    return w < (per << 3) ? (w & 7) * per + (w >> 3) : w;
+}
+
+// One workgroup per (row block, head, request) tile; tiles are numbered
+// row block fastest, then head, then request.
+template <int D, int RB, bool JOINT, bool RAG>
 __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ K,
                                                        const uint16_t *__restrict__ Vv,
                                                        uint16_t *__restrict__ out, int M, int H,
-                                                       int T, float scale_log2, JointArgs jn) {
-    cross_rows<D, RB, JOINT>(q, K, Vv, out, M, H, T, scale_log2, jn, blockIdx.x, blockIdx.y,
-                             blockIdx.z);
+                                                       int T, float scale_log2, int gxc,
+                                                       int n_tiles, JointArgs jn) {
+    const int tile = xcd_tile(blockIdx.x, n_tiles);
+    const int bx = tile % gxc, rest = tile / gxc;
+    cross_rows<D, RB, JOINT, RAG>(q, K, Vv, out, M, H, T, scale_log2, jn, bx, rest % H, rest / H);
 }
 
 // Cross- and self-attention of one decode step in one launch (they are
 // independent): the first n_cross workgroups take the cross-attention tiles
-// (x fastest, then head, then request), the rest take the self-attention
+// (in the XCD-aware order above), the rest take the self-attention
 // rows (4 to 16 per workgroup, by row width).  Saves a launch and lets the MFMA-bound tiles and the
 // gather-bound rows share the machine.
-template <int D, int RB, int LPR, int NCH>
+template <int D, int RB, bool RAG, int LPR, int NCH>
 __global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict__ q,
                                                       const uint16_t *__restrict__ K,
                                                       const uint16_t *__restrict__ Vv,
@@ -348,9 +370,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_pair(const uint16_t *__restrict
                                                       int n_cross, SelfParams sp) {
     const int blk = blockIdx.x;
     if (blk < n_cross) {
-        const int bx = blk % gxc, rest = blk / gxc;
+        const int tile = xcd_tile(blk, n_cross);
+        const int bx = tile % gxc, rest = tile / gxc;
         const JointArgs nj{};
-        cross_rows<D, RB, false>(q, K, Vv, out, M, H, T, scale_log2, nj, bx, rest % H, rest / H);
+        cross_rows<D, RB, false, RAG>(q, K, Vv, out, M, H, T, scale_log2, nj, bx, rest % H,
+                                      rest / H);
     } else {
         self_attn_rows<true, 16, LPR, NCH, D / 8>(sp, blk - n_cross);   // a head: D * 2 / 16 lanes
     }
@@ -433,6 +457,31 @@ __global__ __launch_bounds__(256) void k_joint_f32(const float *__restrict__ q,
     if (act) out[((size_t)r * H + h) * D + lane] = o / l;
 }
 
+// The bf16 tile kernel for head size d, one or two row blocks per
+// wavefront (big) and a ragged last key tile or none (rag).
+template <bool JOINT>
+hipError_t launch_cross_tiles(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              uint16_t *out, int M, int H, int T, int d, float sl2, int gxc,
+                              int n, bool big, bool rag, const JointArgs &jn, hipStream_t s) {
+#define GR_TILES(DD, RBB, RG) \
+    k_cross_bf16<DD, RBB, JOINT, RG><<<n, 256, 0, s>>>(q, k, v, out, M, H, T, sl2, gxc, n, jn)
+#define GR_TILES_R(DD, RBB)        \
+    {                              \
+        if (rag) GR_TILES(DD, RBB, true); \
+        else GR_TILES(DD, RBB, false);    \
+    }
+    if (d == 32) {
+        if (big) GR_TILES_R(32, 2) else GR_TILES_R(32, 1)
+    } else if (d == 64) {
+        if (big) GR_TILES_R(64, 2) else GR_TILES_R(64, 1)
+    } else {
+        GR_TILES_R(128, 1)
+    }
+#undef GR_TILES_R
+#undef GR_TILES
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out, int B, int M,
@@ -452,20 +501,10 @@ hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *
     // (d_h = 128 always: 128 rows would not fit the registers of two waves
     // per SIMD)
     const bool big = T > 2 * TT && d <= 64;
-    dim3 grid((M + (big ? 127 : 63)) / (big ? 128 : 64), H, B);
-    const JointArgs nj{};
-#define GR_CROSS(DD)                                                                          \
-    if (big) k_cross_bf16<DD, 2, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj); \
-    else k_cross_bf16<DD, 1, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj);
-    if (d == 32) {
-        GR_CROSS(32)
-    } else if (d == 64) {
-        GR_CROSS(64)
-    } else {
-        k_cross_bf16<128, 1, false><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, nj);
-    }
-#undef GR_CROSS
-    return hipGetLastError();
+    const int gxc = (M + (big ? 127 : 63)) / (big ? 128 : 64);
+    const int n = gxc * H * B;
+    return launch_cross_tiles<false>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, big, T % TT != 0,
+                                     JointArgs{}, s);
 }
 
 hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const void *k_new,
@@ -494,17 +533,10 @@ hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const 
     jn.t = t;
     jn.L = L;
     const bool big = T > 2 * TT && d <= 64;
-    dim3 grid((M + (big ? 127 : 63)) / (big ? 128 : 64), H, B);
-    if (d == 32) {
-        if (big) k_cross_bf16<32, 2, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
-        else k_cross_bf16<32, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
-    } else if (d == 64) {
-        if (big) k_cross_bf16<64, 2, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
-        else k_cross_bf16<64, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
-    } else {
-        k_cross_bf16<128, 1, true><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, jn);
-    }
-    return hipGetLastError();
+    const int gxc = (M + (big ? 127 : 63)) / (big ? 128 : 64);
+    const int n = gxc * H * B;
+    return launch_cross_tiles<true>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, big, T % TT != 0,
+                                    jn, s);
 }
 
 hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx, void *cross_out,
@@ -532,15 +564,21 @@ hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx
     const int n_cross = gxc * H * B;
     const int srows = 4 * (64 / ly.lpr);
     const dim3 grid(n_cross + (R + srows - 1) / srows);
+    const bool rag = T % TT != 0;
 #define GR_PAIR_K(DD, RBB, LL, NN)                                                              \
-    k_attn_pair<DD, RBB, LL, NN><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T, sl2, gxc, n_cross, sp)
+    {                                                                                           \
+        if (rag) k_attn_pair<DD, RBB, true, LL, NN><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H,  \
+                                                                         T, sl2, gxc, n_cross, sp); \
+        else k_attn_pair<DD, RBB, false, LL, NN><<<grid, 256, 0, s>>>(qq, kk, vv, oo, M, H, T,  \
+                                                                      sl2, gxc, n_cross, sp);   \
+    }
 #define GR_PAIR(DD, RBB)                                                                        \
     {                                                                                           \
-        if (ly.lpr == 16) GR_PAIR_K(DD, RBB, 16, 1);                                            \
-        else if (ly.lpr == 32) GR_PAIR_K(DD, RBB, 32, 1);                                       \
-        else if (ly.nch <= 1) GR_PAIR_K(DD, RBB, 64, 1);                                        \
-        else if (ly.nch <= 2) GR_PAIR_K(DD, RBB, 64, 2);                                        \
-        else GR_PAIR_K(DD, RBB, 64, 4);                                                         \
+        if (ly.lpr == 16) GR_PAIR_K(DD, RBB, 16, 1)                                             \
+        else if (ly.lpr == 32) GR_PAIR_K(DD, RBB, 32, 1)                                        \
+        else if (ly.nch <= 1) GR_PAIR_K(DD, RBB, 64, 1)                                         \
+        else if (ly.nch <= 2) GR_PAIR_K(DD, RBB, 64, 2)                                         \
+        else GR_PAIR_K(DD, RBB, 64, 4)                                                          \
     }
     if (d == 32) {
         if (big) GR_PAIR(32, 2) else GR_PAIR(32, 1)
