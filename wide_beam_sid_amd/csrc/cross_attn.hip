@@ -25,6 +25,7 @@ namespace {
 
 constexpr int TT = 64;          // keys per LDS tile
 constexpr int PAD = 8;          // bf16 padding per LDS row
+constexpr int BUF_DWORD3 = 0x00020000;   // buffer descriptor word 3 for gfx9 raw loads
 
 union V8 {
     uint4 u;
@@ -101,25 +102,46 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     const int mbase = bx * ROWS + wave * RB * 16;
     const size_t kvbase = ((size_t)b * H + h) * (size_t)T * D;
 
+    // K / V tiles through buffer loads: the (request, head) slice is the
+    // buffer (T * D bf16), each lane's offset inside a tile is fixed and the
+    // tile's start goes in the scalar offset.  Keys past T fall outside the
+    // buffer and read as zeros, so a ragged last tile needs no branches.
+    const uint32_t nbytes = (uint32_t)T * D * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(K + kvbase), (short)0, nbytes, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(Vv + kvbase), (short)0, nbytes, BUF_DWORD3);
+    uint32_t ko[KU], vo[VU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+        const int it = tid + u * 256, key = it / (D / 8), dc = it % (D / 8);
+        ko[u] = (uint32_t)(key * D + dc * 8) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+        // consecutive threads take consecutive key pairs of one 8-wide d
+        // block, so the transposed stores below fill consecutive dwords
+        const int it = tid + u * 256, dc = it / (TT / 2), kp = it % (TT / 2);
+        vo[u] = (uint32_t)(2 * kp * D + dc * 8) * 2;
+    }
+    auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+        return make_uint4(x[0], x[1], x[2], x[3]);
+    };
     uint4 kr[KU], vr[VU][2];
     auto load_tile = [&](int t0) {
+        const uint32_t so = (uint32_t)t0 * D * 2;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
-            const int it = tid + u * 256, key = it / (D / 8), dc = it % (D / 8);
             kr[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (it < KIT && t0 + key < T)
-                kr[u] = *(const uint4 *)(K + kvbase + (size_t)(t0 + key) * D + dc * 8);
+            if (KIT % 256 == 0 || tid + u * 256 < KIT) kr[u] = ld16(rk, ko[u], so);
         }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
-            // consecutive threads take consecutive key pairs of one 8-wide d
-            // block, so the transposed stores below fill consecutive dwords
-            const int it = tid + u * 256, dc = it / (TT / 2), kp = it % (TT / 2);
             vr[u][0] = vr[u][1] = make_uint4(0u, 0u, 0u, 0u);
-            if (it < VIT) {
-                const int k0 = t0 + 2 * kp;
-                if (k0 < T) vr[u][0] = *(const uint4 *)(Vv + kvbase + (size_t)k0 * D + dc * 8);
-                if (k0 + 1 < T) vr[u][1] = *(const uint4 *)(Vv + kvbase + (size_t)(k0 + 1) * D + dc * 8);
+            if (VIT % 256 == 0 || tid + u * 256 < VIT) {
+                vr[u][0] = ld16(rv, vo[u], so);
+                vr[u][1] = ld16(rv, vo[u] + D * 2, so);
             }
         }
     };
@@ -145,8 +167,10 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         }
     };
 
-    load_tile(0);
     // Q^T as the B operand: lane (g, a) holds Q[row a][c*32 + g*8 .. +8].
+    // Loaded before the first tile, so that the first tile's wait also
+    // covers them: no load of the prologue is still pending inside the key
+    // loop, where the only loads in flight are the next tile's.
     bf16x8 qf[RB][NDC];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -160,6 +184,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
             qf[rb][c] = t.b;
         }
     }
+    load_tile(0);
     f32x4 o[RB][NDB];
     float mrow[RB], lpart[RB];
 #pragma unroll
