@@ -167,10 +167,14 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         }
     };
 
-    // Q^T as the B operand: lane (g, a) holds Q[row a][c*32 + g*8 .. +8].
-    // Loaded before the first tile, so that the first tile's wait also
-    // covers them: no load of the prologue is still pending inside the key
-    // loop, where the only loads in flight are the next tile's.
+    load_tile(0);
+    // Q^T as the B operand: lane (g, a) holds Q[row a][c*32 + g*8 .. +8];
+    // these loads stay in flight over the first tile's LDS stores and
+    // barrier.
+    // The request's M rows are one buffer, so rows past M read as zeros
+    // and every lane issues the same loads (no branch around them).
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(q + (size_t)b * M * H * D), (short)0, (uint32_t)M * H * D * 2, BUF_DWORD3);
     bf16x8 qf[RB][NDC];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -178,13 +182,10 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
 #pragma unroll
         for (int c = 0; c < NDC; ++c) {
             V8 t;
-            t.u = make_uint4(0, 0, 0, 0);
-            if (m < M)
-                t.u = *(const uint4 *)(q + (((size_t)b * M + m) * H + h) * D + c * 32 + g * 8);
+            t.u = ld16(rq, (uint32_t)(((size_t)m * H + h) * D + c * 32 + g * 8) * 2, 0);
             qf[rb][c] = t.b;
         }
     }
-    load_tile(0);
     f32x4 o[RB][NDB];
     float mrow[RB], lpart[RB];
 #pragma unroll
@@ -197,8 +198,16 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     store_tile(0);
     __syncthreads();
 
-    for (int t0 = 0, cur = 0; t0 < T; t0 += TT, cur ^= 1) {
+    // One 64-key tile: the next tile's loads go out first, the products
+    // and the softmax run on the current buffer, then the next tile is
+    // stored to the other one.  The first tile is peeled off the loop and
+    // waits for every load still in flight (the Q fragments) before it
+    // issues the second tile's, so that neither it nor the loop, where the
+    // only loads in flight are the next tile's, holds its products for
+    // them.
+    auto key_tile = [&](int t0, int cur, bool first) {
         const bool more = t0 + TT < T;
+        if (first) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
         if (more) load_tile(t0 + TT);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -270,7 +279,9 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         }
         if (more) store_tile(cur ^ 1);
         __syncthreads();
-    }
+    };
+    key_tile(0, 0, true);
+    for (int t0 = TT, cur = 1; t0 < T; t0 += TT, cur ^= 1) key_tile(t0, cur, false);
 
     if constexpr (JOINT) {
 #pragma unroll
