@@ -141,30 +141,43 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
     W *kp = (W *)p.k_pool;
     W *vp = (W *)p.v_pool;
 
+    // The first batch's block ids go out before the row's own loads and
+    // the stores of its k, v: the gathers then wait for one round trip, not
+    // two.
+    // (Every lane loads every id of the batch, clamped to the row, and
+    // drops those at or past t, so the loads are not behind branches.)
+    int32_t bid0[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int32_t v = p.table[(size_t)i * p.L + min(jj, p.L - 1)];
+        bid0[jj] = jj < p.t ? v : -1;
+    }
+
+    // The row's q, k, v (a lane past the row's pieces reads its last one;
+    // see the gathers below).  The current token's k, v and block id are
+    // stored at the end: no position of this step reads block f, and a
+    // store here would hold up the gathers' wait.
     float qf[NCH][VEC], kc[NCH][VEC], vc[NCH][VEC];
     float o[NCH][VEC], mrun[NCH], lrun[NCH];
     bool act[NCH];
+    W ukp[NCH], uvp[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int e = c * LPR + lr;
         act[c] = e < E2;
-        W uq = C::zero(), uk = uq, uv = uq;
-        if (act[c]) {
-            uq = q[e];
-            uk = kn[e];
-            uv = vn[e];
-            kp[(size_t)f * E2 + e] = uk;   // current token -> fresh block
-            vp[(size_t)f * E2 + e] = uv;
-        }
+        const int ec = min(e, E2 - 1);
+        W uq = q[ec];
+        ukp[c] = kn[ec];
+        uvp[c] = vn[ec];
+        if (!act[c]) uq = C::zero();
         C::unpack(uq, qf[c]);
-        C::unpack(uk, kc[c]);
-        C::unpack(uv, vc[c]);
+        C::unpack(ukp[c], kc[c]);
+        C::unpack(uvp[c], vc[c]);
         mrun[c] = -INFINITY;
         lrun[c] = 0.0f;
 #pragma unroll
         for (int x = 0; x < VEC; ++x) o[c][x] = 0.0f;
     }
-    if (lr == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
 
     // Prefix positions in batches of JB: the batch's block ids (one load,
     // the same address for the row's lanes), then every block load of the
@@ -174,8 +187,15 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             const int j = j0 + jj;
-            bid[jj] = j < p.t ? p.table[(size_t)i * p.L + j] : -1;
+            bid[jj] = j0 == 0 ? bid0[jj] : (j < p.t ? p.table[(size_t)i * p.L + j] : -1);
         }
+        // Every lane loads a piece for every position of the batch, so the
+        // loads are not behind branches and all of them are in flight
+        // together: a position that is not used (past t, or a dead row's
+        // missing past, skipped below) re-reads the lane's own q piece,
+        // which the cache still holds, and a lane past the row's pieces
+        // reads its last piece (its lanes form whole heads of their own,
+        // whose results are never stored).
         W kr[JB][NCH], vr[JB][NCH];
         bool use[JB];
 #pragma unroll
@@ -183,14 +203,13 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
             const int j = j0 + jj;
             // a dead row's missing past is skipped
             use[jj] = j < p.t && bid[jj] >= 0 && bid[jj] < p.pool_blocks;
+            const W *ks = use[jj] ? kp + (size_t)bid[jj] * E2 : q;
+            const W *vs = use[jj] ? vp + (size_t)bid[jj] * E2 : q;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const int e = c * LPR + lr;
-                kr[jj][c] = vr[jj][c] = C::zero();
-                if (use[jj] && act[c]) {
-                    kr[jj][c] = kp[(size_t)bid[jj] * E2 + e];
-                    vr[jj][c] = vp[(size_t)bid[jj] * E2 + e];
-                }
+                const int e = min(c * LPR + lr, E2 - 1);
+                kr[jj][c] = ks[e];
+                vr[jj][c] = vs[e];
             }
         }
 #pragma unroll
@@ -237,12 +256,15 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
     for (int c = 0; c < NCH; ++c) {
         const int e = c * LPR + lr;
         if (!act[c]) continue;
+        kp[(size_t)f * E2 + e] = ukp[c];   // current token -> fresh block
+        vp[(size_t)f * E2 + e] = uvp[c];
         const float inv = 1.0f / lrun[c];
         float r[VEC];
 #pragma unroll
         for (int x = 0; x < VEC; ++x) r[x] = o[c][x] * inv;
         out[e] = C::pack(r);
     }
+    if (lr == 0) p.table[(size_t)i * p.L + p.t] = (int32_t)f;
 }
 
 inline SelfParams self_params(const void *q, const void *k_new, const void *v_new, void *k_pool,
