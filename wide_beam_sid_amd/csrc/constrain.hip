@@ -310,12 +310,11 @@ __device__ __forceinline__ void write_slot(const TailParams &p, int b, size_t sl
         const uint32_t f = key_flat(key);
         const int m = (int)(f / (uint32_t)V), v = (int)(f % (uint32_t)V);
         const int parent = b * p.M_in + m;
-        p.parent_out[sl] = parent;
-        p.token_out[sl] = v;
-        p.node_out[sl] = child;
-        p.acc_out[sl] = key_score(key);
+        // the parent's rows are read before any store of the slot: stores
+        // count in the same counter as loads, so a store ahead of them
+        // would make their wait cover its completion too
         if (p.vec_rows) {   // rows of L int32 as 16-byte pieces
-            for (int l0 = 0; l0 < L; l0 += 4) {
+            auto piece = [&](int l0) {
                 int4 tk = make_int4(-1, -1, -1, -1), tb = tk;
                 if (p.tokens_out && l0 < t) tk = *(const int4 *)(p.tokens_in + (size_t)parent * L + l0);
                 if (p.table_out && l0 <= t) tb = *(const int4 *)(p.table_in + (size_t)parent * L + l0);
@@ -328,7 +327,9 @@ __device__ __forceinline__ void write_slot(const TailParams &p, int b, size_t sl
                 }
                 if (p.tokens_out) *(int4 *)(p.tokens_out + sl * L + l0) = tk;
                 if (p.table_out) *(int4 *)(p.table_out + sl * L + l0) = tb;
-            }
+            };
+            piece(0);   // the first piece outside a loop: no wait at a loop entry
+            for (int l0 = 4; l0 < L; l0 += 4) piece(l0);
         } else {
             if (p.tokens_out)
                 for (int l = 0; l < L; ++l)
@@ -337,6 +338,10 @@ __device__ __forceinline__ void write_slot(const TailParams &p, int b, size_t sl
                 for (int l = 0; l < L; ++l)
                     p.table_out[sl * L + l] = l <= t ? p.table_in[(size_t)parent * L + l] : -1;
         }
+        p.parent_out[sl] = parent;
+        p.token_out[sl] = v;
+        p.node_out[sl] = child;
+        p.acc_out[sl] = key_score(key);
     } else {
         p.parent_out[sl] = -1;
         p.token_out[sl] = -1;
@@ -1230,14 +1235,19 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         // pairs), 8 pairs in flight per thread.
         const uint32_t n_pairs = n_surv >> 1;
         for (uint32_t p0 = 0; p0 < n_pairs; p0 += 8 * SEL_THREADS) {
+            // every pair's offset first, then every load (a pair past the
+            // end reads the first pair again and is dropped), so no load
+            // waits behind another's search
             uint32_t src[8];
             uint4 kv[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint32_t pp = p0 + u * SEL_THREADS + tid;
                 src[u] = pp < n_pairs ? surv(2 * pp) : 0xFFFFFFFFu;
-                kv[u] = pp < n_pairs ? *(const uint4 *)(keys + src[u]) : make_uint4(0u, 0u, 0u, 0u);
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                kv[u] = *(const uint4 *)(keys + (src[u] != 0xFFFFFFFFu ? src[u] : 0u));
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (src[u] == 0xFFFFFFFFu) continue;
@@ -1343,8 +1353,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
             const int end = (int)s_seg[bin], start = bin ? (int)s_seg[bin - 1] : 0;
             slot = start + count_above(s_key, start, end, keyp);
         }
-        write_slot(p, b, (size_t)b * k + slot, live, keyp,
-                   live ? p.schild[(size_t)b * gx * seg_cap + srcp] : -1);
+        // the child id is read unconditionally (a dead slot reads the first
+        // survivor's), so it goes out with the parent's rows
+        const int32_t ch = p.schild[(size_t)b * gx * seg_cap + (live ? srcp : 0u)];
+        write_slot(p, b, (size_t)b * k + slot, live, keyp, live ? ch : -1);
     }
 }
 
