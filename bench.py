@@ -182,8 +182,10 @@ class Bench:
             R = w.rows(t)
             e = [self.torch.cuda.Event(enable_timing=True) for _ in range(6)]
             e[0].record(self.stream)
-            st = self.L.gr_cross_attn(a.qx, a.k_ctx, a.v_ctx, a.cross_out, w.B, d.M[t], w.H,
-                                      w.T_ctx, w.d_h, gdt, self.sp)
+            # as the decode step runs it: split over the context when the
+            # step has few tiles and a long context
+            st = self.L.gr_cross_attn_ws(a.qx, a.k_ctx, a.v_ctx, a.cross_out, w.B, d.M[t], w.H,
+                                         w.T_ctx, w.d_h, gdt, a.attn_ws, a.attn_ws_bytes, self.sp)
             e[1].record(self.stream)
             st |= self.L.gr_self_attn_paged(a.q, a.k_new, a.v_new, a.k_pool, a.v_pool,
                                             a.pool_blocks, a.tail.table_in, a.fresh_base, R, t,

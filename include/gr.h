@@ -208,6 +208,25 @@ gr_status gr_cross_attn(const void *q, const void *k_ctx, const void *v_ctx, voi
                         int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
                         gr_dtype dtype, void *stream);
 
+/*
+ * The same output, with the context split across workgroups when the launch
+ * has few tiles (beams x heads x requests) and a long context: each split
+ * runs the online softmax over its own key range and leaves its
+ * unnormalised output, running max and normaliser in ws; a second launch
+ * merges the splits with a log-sum-exp (the combination the GR-Inference
+ * page uses to merge its context and beam parts).
+ * gr_cross_attn_workspace returns the bytes ws must hold for these shapes
+ * (0 when no split is used: f32, short contexts, or enough tiles).  ws is
+ * caller-owned device memory, 16-byte aligned, holding no state between
+ * calls; NULL runs gr_cross_attn.  GR_E_WORKSPACE if ws is given but
+ * smaller than needed; otherwise the errors of gr_cross_attn.
+ */
+size_t gr_cross_attn_workspace(int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
+                               gr_dtype dtype);
+gr_status gr_cross_attn_ws(const void *q, const void *k_ctx, const void *v_ctx, void *out,
+                           int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
+                           gr_dtype dtype, void *ws, size_t ws_bytes, void *stream);
+
 /* ===================================================================== */
 /* A2: paged short-prefix self-attention (GRACE Sections 3.3, 5.2, 5.3). */
 /* ===================================================================== */
@@ -352,6 +371,8 @@ typedef struct {
     int64_t pool_blocks, fresh_base;
     void *cross_out, *self_out;    /* [B*M_in, H, d_h]                              */
     gr_tail_args tail;             /* dtype applies to every tensor of the step     */
+    void *attn_ws;                 /* NULL, or the cross-attention workspace of     */
+    size_t attn_ws_bytes;          /*   gr_cross_attn_ws (split context)            */
 } gr_step_args;
 
 gr_status gr_decode_step(const gr_trie *trie, const gr_step_args *args, void *stream);

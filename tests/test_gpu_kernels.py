@@ -75,6 +75,51 @@ def test_cross_attn_parity(B, M, H, T, d, dt):
         assert np.array_equal(got, np.repeat(_as_f(Vv, dt)[:, :, 0], M, axis=0))
 
 
+# Few tiles over a long context: the split path (key ranges over several
+# workgroups, merged with a log-sum-exp) against the oracle, and the same
+# inputs without a workspace.
+SPLIT_CASES = [
+    # B, M, H, T, d
+    (8, 1, 16, 2048, 128),   # the long-context workload's first step
+    (8, 20, 16, 2048, 128),  # its second step
+    (32, 1, 8, 1024, 64),    # 32 requests, one beam each
+    (2, 3, 2, 700, 64),      # ragged last key tile, uneven splits
+    (1, 70, 2, 1000, 32),    # two row tiles, ragged keys, d_h = 32
+]
+
+
+@pytest.mark.parametrize("B,M,H,T,d", SPLIT_CASES)
+def test_cross_attn_split_parity(B, M, H, T, d):
+    gr = _gr()
+    nbytes = gr.cross_attn_workspace(B, M, H, T, d, "bf16")
+    assert nbytes > 0, "these shapes take the split path"
+    rng = np.random.default_rng(B * 31 + M * 7 + T + d)
+    q = _rand((B * M, H, d), "bf16", rng)
+    K = _rand((B, H, T, d), "bf16", rng)
+    Vv = _rand((B, H, T, d), "bf16", rng)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(0xFF)   # no state needed
+    out = torch.empty(to_dev(q, "bf16").shape, dtype=torch.bfloat16, device="cuda")
+    plain = torch.empty_like(out)
+    print(f"[split] {B}x{M}x{H}x{T}x{d} ws={nbytes}", flush=True)
+    gr.cross_attn(to_dev(q, "bf16"), to_dev(K, "bf16"), to_dev(Vv, "bf16"), out, B, M, ws=ws)
+    gr.cross_attn(to_dev(q, "bf16"), to_dev(K, "bf16"), to_dev(Vv, "bf16"), plain, B, M)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attn(_as_f(q, "bf16"), _as_f(K, "bf16"), _as_f(Vv, "bf16"), B, M)
+    attn_close(to_np64(out), ref, "bf16", f"split cross {B}x{M}x{H}x{T}x{d}")
+    attn_close(to_np64(plain), ref, "bf16", f"plain cross {B}x{M}x{H}x{T}x{d}")
+
+
+def test_cross_attn_split_workspace_error():
+    gr = _gr()
+    B, M, H, T, d = 8, 1, 16, 2048, 128
+    nbytes = gr.cross_attn_workspace(B, M, H, T, d, "bf16")
+    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((B * M, H, d), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((B, H, T, d), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gr.GrError):
+        gr.cross_attn(x, kv, kv, torch.empty_like(x), B, M, ws=small)
+
+
 # ---------------------------------------------------------------------------
 # Joint attention: context + the row's beam prefix in one softmax
 # ---------------------------------------------------------------------------

@@ -153,3 +153,17 @@ def test_decode_graph_argument_errors_without_capture():
     assert L.gr_decode_graph_create(None, None, 1, ctypes.c_void_p(16), None) == _lib.GR_E_INVALID
     assert L.gr_decode_graph_launch(None, None) == _lib.GR_E_INVALID
     L.gr_decode_graph_destroy(None)   # no-op
+
+
+def test_cross_attn_workspace_plan():
+    """The split cross-attention is planned only for bf16 launches with few
+    tiles and a long context; its workspace holds S * rows * heads * (d + 2)
+    floats."""
+    import wide_beam_sid_amd as gr
+    assert gr.cross_attn_workspace(16, 1024, 4, 64, 64, "bf16") == 0      # short context
+    assert gr.cross_attn_workspace(32, 64, 8, 256, 64, "bf16") == 0       # four key tiles
+    assert gr.cross_attn_workspace(64, 1024, 8, 512, 64, "bf16") == 0     # many tiles
+    assert gr.cross_attn_workspace(8, 1, 16, 2048, 128, "f32") == 0       # fp32 path
+    n = gr.cross_attn_workspace(8, 1, 16, 2048, 128, "bf16")
+    per_split = 8 * 1 * 16 * (128 + 2) * 4
+    assert n > 0 and n % per_split == 0 and 2 <= n // per_split <= 16

@@ -180,11 +180,24 @@ class Trie:
             pass
 
 
-def cross_attn(q, k_ctx, v_ctx, out, B: int, M: int, stream=None) -> None:
-    """A1 on torch tensors: q/out [B*M, H, d_h], k_ctx/v_ctx [B, H, T_ctx, d_h]."""
+def cross_attn(q, k_ctx, v_ctx, out, B: int, M: int, stream=None, ws=None) -> None:
+    """A1 on torch tensors: q/out [B*M, H, d_h], k_ctx/v_ctx [B, H, T_ctx, d_h].
+    With ws (a device buffer of cross_attn_workspace bytes) a long context
+    is split across workgroups when the launch has few tiles."""
     H, T, d = k_ctx.shape[1], k_ctx.shape[2], k_ctx.shape[3]
-    check(_lib.lib().gr_cross_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(out), B, M, H, T, d,
-                                   _dtype(q), _stream(stream)))
+    if ws is None:
+        check(_lib.lib().gr_cross_attn(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(out), B, M, H, T,
+                                       d, _dtype(q), _stream(stream)))
+    else:
+        check(_lib.lib().gr_cross_attn_ws(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(out), B, M, H,
+                                          T, d, _dtype(q), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)))
+
+
+def cross_attn_workspace(B: int, M: int, H: int, T_ctx: int, d_h: int, dtype: str) -> int:
+    """Bytes of the split cross-attention workspace for these shapes (0: no split)."""
+    return int(_lib.lib().gr_cross_attn_workspace(B, M, H, T_ctx, d_h,
+                                                  GR_BF16 if dtype == "bf16" else GR_F32))
 
 
 def self_attn_paged(q, k_new, v_new, k_pool, v_pool, table, fresh_base: int, t: int, out,

@@ -21,7 +21,8 @@ EXPORTS = [
     "gr_last_error", "gr_version", "gr_bloom_probes",
     "gr_trie_builder_create", "gr_trie_builder_add_ads", "gr_trie_builder_finish",
     "gr_trie_builder_destroy", "gr_trie_create", "gr_trie_host_view", "gr_trie_info",
-    "gr_trie_destroy", "gr_cross_attn", "gr_self_attn_paged", "gr_joint_attn",
+    "gr_trie_destroy", "gr_cross_attn", "gr_cross_attn_workspace", "gr_cross_attn_ws",
+    "gr_self_attn_paged", "gr_joint_attn",
     "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
     "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
     "gr_decode_graph_destroy", "gr_ad_index_create", "gr_ad_index_add_ads",
@@ -69,7 +70,8 @@ class StepArgs(ctypes.Structure):
     _fields_ = [("H", i32), ("d_h", i32), ("T_ctx", i32),
                 ("k_ctx", P), ("v_ctx", P), ("qx", P), ("q", P), ("k_new", P), ("v_new", P),
                 ("k_pool", P), ("v_pool", P), ("pool_blocks", i64), ("fresh_base", i64),
-                ("cross_out", P), ("self_out", P), ("tail", TailArgs)]
+                ("cross_out", P), ("self_out", P), ("tail", TailArgs),
+                ("attn_ws", P), ("attn_ws_bytes", sz)]
 
 
 _lib = None
@@ -99,6 +101,9 @@ def lib() -> ctypes.CDLL:
     L.gr_trie_destroy.argtypes = [P]
     L.gr_trie_destroy.restype = None
     L.gr_cross_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P]
+    L.gr_cross_attn_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    L.gr_cross_attn_workspace.restype = sz
+    L.gr_cross_attn_ws.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P, sz, P]
     L.gr_self_attn_paged.argtypes = [P, P, P, P, P, i64, P, i64, i32, i32, i32, i32, i32,
                                      ctypes.c_int, P, P]
     L.gr_joint_attn.argtypes = [P, P, P, P, P, P, P, i64, P, i64, i32, i32, i32, i32, i32, i32,
@@ -122,6 +127,7 @@ def lib() -> ctypes.CDLL:
     for name in EXPORTS:
         if name not in ("gr_last_error", "gr_version", "gr_trie_builder_destroy",
                         "gr_trie_destroy", "gr_constrain_topk_workspace",
+                        "gr_cross_attn_workspace",
                         "gr_decode_graph_destroy", "gr_ad_index_destroy"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L

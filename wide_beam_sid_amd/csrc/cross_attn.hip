@@ -53,6 +53,15 @@ struct JointArgs {
     int t, L;
 };
 
+// Split-K: the workgroup covers keys [k0, k1) only and leaves, for split s,
+// its unnormalised output (fp32) and the row's running max (scaled log2
+// units) and normaliser in po / pml, which k_cross_merge combines.
+struct SplitArgs {
+    int k0, k1, s, R;
+    float *po;    // [S, R, H, D]
+    float *pml;   // [S, R, H, 2]
+};
+
 // One workgroup = (request b, head h, 64 * RB beam rows); wavefront w takes
 // RB blocks of 16 rows.  The K / V tiles of 64 keys are double-buffered in
 // LDS: the global loads of tile i + 1 are in flight (in registers) while
@@ -67,13 +76,14 @@ struct JointArgs {
 // lanes of the row sum their parts, and the lane's output columns take the
 // weighted value; position t is the current token, which also goes to the
 // pool.  One output, no partial results leave the kernel.
-template <int D, int RB, bool JOINT, bool RAG>
+template <int D, int RB, bool JOINT, bool RAG, bool SPLIT = false>
 __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ K,
                                            const uint16_t *__restrict__ Vv,
                                            uint16_t *__restrict__ out, int M, int H, int T,
                                            float scale_log2, const JointArgs &jn, int bx, int h,
-                                           int b) {
+                                           int b, const SplitArgs &sp = SplitArgs{}) {
+    const int k0 = SPLIT ? sp.k0 : 0, k1 = SPLIT ? sp.k1 : T;   // keys of this workgroup
     constexpr int NDC = D / 32;   // k steps of S = Q K^T
     constexpr int NDB = D / 16;   // 16-wide blocks of d in O^T
     constexpr int ROWS = 4 * RB * 16;
@@ -167,7 +177,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         }
     };
 
-    load_tile(0);
+    load_tile(k0);
     // Q^T as the B operand: lane (g, a) holds Q[row a][c*32 + g*8 .. +8];
     // these loads stay in flight over the first tile's LDS stores and
     // barrier.
@@ -206,7 +216,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     // only loads in flight are the next tile's, holds its products for
     // them.
     auto key_tile = [&](int t0, int cur, bool first) {
-        const bool more = t0 + TT < T;
+        const bool more = t0 + TT < k1;
         if (first) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
         if (more) load_tile(t0 + TT);
 #pragma unroll
@@ -280,8 +290,8 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         if (more) store_tile(cur ^ 1);
         __syncthreads();
     };
-    key_tile(0, 0, true);
-    for (int t0 = TT, cur = 1; t0 < T; t0 += TT, cur ^= 1) key_tile(t0, cur, false);
+    key_tile(k0, 0, true);
+    for (int t0 = k0 + TT, cur = 1; t0 < k1; t0 += TT, cur ^= 1) key_tile(t0, cur, false);
 
     if constexpr (JOINT) {
 #pragma unroll
@@ -348,6 +358,22 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     }
 
     // Lane (g, a) holds O[row a][d = g*4*NDB + db*4 + i].
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float lt = pair32_sum(pair16_sum(lpart[rb]));
+            const int m = mbase + rb * 16 + a;
+            if (m >= M) continue;
+            const size_t rh = ((size_t)sp.s * sp.R + (size_t)b * M + m) * H + h;
+            float *dst = sp.po + rh * D + g * 4 * NDB;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                *(float4 *)(dst + db * 4) = make_float4(o[rb][db][0], o[rb][db][1], o[rb][db][2],
+                                                        o[rb][db][3]);
+            if (g == 0) *(float2 *)(sp.pml + rh * 2) = make_float2(mrow[rb], lt);
+        }
+        return;
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         float lt = lpart[rb];
@@ -390,6 +416,65 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
     const int tile = xcd_tile(blockIdx.x, n_tiles);
     const int bx = tile % gxc, rest = tile / gxc;
     cross_rows<D, RB, JOINT, RAG>(q, K, Vv, out, M, H, T, scale_log2, jn, bx, rest % H, rest / H);
+}
+
+// Split-K tiles: workgroup w takes tile-split x = xcd_tile(w, n) with the
+// split fastest (tile = x / S, split s = x mod S); split s covers keys
+// [s * Ts, min(T, (s + 1) * Ts)), Ts a multiple of the 64-key tile.  One
+// row block per wavefront: the split path serves launches with few tiles.
+template <int D, bool RAG>
+__global__ __launch_bounds__(256, 2) void k_cross_split(const uint16_t *__restrict__ q,
+                                                        const uint16_t *__restrict__ K,
+                                                        const uint16_t *__restrict__ Vv, int M,
+                                                        int H, int T, float scale_log2, int gxc,
+                                                        int n, int S, int Ts, int R,
+                                                        float *__restrict__ po,
+                                                        float *__restrict__ pml) {
+    const int x = xcd_tile(blockIdx.x, n);
+    const int tile = x / S, s = x - tile * S;
+    const int bx = tile % gxc, rest = tile / gxc;
+    SplitArgs sp;
+    sp.k0 = s * Ts;
+    sp.k1 = min(T, sp.k0 + Ts);
+    sp.s = s;
+    sp.R = R;
+    sp.po = po;
+    sp.pml = pml;
+    cross_rows<D, 1, false, RAG, true>(q, K, Vv, nullptr, M, H, T, scale_log2, JointArgs{}, bx,
+                                       rest % H, rest / H, sp);
+}
+
+// The S splits of one (row, head) combined with a log-sum-exp: with
+// c_s = 2^(m_s - max m), out = sum_s c_s o_s / sum_s c_s l_s, to bf16.
+// One wavefront per (row, head), D / 64 elements per lane (at least one).
+template <int D>
+__global__ __launch_bounds__(256) void k_cross_merge(const float *__restrict__ po,
+                                                     const float *__restrict__ pml,
+                                                     uint16_t *__restrict__ out, int RH, int S) {
+    constexpr int EPL = D >= 64 ? D / 64 : 1;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (w >= RH) return;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pml[((size_t)s * RH + w) * 2]);
+    float l = 0.0f, acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float2 ml = *(const float2 *)(pml + ((size_t)s * RH + w) * 2);
+        const float c = __builtin_amdgcn_exp2f(ml.x - mx);
+        l += c * ml.y;
+        const float *src = po + ((size_t)s * RH + w) * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            if (lane * EPL + e < D) acc[e] += c * src[lane * EPL + e];
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        if (lane * EPL + e < D) {
+            const uint32_t pk = cvt_bf16x2(acc[e] * inv, 0.0f);
+            out[(size_t)w * D + lane * EPL + e] = (uint16_t)(pk & 0xFFFFu);
+        }
 }
 
 // Cross- and self-attention of one decode step in one launch (they are
@@ -519,6 +604,52 @@ hipError_t launch_cross_tiles(const uint16_t *q, const uint16_t *k, const uint16
 }
 
 }  // namespace
+
+CrossSplit cross_split_plan(int B, int M, int H, int T, int d, gr_dtype dt) {
+    CrossSplit p{1, T, 0};
+    if (dt != GR_BF16 || (d != 32 && d != 64 && d != 128)) return p;
+    const int64_t n_tiles = (int64_t)((M + 63) / 64) * H * B;   // one row block per wavefront
+    const int nkt = (T + TT - 1) / TT;                           // 64-key tiles
+    // two workgroups per CU fill the chip at 512 tiles; below that a long
+    // key loop (8 tiles or more) is split so that about 1024 workgroups
+    // run, each over at least four key tiles (shorter splits lost to the
+    // extra merge launch: a 256-key context ran 1.5x slower split)
+    if (n_tiles >= 512 || nkt < 8) return p;
+    const int64_t want = (1024 + n_tiles - 1) / n_tiles;
+    const int S0 = (int)(want < nkt / 4 ? want : nkt / 4);
+    if (S0 < 2) return p;
+    const int tps = (nkt + S0 - 1) / S0;
+    const int Ts = tps * TT, S = (T + Ts - 1) / Ts;
+    if (S < 2) return p;
+    p.S = S;
+    p.Ts = Ts;
+    p.bytes = (size_t)S * B * M * H * (d + 2) * sizeof(float);
+    return p;
+}
+
+hipError_t launch_cross_split(const void *q, const void *k, const void *v, void *out, int B,
+                              int M, int H, int T, int d, const CrossSplit &pl, void *ws,
+                              hipStream_t s) {
+    const float sl2 = 1.4426950408889634f / sqrtf((float)d);
+    const int gxc = (M + 63) / 64, R = B * M, n = gxc * H * B * pl.S;
+    float *po = (float *)ws;
+    float *pml = po + (size_t)pl.S * R * H * d;
+    const bool rag = T % TT != 0;
+    const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
+#define GR_SPLIT(DD)                                                                            \
+    {                                                                                           \
+        if (rag) k_cross_split<DD, true><<<n, 256, 0, s>>>(qq, kk, vv, M, H, T, sl2, gxc, n,    \
+                                                           pl.S, pl.Ts, R, po, pml);            \
+        else k_cross_split<DD, false><<<n, 256, 0, s>>>(qq, kk, vv, M, H, T, sl2, gxc, n, pl.S, \
+                                                        pl.Ts, R, po, pml);                     \
+        k_cross_merge<DD><<<(R * H + 3) / 4, 256, 0, s>>>(po, pml, (uint16_t *)out, R * H, pl.S); \
+    }
+    if (d == 32) GR_SPLIT(32)
+    else if (d == 64) GR_SPLIT(64)
+    else GR_SPLIT(128)
+#undef GR_SPLIT
+    return hipGetLastError();
+}
 
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out, int B, int M,
                              int H, int T, int d, gr_dtype dt, hipStream_t s) {

@@ -998,6 +998,32 @@ gr_status gr_cross_attn(const void *q, const void *k_ctx, const void *v_ctx, voi
     return GR_OK;
 }
 
+size_t gr_cross_attn_workspace(int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
+                               gr_dtype dtype) {
+    if (B < 1 || M < 1 || H < 1 || T_ctx < 1 || d_h < 1) return 0;
+    return cross_split_plan(B, M, H, T_ctx, d_h, dtype).bytes;
+}
+
+gr_status gr_cross_attn_ws(const void *q, const void *k_ctx, const void *v_ctx, void *out,
+                           int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
+                           gr_dtype dtype, void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return gr_cross_attn(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, dtype, stream);
+    gr_status st = check_attn_common("gr_cross_attn_ws", B, M, H, d_h, dtype);
+    if (st) return st;
+    if (T_ctx < 1) return fail(GR_E_INVALID, "gr_cross_attn_ws: T_ctx %d < 1", T_ctx);
+    const CrossSplit pl = cross_split_plan(B, M, H, T_ctx, d_h, dtype);
+    if (pl.S < 2) return gr_cross_attn(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, dtype, stream);
+    if (!q || !k_ctx || !v_ctx || !out) return fail(GR_E_INVALID, "gr_cross_attn_ws: null pointer");
+    if ((int64_t)B * M * H > INT32_MAX) return fail(GR_E_INVALID, "gr_cross_attn_ws: too many rows");
+    if (ws_bytes < pl.bytes || ((uintptr_t)ws & 15))
+        return fail(GR_E_WORKSPACE, "gr_cross_attn_ws: workspace of %zu bytes (16-byte aligned) needed",
+                    pl.bytes);
+    hipError_t e = launch_cross_split(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, pl, ws,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gr_cross_attn_ws launch");
+    return GR_OK;
+}
+
 gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new,
                              void *k_pool, void *v_pool, int64_t pool_blocks,
                              int32_t *table, int64_t fresh_base, int32_t R, int32_t t,
@@ -1162,18 +1188,40 @@ static gr_status check_step(const gr_trie *trie, const gr_step_args *s) {
     const int vec = a.dtype == GR_BF16 ? 4 : 2;
     if (s->d_h % vec || (int64_t)s->H * s->d_h > 64 * vec * 16)
         return fail(GR_E_UNSUPPORTED, "gr_decode_step: H*d_h unsupported for self-attention");
+    if (s->attn_ws) {
+        const CrossSplit pl = cross_split_plan(a.B, a.M_in, s->H, s->T_ctx, s->d_h, a.dtype);
+        if (pl.S > 1 && (s->attn_ws_bytes < pl.bytes || ((uintptr_t)s->attn_ws & 15)))
+            return fail(GR_E_WORKSPACE, "gr_decode_step: attention workspace of %zu bytes needed",
+                        pl.bytes);
+    }
     return GR_OK;
 }
 
 static gr_status launch_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
     const gr_tail_args &a = s->tail;
     hipStream_t hs = (hipStream_t)stream;
-    // A1 and A2 are independent: one launch runs both
-    hipError_t e = launch_attn_pair(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H,
-                                    s->T_ctx, s->d_h, s->q, s->k_new, s->v_new, s->k_pool,
-                                    s->v_pool, s->pool_blocks, const_cast<int32_t *>(a.table_in),
-                                    s->fresh_base, a.t, a.L, a.dtype, s->self_out, hs);
-    if (e != hipSuccess) return hip_fail(e, "gr_decode_step attention launch");
+    hipError_t e = hipSuccess;
+    const CrossSplit pl = s->attn_ws
+                              ? cross_split_plan(a.B, a.M_in, s->H, s->T_ctx, s->d_h, a.dtype)
+                              : CrossSplit{1, s->T_ctx, 0};
+    if (pl.S > 1) {
+        // few tiles over a long context: the split cross-attention (and its
+        // merge), then the self-attention
+        e = launch_cross_split(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H,
+                               s->T_ctx, s->d_h, pl, s->attn_ws, hs);
+        if (e == hipSuccess)
+            e = launch_self_attn(s->q, s->k_new, s->v_new, s->k_pool, s->v_pool, s->pool_blocks,
+                                 const_cast<int32_t *>(a.table_in), s->fresh_base, a.B * a.M_in,
+                                 a.t, a.L, s->H, s->d_h, a.dtype, s->self_out, hs);
+        if (e != hipSuccess) return hip_fail(e, "gr_decode_step attention launch");
+    } else {
+        // A1 and A2 are independent: one launch runs both
+        e = launch_attn_pair(s->qx, s->k_ctx, s->v_ctx, s->cross_out, a.B, a.M_in, s->H, s->T_ctx,
+                             s->d_h, s->q, s->k_new, s->v_new, s->k_pool, s->v_pool,
+                             s->pool_blocks, const_cast<int32_t *>(a.table_in), s->fresh_base,
+                             a.t, a.L, a.dtype, s->self_out, hs);
+        if (e != hipSuccess) return hip_fail(e, "gr_decode_step attention launch");
+    }
     e = launch_constrain(trie->d, a, hs);
     if (e == hipSuccess) e = launch_topk_reorder(trie->d, a, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");

@@ -85,6 +85,19 @@ struct TailWsLayout {
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
 
+// Split-K plan of the bf16 cross-attention for a launch with few tiles and
+// a long key loop: S splits of Ts keys (S = 1: no split) and the workspace
+// bytes they need (S * B*M * H * (d + 2) floats).
+struct CrossSplit {
+    int S, Ts;
+    size_t bytes;
+};
+CrossSplit cross_split_plan(int B, int M, int H, int T, int d, gr_dtype dt);
+// The split tiles, then the log-sum-exp merge into out (bf16); ws holds
+// pl.bytes, 16-byte aligned.
+hipError_t launch_cross_split(const void *q, const void *k, const void *v, void *out, int B,
+                              int M, int H, int T, int d, const CrossSplit &pl, void *ws,
+                              hipStream_t s);
 hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *out,
                              int B, int M, int H, int T, int d, gr_dtype dt,
                              hipStream_t s);

@@ -11,8 +11,8 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import (DecodeGraph, StepArgs, Trie, _ptr, constrain_topk_workspace, decode_step,
-               tail_args)
+from . import (DecodeGraph, StepArgs, Trie, _ptr, constrain_topk_workspace, cross_attn_workspace,
+               decode_step, tail_args)
 from ._lib import GR_BF16, GR_F32
 
 
@@ -51,6 +51,12 @@ class Decoder:
         self.ws_bytes = max(constrain_topk_workspace(B, self.M[t], V, self.schedule[t])
                             for t in range(L))
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled once
+        # split cross-attention partials (steps with few tiles over a long
+        # context); no state between calls
+        self.attn_ws_bytes = max(cross_attn_workspace(B, self.M[t], H, T_ctx, d_h, dtype)
+                                 for t in range(L))
+        self.attn_ws = (torch.empty(self.attn_ws_bytes, dtype=torch.uint8, device=dev)
+                        if self.attn_ws_bytes else None)
         self.debug = debug
         words = (V + 63) // 64
         if debug:
@@ -79,6 +85,8 @@ class Decoder:
             dbg_mask=self.dbg_mask[t] if self.debug else None,
             dbg_scores=self.dbg_scores[t] if self.debug else None,
             ws=self.ws, ws_bytes=self.ws_bytes)
+        if self.attn_ws is not None:
+            a.attn_ws, a.attn_ws_bytes = _ptr(self.attn_ws), self.attn_ws_bytes
         return a
 
     def step(self, t: int, user_bm, user_probes, n_loc: int, k_ctx, v_ctx, inp: Dict,
