@@ -672,13 +672,22 @@ void k_expand(TailParams p) {
 #pragma unroll
                     for (int qq = 0; qq < MAX_KP / 4; ++qq)
                         if (qq * 4 < kp) {
+                            // the pads of the last group (copies of the
+                            // location's first probe) are not loaded again
+                            const int bk = p.bloom_k - qq * 4;   // real probes in this group
                             uint64_t c0[4], c1[4], c2[4], c3[4];
                             col4(tab + (size_t)pr0[qq].x * wc + w0, even, c0);
-                            col4(tab + (size_t)pr0[qq].y * wc + w0, even, c1);
-                            col4(tab + (size_t)pr0[qq].z * wc + w0, even, c2);
-                            col4(tab + (size_t)pr0[qq].w * wc + w0, even, c3);
+                            if (bk > 1) col4(tab + (size_t)pr0[qq].y * wc + w0, even, c1);
+                            if (bk > 2) col4(tab + (size_t)pr0[qq].z * wc + w0, even, c2);
+                            if (bk > 3) col4(tab + (size_t)pr0[qq].w * wc + w0, even, c3);
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) a[u] &= c0[u] & c1[u] & c2[u] & c3[u];
+                            for (int u = 0; u < 4; ++u) {
+                                uint64_t x = c0[u];
+                                if (bk > 1) x &= c1[u];
+                                if (bk > 2) x &= c2[u];
+                                if (bk > 3) x &= c3[u];
+                                a[u] &= x;
+                            }
                         }
                     if (lane < p.n_loc)
                         for (int q = MAX_KP; q < kp; q += 4) {   // probes past the registers
