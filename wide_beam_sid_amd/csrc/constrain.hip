@@ -379,6 +379,8 @@ void k_expand(TailParams p) {
     __shared__ uint32_t s_nsurv;                   // survivors written to the segment
     __shared__ int32_t s_slist[MAX_ROWS_WG];       // rows with a bit-sliced block
     __shared__ int s_nsl;
+    __shared__ int32_t s_sck[MAX_ROWS_WG];         // first chunk item of each listed row
+    __shared__ int s_nck;                          // chunk items over all listed rows
     __shared__ float s_ub[EXP_WAVES];
     __shared__ int s_nub;
     __shared__ int32_t s_lb[2 * EXP_THREADS];      // the round's Bloom rows awaiting eq 8
@@ -456,6 +458,13 @@ void k_expand(TailParams p) {
         const uint64_t sl = __ballot(lane < nrows && cnt > 0 && s_rblk[lane < nrows ? lane : 0] >= 0);
         if ((sl >> lane) & 1ull) s_slist[__popcll(sl & ((1ull << lane) - 1ull))] = lane;
         if (lane == 0) s_nsl = __popcll(sl);
+        // a listed row is processed in chunks of 4 column words (4 * 64
+        // children), one wavefront per chunk, so the chunks of a wide row
+        // run side by side; chunk items are numbered row by row
+        const int nck = ((sl >> lane) & 1ull) ? (((cnt + 63) >> 6) + 3) >> 2 : 0;
+        const int inc3 = (int)wave_incl_sum((uint32_t)nck);   // inclusive prefix over the lanes
+        if ((sl >> lane) & 1ull) s_sck[__popcll(sl & ((1ull << lane) - 1ull))] = inc3 - nck;
+        if (lane == 63) s_nck = inc3;
         // prefix over the rows without a block: their entries go through the rounds
         int inc2 = ((sl >> lane) & 1ull) ? 0 : cnt;
         inc2 = (int)wave_incl_sum((uint32_t)inc2);   // inclusive prefix over the lanes
@@ -599,14 +608,19 @@ void k_expand(TailParams p) {
     };
 
     // eqs 5 and 8 for every child of a node with a bit-sliced block, one
-    // wavefront per row.  Eq 5: AND of the columns of the user's attribute
-    // bits.  Eq 8: lane l ANDs the columns of location l's probe positions
-    // (bit j set = child j has all of them), then the lanes OR (ANY location).
+    // wavefront per chunk of 4 column words (256 children) of a row.  Eq 5:
+    // AND of the columns of the user's attribute bits.  Eq 8: lane l ANDs
+    // the columns of location l's probe positions (bit j set = child j has
+    // all of them), then the lanes OR (ANY location).
     if (p.wmax) {
         const int nub = s_nub, nsl = s_nsl;
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
         const int ub0 = nub ? s_ubit[lane < nub ? lane : 0] : 0;   // lane's user bit
-        for (int li = wave; li < nsl; li += EXP_WAVES) {
+        const int nitems = s_nck;
+        for (int it = wave; it < nitems; it += EXP_WAVES) {
+            int li = 0;   // the listed row of chunk item it, and its chunk ck
+            while (li + 1 < nsl && s_sck[li + 1] <= it) ++li;
+            const int ck = it - s_sck[li];
             const int i = s_slist[li];
             const int64_t blk = s_rblk[i];
             const int c = s_rstart[i + 1] - s_rstart[i];
@@ -649,7 +663,7 @@ void k_expand(TailParams p) {
                 if (lane == 0) s_pass[(size_t)i * p.wmax] = pass;
             } else {
             const bool even = (wc & 1) == 0;
-            for (int w0 = 0; w0 < wc; w0 += 4) {
+            for (int w0 = 4 * ck; w0 < min(wc, 4 * ck + 4); w0 += 4) {   // this chunk
                 const int n = min(4, wc - w0);
                 // every column load of the row first, the reductions after
                 uint64_t bm[4];
@@ -744,7 +758,7 @@ void k_expand(TailParams p) {
             const int off0 = s_roff[i], m = s_rm[i];
             const float acc = s_acc[i], lse = s_lse[i];
             const uint64_t *pw = s_pass + (size_t)i * p.wmax;
-            for (int u0 = 0; u0 < wc; u0 += 4) {
+            for (int u0 = 4 * ck; u0 < min(wc, 4 * ck + 4); u0 += 4) {   // this chunk
                 int tk[4], ch[4];
                 bool okc[4];
 #pragma unroll
