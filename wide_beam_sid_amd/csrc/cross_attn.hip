@@ -76,7 +76,7 @@ struct SplitArgs {
 // lanes of the row sum their parts, and the lane's output columns take the
 // weighted value; position t is the current token, which also goes to the
 // pool.  One output, no partial results leave the kernel.
-template <int D, int RB, bool JOINT, bool RAG, bool SPLIT = false>
+template <int D, int RB, bool JOINT, bool RAG, bool SPLIT = false, int NBUF = 2>
 __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ K,
                                            const uint16_t *__restrict__ Vv,
@@ -90,7 +90,13 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     constexpr int KIT = TT * (D / 8);              // 16-byte K pieces per tile
     constexpr int VIT = (TT / 2) * (D / 8);        // (key pair, 8 d) V pieces per tile
     constexpr int KU = (KIT + 255) / 256, VU = (VIT + 255) / 256;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][TT][D + PAD];
+    // NBUF = 2: double-buffered tiles.  NBUF = 1 (the standalone d_h = 128
+    // kernel): one buffer, 33 KB of LDS instead of 66 KB, so three
+    // workgroups fit a CU instead of two; the next tile's loads are still in
+    // flight (in registers) over the current tile's products, and one more
+    // barrier per tile guards the buffer before they are stored.
+    static_assert(NBUF == 1 || NBUF == 2, "tile buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TT][D + PAD];
     // V^T as key pairs, row d of TT / 2 dwords.  SWZ (one row block, short
     // key loops): the dword column is XORed with vsw(d), so the 16 rows a
     // 16-lane pass of the P.V product reads (d & 3 and d / (D / 4) varying)
@@ -99,7 +105,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     // long key loops.
     constexpr bool SWZ = RB == 1;
     constexpr int VP = TT / 2 + (SWZ ? 0 : PAD / 2);   // dwords per V^T row
-    __shared__ __attribute__((aligned(16))) uint32_t sVt[2][D][VP];
+    __shared__ __attribute__((aligned(16))) uint32_t sVt[NBUF][D][VP];
     static_assert(D == 32 || D == 64 || D == 128, "head size");
     constexpr int SHV = D == 32 ? 3 : (D == 64 ? 4 : 5);   // log2(D / 4)
     auto vsw = [](int d) { return SWZ ? 2 * ((d & 3) | (((d >> SHV) & 3) << 2)) : 0; };
@@ -217,6 +223,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     // them.
     auto key_tile = [&](int t0, int cur, bool first) {
         const bool more = t0 + TT < k1;
+        const int cb = NBUF == 1 ? 0 : cur;   // the buffer holding this tile
         if (first) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
         if (more) load_tile(t0 + TT);
 #pragma unroll
@@ -229,7 +236,7 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
 #pragma unroll
                 for (int c = 0; c < NDC; ++c) {
                     V8 ka;
-                    ka.u = *(const uint4 *)&sK[cur][kb * 16 + a][c * 32 + g * 8];
+                    ka.u = *(const uint4 *)&sK[cb][kb * 16 + a][c * 32 + g * 8];
                     s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[kb], 0, 0, 0);
                 }
             }
@@ -279,15 +286,18 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                 for (int db = 0; db < NDB; ++db) {
                     // A row a <-> d = (a/4)*4*NDB + db*4 + a%4
                     const int d = (a >> 2) * (4 * NDB) + db * 4 + (a & 3);
-                    const uint2 lo = *(const uint2 *)&sVt[cur][d][vc0 ^ (pc * 16)];
-                    const uint2 hi = *(const uint2 *)&sVt[cur][d][vc0 ^ (pc * 16 + 8)];
+                    const uint2 lo = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16)];
+                    const uint2 hi = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16 + 8)];
                     V8 va;
                     va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.b, pb.b, o[rb][db], 0, 0, 0);
                 }
             }
         }
-        if (more) store_tile(cur ^ 1);
+        if (more) {
+            if (NBUF == 1) __syncthreads();   // every wavefront is done with the buffer
+            store_tile(NBUF == 1 ? 0 : cur ^ 1);
+        }
         __syncthreads();
     };
     key_tile(k0, 0, true);
@@ -415,7 +425,8 @@ __global__ __launch_bounds__(256, 2) void k_cross_bf16(const uint16_t *__restric
                                                        int n_tiles, JointArgs jn) {
     const int tile = xcd_tile(blockIdx.x, n_tiles);
     const int bx = tile % gxc, rest = tile / gxc;
-    cross_rows<D, RB, JOINT, RAG>(q, K, Vv, out, M, H, T, scale_log2, jn, bx, rest % H, rest / H);
+    cross_rows<D, RB, JOINT, RAG, false, D == 128 ? 1 : 2>(q, K, Vv, out, M, H, T, scale_log2, jn,
+                                                          bx, rest % H, rest / H);
 }
 
 // Split-K tiles: workgroup w takes tile-split x = xcd_tile(w, n) with the
