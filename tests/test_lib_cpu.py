@@ -59,6 +59,17 @@ def test_argument_errors_return_codes_without_launch():
     # t outside [0, L)
     assert L.gr_self_attn_paged(buf, buf, buf, buf, buf, 100, buf, 0, 4, 4, 4, 2, 64, 1, buf,
                                 None) == _lib.GR_E_INVALID
+    # split cross-attention: a workspace smaller than the plan, or not
+    # 16-byte aligned, is refused before any launch
+    need = L.gr_cross_attn_workspace(8, 1, 16, 2048, 128, 1)
+    assert need > 0
+    ws = ctypes.c_void_p(256)
+    assert L.gr_cross_attn_ws(buf, buf, buf, buf, 8, 1, 16, 2048, 128, 1, ws, need - 16,
+                              None) == _lib.GR_E_WORKSPACE
+    assert L.gr_cross_attn_ws(buf, buf, buf, buf, 8, 1, 16, 2048, 128, 1, ctypes.c_void_p(264),
+                              need, None) == _lib.GR_E_WORKSPACE
+    assert L.gr_cross_attn_ws(None, buf, buf, buf, 8, 1, 16, 2048, 128, 1, ws, need,
+                              None) == _lib.GR_E_INVALID
     assert L.gr_bloom_probes(None, 3, 4096, 4, None) == _lib.GR_E_INVALID
     assert L.gr_bloom_probes(None, 0, 1000, 4, None) == _lib.GR_E_INVALID
     assert gr.constrain_topk_workspace(16, 1024, 256, 1024) > 16 * 1024 * 256 * 12
