@@ -121,6 +121,9 @@ SMALL = {
                                                         schedule=(16, 64, 130, 130)), 2),
     "long_small": (W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000, B=2, T_ctx=300,
                                                     schedule=(20, 300, 900)), 3),
+    # every step's cross-attention split over the 1024-token context
+    "long_split": (W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000, B=2, T_ctx=1000,
+                                                    schedule=(20, 300, 900)), 3),
     "stress_small": (W.WORKLOADS["stress_b64"].scaled(n_sids=20_000, B=2, geo_per_ad=(1, 64),
                                                       T_ctx=130, schedule=(64, 256, 512, 512)), 4),
 }

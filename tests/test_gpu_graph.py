@@ -27,6 +27,10 @@ CASES = {
                                                         schedule=(200, 300, 300, 300)), 1),
     "long_small": (W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000, B=2, T_ctx=300,
                                                     schedule=(20, 300, 900)), 3),
+    # a 1024-token context over few tiles: every step's cross-attention runs
+    # split over the context (its workspace is part of the step arguments)
+    "long_split": (W.WORKLOADS["longctx_b8"].scaled(n_sids=50_000, B=2, T_ctx=1024,
+                                                    schedule=(20, 300, 900)), 3),
 }
 
 
