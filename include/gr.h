@@ -17,10 +17,12 @@
  * Conventions (every entry point):
  *   - Device pointers are owned by the caller; the library never frees them.
  *     Host pointers are read during the call only (copied where kept).
- *   - Hot-path calls (gr_cross_attn, gr_self_attn_paged, gr_constrain_topk,
- *     gr_decode_step) never allocate and never synchronise the host: they
- *     validate, enqueue kernels on `stream` (a hipStream_t; NULL = the null
- *     stream) and return.
+ *   - Hot-path calls (gr_cross_attn, gr_cross_attn_ws, gr_self_attn_paged,
+ *     gr_joint_attn, gr_constrain_topk, gr_decode_step) never allocate and
+ *     never synchronise the host: they validate, enqueue kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and return.  Scratch memory
+ *     (the tail workspace, the split cross-attention workspace) is the
+ *     caller's.
  *   - Argument errors return GR_E_INVALID / GR_E_UNSUPPORTED /
  *     GR_E_WORKSPACE before anything is launched; a failed launch returns
  *     GR_E_HIP.  Faults inside kernels surface at the caller's next
