@@ -204,7 +204,10 @@ gr_status gr_bloom_probes(const int32_t *ids, int64_t n, int32_t bloom_bits,
  * row-major, dtype `dtype` (bf16: MFMA path, fp32 accumulation; f32: fp32
  * path).  No mask: every context token is valid.
  * Limits: bf16 needs d_h in {32, 64, 128}; f32 needs d_h <= 64; both need
- * B, M, H, T_ctx >= 1.  GR_E_INVALID / GR_E_UNSUPPORTED otherwise.
+ * B, M, H, T_ctx >= 1.  bf16 also needs one request's queries
+ * (M*H*d_h*2 bytes) and one head's context (T_ctx*d_h*2 bytes) below 2^32
+ * bytes (they are read through 32-bit buffer extents).
+ * GR_E_INVALID / GR_E_UNSUPPORTED otherwise.
  */
 gr_status gr_cross_attn(const void *q, const void *k_ctx, const void *v_ctx, void *out,
                         int32_t B, int32_t M, int32_t H, int32_t T_ctx, int32_t d_h,
@@ -244,8 +247,9 @@ gr_status gr_cross_attn_ws(const void *q, const void *k_ctx, const void *v_ctx, 
  * q, k_new, v_new, out [R, H, d_h]; k_pool, v_pool [pool_blocks, H, d_h];
  * table [R, L] int32 (columns < t read, column t written).  Device, dtype.
  * GR_E_INVALID if fresh_base + R > pool_blocks, t >= L, or shapes are bad;
- * GR_E_UNSUPPORTED if d_h is not a multiple of 4 (bf16) / 2 (f32) or
- * d_h > 256.
+ * GR_E_UNSUPPORTED unless d_h = vec * 2^j <= 64 * vec (vec = 4 for bf16,
+ * 2 for f32: a head's lanes form a power-of-two group) and
+ * H * d_h <= 1024 * vec.
  */
 gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new,
                              void *k_pool, void *v_pool, int64_t pool_blocks,
@@ -349,6 +353,15 @@ typedef struct {
 } gr_tail_args;
 
 size_t gr_constrain_topk_workspace(int32_t B, int32_t M_in, int32_t V, int32_t k_out);
+/*
+ * Launch shape of the tail for these sizes (informational; it sizes the
+ * workspace): the constrain stage runs gx workgroups per request, workgroup
+ * x taking the beam rows m = x + i * gx (i < rows_wg) and owning a survivor
+ * segment of seg_cap entries; gx <= 2048.  Host pointers; GR_E_INVALID for
+ * non-positive sizes or a NULL output.
+ */
+gr_status gr_constrain_topk_shape(int32_t B, int32_t M_in, int32_t V, int32_t *rows_wg,
+                                  int32_t *gx, int64_t *seg_cap);
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *args, void *stream);
 gr_status gr_constrain(const gr_trie *trie, const gr_tail_args *args, void *stream);
 gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *args, void *stream);
@@ -362,7 +375,8 @@ gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *args, void *s
  * gr_constrain_topk (tail) on one stream.  The caller chains steps
  * t = 0..L-1 with M_0 = 1, M_{t+1} = k_t, fresh_base_t = sum_{s<t} B*M_s,
  * ping-ponging the state buffers (node/acc/tokens/table).  Outputs cross_out
- * and self_out [B*M_in, H, d_h] are written for every row.
+ * and self_out [B*M_in, H, d_h] are written for every row.  The shape limits
+ * of gr_cross_attn and gr_self_attn_paged both apply (GR_E_UNSUPPORTED).
  */
 typedef struct {
     int32_t H, d_h, T_ctx;

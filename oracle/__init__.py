@@ -21,6 +21,11 @@ Parity status per function (pins live in tests/test_oracle_*.py):
                     Section 5.2, torch SDPA fp64 per row
   post.post_filter  pinned: hand-worked example, brute-force properties
                     (tests/test_oracle_post.py)
+  decode.step       pinned: the dense K/V history reorder against each beam's
+                    parent chain rebuilt independently, with brute-force
+                    self-attention per row (dead slots included); final
+                    scores = sum of per-step log-probs; finished SIDs in the
+                    catalog (tests/test_oracle_pins.py)
   joint_attn        pinned: no beam positions = cross_attn; the log-sum-exp
                     merge of the pinned cross_attn and self_attn results;
                     identical keys (mean of every value); q = 0

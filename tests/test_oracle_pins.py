@@ -420,3 +420,74 @@ def test_oracle_decode_invariants(seed):
         st = nxt
     final = {tuple(x) for x in st.tokens[st.live].tolist()}
     assert final and final <= catalog
+
+
+@pytest.mark.parametrize("seed", [0, 3, 7])
+def test_oracle_dense_history_follows_the_parent_chain(seed):
+    """The dense per-row K/V history the oracle reorders by copying parent
+    rows (the baseline that GRACE Section 3.3 replaces with a block table)
+    is rebuilt here by walking each beam's parent chain back through the
+    selections, with no state of the oracle's own: position j of a row at
+    step t holds the k / v its ancestor received at step j.  A dead slot has
+    no past, and the step's own token is always present.  The history rows,
+    their validity flags and every self-attention output (a softmax written
+    out here per row and head) must match."""
+    # widths above the root's 16 candidates leave dead slots at step 0
+    w = W.WORKLOADS["tiny_fp32"].scaled(B=2, schedule=(20, 24, 24))
+    sids = W.make_catalog(w, seed)
+    ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+    req = W.make_requests(w, seed)
+    ctx = W.make_context(w, seed)
+    ix = oracle.build_index(w, sids, ads)
+    st = initial_state(w)
+    parents, ks, vs = [], [], []
+    n_dead = 0
+    for t in range(w.L):
+        inp = W.make_step(w, seed, t)
+        ks.append(W.as_float(w, inp["k"]).astype(np.float64))
+        vs.append(W.as_float(w, inp["v"]).astype(np.float64))
+        q = W.as_float(w, inp["q"]).astype(np.float64)
+        out = step(w, ix, req, ctx, t, st, inp, lambda a: W.as_float(w, a))
+        R = w.rows(t)
+        for r in range(R):
+            # ancestors of row r at steps t-1, t-2, ..., 0 (None: no past)
+            rows_at = {t: r}
+            cur = r
+            for s in range(t - 1, -1, -1):
+                cur = parents[s][cur]
+                if cur < 0:
+                    rows_at = {t: r}
+                    break
+                rows_at[s] = cur
+            pos = sorted(rows_at)
+            if t > 0 and pos == [t]:
+                n_dead += 1
+            for h in range(w.H):
+                kk = np.stack([ks[j][rows_at[j], h] for j in pos])
+                vv = np.stack([vs[j][rows_at[j], h] for j in pos])
+                sc = kk @ q[r, h] / math.sqrt(w.d_h)
+                e = np.exp(sc - sc.max())
+                ref = (e[:, None] * vv).sum(axis=0) / e.sum()
+                assert np.abs(out.self_out[r, h] - ref).max() < 1e-12, (t, r, h)
+        parents.append(out.parent.copy())
+        # the history carried into step t + 1, rebuilt from the chain
+        nxt = out.next_state
+        for r2 in range(w.B * w.schedule[t]):
+            cur, chain = r2, {}
+            cur = parents[t][cur]
+            if cur < 0:
+                assert not nxt.hist_ok[r2].any() and not nxt.hist_k[r2].any(), (t, r2)
+                continue
+            chain[t] = cur
+            for s in range(t - 1, -1, -1):
+                cur = parents[s][cur]
+                chain[s] = cur
+            for j in range(w.L):
+                if j <= t:
+                    assert nxt.hist_ok[r2, j] == 1
+                    assert np.array_equal(nxt.hist_k[r2, j], ks[j][chain[j]]), (t, r2, j)
+                    assert np.array_equal(nxt.hist_v[r2, j], vs[j][chain[j]]), (t, r2, j)
+                else:
+                    assert nxt.hist_ok[r2, j] == 0
+        st = nxt
+    assert n_dead > 0   # dead slots were exercised

@@ -19,7 +19,8 @@ from ._lib import GR_BF16, GR_F32, GrError, StepArgs, TailArgs, TrieParams, Trie
 
 __all__ = [
     "GrError", "Trie", "bloom_probes", "cross_attn", "self_attn_paged", "joint_attn",
-    "constrain_topk_workspace", "constrain_topk", "constrain", "topk_reorder", "decode_step",
+    "constrain_topk_workspace", "constrain_topk_shape", "constrain_topk", "constrain",
+    "topk_reorder", "decode_step",
     "DecodeGraph", "AdIndex", "version",
 ]
 
@@ -227,6 +228,15 @@ def joint_attn(q, k_ctx, v_ctx, k_new, v_new, k_pool, v_pool, table, fresh_base:
 
 def constrain_topk_workspace(B: int, M_in: int, V: int, k_out: int) -> int:
     return int(_lib.lib().gr_constrain_topk_workspace(B, M_in, V, k_out))
+
+
+def constrain_topk_shape(B: int, M_in: int, V: int):
+    """(rows_wg, gx, seg_cap): the tail's expand workgroups per request, the
+    beam rows each takes and its survivor segment size."""
+    rw, gx, sc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _lib.check(_lib.lib().gr_constrain_topk_shape(B, M_in, V, ctypes.byref(rw), ctypes.byref(gx),
+                                                  ctypes.byref(sc)))
+    return rw.value, gx.value, sc.value
 
 
 def tail_args(**kw) -> TailArgs:

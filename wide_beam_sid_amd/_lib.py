@@ -23,7 +23,8 @@ EXPORTS = [
     "gr_trie_builder_destroy", "gr_trie_create", "gr_trie_host_view", "gr_trie_info",
     "gr_trie_destroy", "gr_cross_attn", "gr_cross_attn_workspace", "gr_cross_attn_ws",
     "gr_self_attn_paged", "gr_joint_attn",
-    "gr_constrain_topk_workspace", "gr_constrain_topk", "gr_constrain", "gr_topk_reorder",
+    "gr_constrain_topk_workspace", "gr_constrain_topk_shape", "gr_constrain_topk",
+    "gr_constrain", "gr_topk_reorder",
     "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
     "gr_decode_graph_destroy", "gr_ad_index_create", "gr_ad_index_add_ads",
     "gr_ad_index_finish", "gr_post_filter", "gr_ad_index_destroy",
@@ -110,6 +111,7 @@ def lib() -> ctypes.CDLL:
                                 i32, ctypes.c_int, P, P]
     L.gr_constrain_topk_workspace.argtypes = [i32, i32, i32, i32]
     L.gr_constrain_topk_workspace.restype = sz
+    L.gr_constrain_topk_shape.argtypes = [i32, i32, i32, P, P, P]
     L.gr_constrain_topk.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_constrain.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_topk_reorder.argtypes = [P, ctypes.POINTER(TailArgs), P]

@@ -1113,8 +1113,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         uint32_t spre = 0;
         for (int w = 0; w < wave; ++w) spre += s_wsum2[w];
         const uint32_t ex = spre + sinc - c0 - c1;
+        // thread tid writes entries 2 tid and 2 tid + 1; entry gx (the total)
+        // lies past the last thread's pair when gx = 2 * SEL_THREADS
         if (2 * tid <= gx) s_segpre[2 * tid] = ex;
         if (2 * tid + 1 <= gx) s_segpre[2 * tid + 1] = ex + c0;
+        if (gx == 2 * SEL_THREADS && tid == SEL_THREADS - 1) s_segpre[gx] = ex + c0 + c1;
     }
     float U = s_ub[0];
     for (int w = 1; w < SEL_THREADS / 64; ++w) U = fmaxf(U, s_ub[w]);
@@ -1159,7 +1162,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     if (tid == 0) s_ncl = 0u;
     __syncthreads();
     const int thr = s_thr, below = s_below;
-    const uint32_t n_surv = s_segpre[gx];
+    uint32_t n_surv = 0;   // the total of the segment counts
+    for (int w = 0; w < SEL_THREADS / 64; ++w) n_surv += s_wsum2[w];
     // offset of the f-th survivor (segments concatenated) in the request's keys
     auto surv = [&](uint32_t f) -> uint32_t {
         int lo = 0, hi = gx;

@@ -975,6 +975,37 @@ void gr_trie_destroy(gr_trie *t) {
 
 static bool dtype_ok(gr_dtype d) { return d == GR_F32 || d == GR_BF16; }
 
+// Shapes the self-attention kernels take: a head is d_h / vec pieces of
+// vec elements (4 bf16 or 2 fp32) spread over a power-of-two group of lanes,
+// whose dot products are summed by a butterfly over that group, and a row
+// of H * d_h elements fits 16 pieces on each of the 64 lanes.
+static gr_status check_self_shape(const char *fn, int H, int d, gr_dtype dt) {
+    const int vec = dt == GR_BF16 ? 4 : 2;
+    if (d % vec || d / vec > 64 || (d / vec & (d / vec - 1)))
+        return fail(GR_E_UNSUPPORTED, "%s: self-attention d_h %d unsupported for this dtype "
+                    "(a multiple of %d with d_h / %d a power of two <= 64)", fn, d, vec, vec);
+    if ((int64_t)H * d > 64 * vec * 16)
+        return fail(GR_E_UNSUPPORTED, "%s: H*d_h %lld too large for self-attention", fn,
+                    (long long)H * d);
+    return GR_OK;
+}
+
+// The bf16 cross-attention tiles read one request's queries and one
+// (request, head)'s context through buffer descriptors whose extent is a
+// 32-bit byte count: M*H*d_h and T_ctx*d_h bf16 values must stay below 2^32
+// bytes.
+static gr_status check_cross_extent(const char *fn, int M, int H, int T, int d, gr_dtype dt) {
+    if (dt != GR_BF16) return GR_OK;
+    const int64_t lim = (int64_t)1 << 32;
+    if ((int64_t)M * H * d * 2 >= lim)
+        return fail(GR_E_UNSUPPORTED, "%s: one request's queries (M*H*d_h = %lld bf16) exceed 2^32 bytes",
+                    fn, (long long)M * H * d);
+    if ((int64_t)T * d * 2 >= lim)
+        return fail(GR_E_UNSUPPORTED, "%s: one head's context (T_ctx*d_h = %lld bf16) exceeds 2^32 bytes",
+                    fn, (long long)T * d);
+    return GR_OK;
+}
+
 static gr_status check_attn_common(const char *fn, int B, int M, int H, int d, gr_dtype dt) {
     if (!dtype_ok(dt)) return fail(GR_E_INVALID, "%s: unknown dtype %d", fn, (int)dt);
     if (B < 1 || M < 1 || H < 1 || d < 1) return fail(GR_E_INVALID, "%s: non-positive shape", fn);
@@ -993,6 +1024,8 @@ gr_status gr_cross_attn(const void *q, const void *k_ctx, const void *v_ctx, voi
         return fail(GR_E_UNSUPPORTED, "gr_cross_attn: bf16 d_h %d not in {32, 64, 128}", d_h);
     if (dtype == GR_F32 && d_h > 64)
         return fail(GR_E_UNSUPPORTED, "gr_cross_attn: f32 d_h %d > 64", d_h);
+    st = check_cross_extent("gr_cross_attn", M, H, T_ctx, d_h, dtype);
+    if (st) return st;
     hipError_t e = launch_cross_attn(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_cross_attn launch");
     return GR_OK;
@@ -1015,6 +1048,8 @@ gr_status gr_cross_attn_ws(const void *q, const void *k_ctx, const void *v_ctx, 
     if (pl.S < 2) return gr_cross_attn(q, k_ctx, v_ctx, out, B, M, H, T_ctx, d_h, dtype, stream);
     if (!q || !k_ctx || !v_ctx || !out) return fail(GR_E_INVALID, "gr_cross_attn_ws: null pointer");
     if ((int64_t)B * M * H > INT32_MAX) return fail(GR_E_INVALID, "gr_cross_attn_ws: too many rows");
+    st = check_cross_extent("gr_cross_attn_ws", M, H, T_ctx, d_h, dtype);
+    if (st) return st;
     if (ws_bytes < pl.bytes || ((uintptr_t)ws & 15))
         return fail(GR_E_WORKSPACE, "gr_cross_attn_ws: workspace of %zu bytes (16-byte aligned) needed",
                     pl.bytes);
@@ -1037,11 +1072,8 @@ gr_status gr_self_attn_paged(const void *q, const void *k_new, const void *v_new
     if (fresh_base < 0 || pool_blocks < 0 || fresh_base + R > pool_blocks || fresh_base + R > INT32_MAX)
         return fail(GR_E_INVALID, "gr_self_attn_paged: blocks [%lld, %lld) exceed pool of %lld",
                     (long long)fresh_base, (long long)(fresh_base + R), (long long)pool_blocks);
-    const int vec = dtype == GR_BF16 ? 4 : 2;
-    if (d_h % vec || d_h / vec > 64 || (d_h / vec & (d_h / vec - 1)))
-        return fail(GR_E_UNSUPPORTED, "gr_self_attn_paged: d_h %d unsupported for this dtype", d_h);
-    if ((int64_t)H * d_h > 64 * vec * 16)
-        return fail(GR_E_UNSUPPORTED, "gr_self_attn_paged: H*d_h %d too large", H * d_h);
+    st = check_self_shape("gr_self_attn_paged", H, d_h, dtype);
+    if (st) return st;
     hipError_t e = launch_self_attn(q, k_new, v_new, k_pool, v_pool, pool_blocks, table, fresh_base, R, t, L, H, d_h,
                                     dtype, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_self_attn_paged launch");
@@ -1068,6 +1100,8 @@ gr_status gr_joint_attn(const void *q, const void *k_ctx, const void *v_ctx, con
         return fail(GR_E_UNSUPPORTED, "gr_joint_attn: bf16 d_h %d not in {32, 64, 128}", d_h);
     if (dtype == GR_F32 && d_h > 64)
         return fail(GR_E_UNSUPPORTED, "gr_joint_attn: f32 d_h %d > 64", d_h);
+    st = check_cross_extent("gr_joint_attn", M, H, T_ctx, d_h, dtype);
+    if (st) return st;
     hipError_t e = launch_joint_attn(q, k_ctx, v_ctx, k_new, v_new, k_pool, v_pool, pool_blocks, table,
                                      fresh_base, B, M, H, T_ctx, d_h, t, L, dtype, out,
                                      (hipStream_t)stream);
@@ -1103,6 +1137,17 @@ size_t gr_constrain_topk_workspace(int32_t B, int32_t M_in, int32_t V, int32_t k
     (void)k_out;
     if (B < 1 || M_in < 1 || V < 1) return 0;
     return tail_ws_layout(B, M_in, V).total;
+}
+
+gr_status gr_constrain_topk_shape(int32_t B, int32_t M_in, int32_t V, int32_t *rows_wg,
+                                  int32_t *gx, int64_t *seg_cap) {
+    if (B < 1 || M_in < 1 || V < 1 || !rows_wg || !gx || !seg_cap)
+        return fail(GR_E_INVALID, "gr_constrain_topk_shape: non-positive size or NULL output");
+    const TailShape sh = tail_shape(B, M_in, V);
+    *rows_wg = sh.rows_wg;
+    *gx = sh.gx;
+    *seg_cap = sh.seg_cap;
+    return GR_OK;
 }
 
 static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const char *fn) {
@@ -1169,32 +1214,33 @@ gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *st
 static gr_status check_step(const gr_trie *trie, const gr_step_args *s) {
     if (!trie || !s) return fail(GR_E_INVALID, "gr_decode_step: null argument");
     const gr_tail_args &a = s->tail;
-    gr_status st = check_tail(trie, &a, "gr_decode_step");
-    if (st) return st;
-    if (!a.table_in) return fail(GR_E_INVALID, "gr_decode_step: tail.table_in is NULL");
-    // Validate everything before the first launch.
-    st = check_attn_common("gr_decode_step", a.B, a.M_in, s->H, s->d_h, a.dtype);
+    // The attention shapes first (they need nothing from the trie), then the
+    // tail; everything is validated before the first launch.
+    gr_status st = check_attn_common("gr_decode_step", a.B, a.M_in, s->H, s->d_h, a.dtype);
     if (st) return st;
     if (!s->k_ctx || !s->v_ctx || !s->qx || !s->q || !s->k_new || !s->v_new || !s->k_pool ||
         !s->v_pool || !s->cross_out || !s->self_out)
         return fail(GR_E_INVALID, "gr_decode_step: null pointer");
-    const int R = a.B * a.M_in;
+    if ((int64_t)a.B * a.M_in > INT32_MAX) return fail(GR_E_INVALID, "gr_decode_step: too many rows");
+    const int64_t R = (int64_t)a.B * a.M_in;
     if (s->T_ctx < 1) return fail(GR_E_INVALID, "gr_decode_step: T_ctx < 1");
     if (a.dtype == GR_BF16 && s->d_h != 32 && s->d_h != 64 && s->d_h != 128)
         return fail(GR_E_UNSUPPORTED, "gr_decode_step: bf16 d_h %d not in {32, 64, 128}", s->d_h);
     if (a.dtype == GR_F32 && s->d_h > 64) return fail(GR_E_UNSUPPORTED, "gr_decode_step: f32 d_h > 64");
+    st = check_cross_extent("gr_decode_step", a.M_in, s->H, s->T_ctx, s->d_h, a.dtype);
+    if (st) return st;
+    st = check_self_shape("gr_decode_step", s->H, s->d_h, a.dtype);
+    if (st) return st;
     if (s->fresh_base < 0 || s->fresh_base + R > s->pool_blocks || s->fresh_base + R > INT32_MAX)
         return fail(GR_E_INVALID, "gr_decode_step: pool of %lld blocks too small", (long long)s->pool_blocks);
-    const int vec = a.dtype == GR_BF16 ? 4 : 2;
-    if (s->d_h % vec || (int64_t)s->H * s->d_h > 64 * vec * 16)
-        return fail(GR_E_UNSUPPORTED, "gr_decode_step: H*d_h unsupported for self-attention");
+    if (!a.table_in) return fail(GR_E_INVALID, "gr_decode_step: tail.table_in is NULL");
     if (s->attn_ws) {
         const CrossSplit pl = cross_split_plan(a.B, a.M_in, s->H, s->T_ctx, s->d_h, a.dtype);
         if (pl.S > 1 && (s->attn_ws_bytes < pl.bytes || ((uintptr_t)s->attn_ws & 15)))
             return fail(GR_E_WORKSPACE, "gr_decode_step: attention workspace of %zu bytes needed",
                         pl.bytes);
     }
-    return GR_OK;
+    return check_tail(trie, &a, "gr_decode_step");
 }
 
 static gr_status launch_step(const gr_trie *trie, const gr_step_args *s, void *stream) {
