@@ -9,6 +9,7 @@
 // of one-token blocks addressed through the block table P).
 #pragma once
 
+#include <cmath>
 #include <type_traits>
 
 #include "gr_device.h"
@@ -24,7 +25,7 @@ struct SelfParams {
     void *out;
     int64_t fresh_base, pool_blocks;
     int R, t, L, H, d, E, G, CB;
-    float scale;
+    float scale_log2;   // log2(e) / sqrt(d_h)
 };
 
 // CB-byte pieces of a row: 4 or 8 bf16, 2 or 4 fp32.
@@ -240,10 +241,14 @@ __device__ __forceinline__ void self_attn_rows(const SelfParams &p, int blk) {
                     for (int o2 = p.G >> 1; o2 > 0; o2 >>= 1) dot += __shfl_xor(dot, o2, 64);
                 }
                 if (skip) continue;
-                const float sc = dot * p.scale;
-                const float mn = fmaxf(mrun[c], sc);
-                const float alpha = __expf(mrun[c] - mn);
-                const float pe = __expf(sc - mn);
+                // The running max is taken over the raw dot products (the
+                // scale is positive) and the scale applied after the
+                // subtraction, which cannot contract into an FMA: the
+                // maximal position's weight is exp2(0) = 1 exactly, so one
+                // position returns its value unchanged.
+                const float mn = fmaxf(mrun[c], dot);
+                const float alpha = __builtin_amdgcn_exp2f((mrun[c] - mn) * p.scale_log2);
+                const float pe = __builtin_amdgcn_exp2f((dot - mn) * p.scale_log2);
                 lrun[c] = lrun[c] * alpha + pe;
 #pragma unroll
                 for (int x = 0; x < VEC; ++x) o[c][x] = o[c][x] * alpha + pe * vj[x];
@@ -287,7 +292,7 @@ inline SelfParams self_params(const void *q, const void *k_new, const void *v_ne
     p.H = H;
     p.d = d;
     p.E = H * d;
-    p.scale = 1.0f / sqrtf((float)d);
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     // 16-byte pieces when a head fills whole ones, else 8-byte pieces
     const int es = dt == GR_BF16 ? 2 : 4;
     p.CB = (d * es) % 16 == 0 ? 16 : 8;
