@@ -363,6 +363,24 @@ size_t gr_constrain_topk_workspace(int32_t B, int32_t M_in, int32_t V, int32_t k
 gr_status gr_constrain_topk_shape(int32_t B, int32_t M_in, int32_t V, int32_t *rows_wg,
                                   int32_t *gx, int64_t *seg_cap);
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *args, void *stream);
+/*
+ * gr_constrain_topk without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and outputs,
+ * with args->ws / ws_bytes ignored and the workspace taken from a scratch
+ * array of 128 MiB that the library holds on each device it runs on, until
+ * the process ends.  The call allocates nothing and frees nothing; it clears
+ * the scratch's score histograms of the B requests with a kernel on
+ * `stream`, then runs the tail.  Every call on one device shares that
+ * device's scratch: calls that may overlap on one device (different streams,
+ * threads or processes' graphs replayed concurrently) race and must be
+ * ordered by the caller.  GR_E_UNSUPPORTED when the shapes need more than
+ * 128 MiB (gr_constrain_topk_workspace(B, M_in, V, k_out) > 128 MiB, e.g.
+ * B * M_in * V beyond about 8.9 M candidates); otherwise the errors of
+ * gr_constrain_topk, with no GR_E_WORKSPACE.
+ */
+gr_status gr_constrain_topk_noalloc(const gr_trie *trie, const gr_tail_args *args,
+                                    void *stream);
 gr_status gr_constrain(const gr_trie *trie, const gr_tail_args *args, void *stream);
 gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *args, void *stream);
 

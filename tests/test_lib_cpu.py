@@ -332,3 +332,19 @@ def test_trie_create_validates_every_appendix_a_field():
         gr.Trie.create(base, **kw).close()
     except gr.GrError as e:
         assert e.status in (_lib.GR_E_HIP, _lib.GR_E_NOMEM), str(e)
+
+
+def test_noalloc_tail_refuses_shapes_beyond_its_scratch_before_any_launch():
+    """gr_constrain_topk_noalloc holds 128 MiB of scratch per device: larger
+    shapes are refused with GR_E_UNSUPPORTED before the trie or any device
+    state is touched; a fitting shape reaches the trie checks."""
+    L = _lib.lib()
+    t = gr.Trie.build(np.array([[0, 1]], np.int32), 4, 1, 0, 0, [], host_only=True)
+    big = gr.tail_args(B=64, M_in=1024, V=1024, k_out=1024, t=0, L=2, n_loc=0, dtype=0)
+    assert gr.constrain_topk_workspace(64, 1024, 1024, 1024) > (128 << 20)
+    assert L.gr_constrain_topk_noalloc(t.h, ctypes.byref(big), None) == _lib.GR_E_UNSUPPORTED
+    assert b"128" in L.gr_last_error() or b"scratch" in L.gr_last_error()
+    fits = gr.tail_args(B=32, M_in=1024, V=4, k_out=1024, t=0, L=2, n_loc=0, dtype=0)
+    assert L.gr_constrain_topk_noalloc(t.h, ctypes.byref(fits), None) == _lib.GR_E_INVALID
+    assert b"host_only" in L.gr_last_error()
+    assert L.gr_constrain_topk_noalloc(None, ctypes.byref(fits), None) == _lib.GR_E_INVALID

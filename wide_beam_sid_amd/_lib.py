@@ -24,6 +24,7 @@ EXPORTS = [
     "gr_trie_destroy", "gr_cross_attn", "gr_cross_attn_workspace", "gr_cross_attn_ws",
     "gr_self_attn_paged", "gr_joint_attn",
     "gr_constrain_topk_workspace", "gr_constrain_topk_shape", "gr_constrain_topk",
+    "gr_constrain_topk_noalloc",
     "gr_constrain", "gr_topk_reorder",
     "gr_decode_step", "gr_decode_graph_create", "gr_decode_graph_launch",
     "gr_decode_graph_destroy", "gr_ad_index_create", "gr_ad_index_add_ads",
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
     L.gr_constrain_topk_workspace.restype = sz
     L.gr_constrain_topk_shape.argtypes = [i32, i32, i32, P, P, P]
     L.gr_constrain_topk.argtypes = [P, ctypes.POINTER(TailArgs), P]
+    L.gr_constrain_topk_noalloc.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_constrain.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_topk_reorder.argtypes = [P, ctypes.POINTER(TailArgs), P]
     L.gr_decode_step.argtypes = [P, ctypes.POINTER(StepArgs), P]

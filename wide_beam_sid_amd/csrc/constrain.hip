@@ -30,6 +30,7 @@
 //              token / child node / score and the token and block-table rows
 //              of the new beams.
 #include <algorithm>
+#include <mutex>
 
 #include "gr_device.h"
 #include "gr_internal.h"
@@ -1500,6 +1501,53 @@ hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStre
     size_t shm = 0;
     const TailParams p = tail_params(tr, a, &shm);
     k_select<<<a.B, SEL_THREADS, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-held tail scratch for callers that cannot allocate: one file-scope
+// device array per GPU (each device that loads the library holds its own copy
+// until the process ends).  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// pointer is used.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[TAIL_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEV = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEV];   // device address of `scratch`, per device
+
+__global__ __launch_bounds__(256) void k_clear_u32x4(uint4 *p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t tail_scratch(void **out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr || ((uintptr_t)ptr & 255)) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_clear_hist(void *ws, int B, hipStream_t s) {
+    // the histogram region sits at offset 0 of the tail workspace layout
+    const size_t n = (size_t)B * NBINS * sizeof(uint32_t) / sizeof(uint4);
+    k_clear_u32x4<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((uint4 *)ws, n);
     return hipGetLastError();
 }
 

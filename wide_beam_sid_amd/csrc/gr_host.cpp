@@ -1150,7 +1150,8 @@ gr_status gr_constrain_topk_shape(int32_t B, int32_t M_in, int32_t V, int32_t *r
     return GR_OK;
 }
 
-static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const char *fn) {
+static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const char *fn,
+                            bool caller_ws = true) {
     if (!trie || !a) return fail(GR_E_INVALID, "%s: null argument", fn);
     if (trie->host_only) return fail(GR_E_INVALID, "%s: trie was built host_only", fn);
     const TrieDev &d = trie->d;
@@ -1178,6 +1179,7 @@ static gr_status check_tail(const gr_trie *trie, const gr_tail_args *a, const ch
     }
     if (a->tokens_out && a->t > 0 && !a->tokens_in) return fail(GR_E_INVALID, "%s: tokens_in is NULL", fn);
     if (a->table_out && !a->table_in) return fail(GR_E_INVALID, "%s: table_in is NULL", fn);
+    if (!caller_ws) return GR_OK;
     size_t need = tail_ws_layout(a->B, a->M_in, a->V).total;
     if (!a->ws || a->ws_bytes < need)
         return fail(GR_E_WORKSPACE, "%s: workspace %zu bytes < %zu required", fn, a->ws_bytes, need);
@@ -1207,6 +1209,35 @@ gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *st
     hipError_t e = launch_constrain(trie->d, *a, (hipStream_t)stream);
     if (e == hipSuccess) e = launch_topk_reorder(trie->d, *a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk launch");
+    return GR_OK;
+}
+
+gr_status gr_constrain_topk_noalloc(const gr_trie *trie, const gr_tail_args *a, void *stream) {
+    const char *fn = "gr_constrain_topk_noalloc";
+    if (!trie || !a) return fail(GR_E_INVALID, "%s: null argument", fn);
+    if (a->B >= 1 && a->M_in >= 1 && a->V >= 1) {
+        const size_t need = tail_ws_layout(a->B, a->M_in, a->V).total;
+        if (need > TAIL_SCRATCH_BYTES)
+            return fail(GR_E_UNSUPPORTED,
+                        "%s: B %d x M_in %d x V %d needs %zu bytes of tail scratch, more than the "
+                        "%zu the library holds per device (use gr_constrain_topk with a workspace)",
+                        fn, a->B, a->M_in, a->V, need, TAIL_SCRATCH_BYTES);
+    }
+    gr_status st = check_tail(trie, a, fn, false);
+    if (st) return st;
+    void *ws = nullptr;
+    hipError_t e = tail_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk_noalloc: scratch lookup");
+    gr_tail_args b = *a;
+    b.ws = ws;
+    b.ws_bytes = TAIL_SCRATCH_BYTES;
+    hipStream_t hs = (hipStream_t)stream;
+    // the scratch keeps the last call's contents: clear the histograms this
+    // call accumulates into (the rest is written before it is read)
+    e = launch_clear_hist(ws, b.B, hs);
+    if (e == hipSuccess) e = launch_constrain(trie->d, b, hs);
+    if (e == hipSuccess) e = launch_topk_reorder(trie->d, b, hs);
+    if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk_noalloc launch");
     return GR_OK;
 }
 

@@ -116,6 +116,13 @@ hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const 
                              int t, int L, gr_dtype dt, void *out, hipStream_t s);
 hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 
+// Tail scratch held by the library (gr_constrain_topk_noalloc): the device
+// address of this device's copy (looked up once per device), and a kernel
+// that zero-fills the score histograms of B requests in a workspace.
+constexpr size_t TAIL_SCRATCH_BYTES = (size_t)128 << 20;
+hipError_t tail_scratch(void **out);
+hipError_t launch_clear_hist(void *ws, int B, hipStream_t s);
+
 // Records msg as the message gr_last_error returns and returns st.
 gr_status report(gr_status st, const char *msg);
 hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
