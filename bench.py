@@ -300,27 +300,18 @@ def cpu_model() -> str:
     return platform.machine()
 
 
-def cpu_baseline(b: Bench, n_req: int, min_seconds: float = 10.0):
-    """The oracle's decodes of the first n_req requests (all L SID steps,
-    attention, masks, top-k, reorder), repeated on fresh step inputs until
-    about min_seconds of host time; index build excluded."""
-    import oracle
+def _oracle_decodes(b: Bench, ix, n_req: int, min_seconds: float, max_decodes: int):
+    """Whole oracle decodes (all L SID steps: attention, masks, top-k,
+    reorder) of the first n_req requests on fresh seeded step inputs, until
+    about min_seconds of host time; returns (beam rows, seconds, decodes)."""
     from oracle.decode import initial_state, step as oracle_step
     W, w = b.W, b.w
-    threads = min(16, len(os.sched_getaffinity(0)))
-    os.environ["OMP_NUM_THREADS"] = str(threads)
-    t0 = time.time()
-    ix = oracle.build_index(w, b.sids, b.ads)
-    log(f"[cpu] oracle index built ({time.time() - t0:.1f} s)")
     w1 = w.scaled(B=n_req)
     req = W.Requests(b.req.attrs[:n_req], b.req.user_bm[:n_req], b.req.locs[:n_req])
     kc, vc = W.make_context(w, b.seed)
     ctx = (kc[:n_req], vc[:n_req])
-    rows = 0
-    spent = 0.0
-    decodes = 0
-    # whole decodes of fresh seeded step inputs until about 10 s of CPU work
-    while decodes < 8 and (decodes == 0 or spent < min_seconds):
+    rows, spent, decodes = 0, 0.0, 0
+    while decodes < max_decodes and (decodes == 0 or spent < min_seconds):
         st = initial_state(w1)
         for t in range(w.L):
             full = W.make_step(w, b.seed + decodes, t)
@@ -332,13 +323,41 @@ def cpu_baseline(b: Bench, n_req: int, min_seconds: float = 10.0):
             rows += R1
             st = ref.next_state
         decodes += 1
-        log(f"[cpu] decode {decodes}: cumulative {spent:.2f} s")
-    return dict(value=rows / spent, unit="beam-rows/s", cores=threads, kind="oracle",
-                sample=(f"{decodes} decodes of the first {n_req} of {w.B} requests, all {w.L} "
-                        f"SID steps ({rows} beam rows): cross/self attention in fp64, CD+GTM "
-                        f"masks, log-softmax, top-k, reorder; index build excluded; "
-                        f"{spent:.1f} s on {cpu_model()}"),
-                seconds=spent)
+        log(f"[cpu] decode {decodes} of {n_req} requests: cumulative {spent:.2f} s")
+    return rows, spent, decodes
+
+
+def cpu_baseline(b: Bench, n_req: int, min_seconds: float = 10.0):
+    """The oracle's decodes of the first n_req requests (all L SID steps,
+    attention, masks, top-k, reorder), repeated on fresh step inputs until
+    about min_seconds of host time; index build excluded.  On the tiny and
+    main workloads a second, single-threaded run on a smaller sample is
+    reported beside it."""
+    import oracle
+    w = b.w
+    threads = min(16, len(os.sched_getaffinity(0)))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    oracle.set_threads(threads)
+    t0 = time.time()
+    ix = oracle.build_index(w, b.sids, b.ads)
+    log(f"[cpu] oracle index built ({time.time() - t0:.1f} s)")
+    rows, spent, decodes = _oracle_decodes(b, ix, n_req, min_seconds, 8)
+    res = dict(value=rows / spent, unit="beam-rows/s", cores=oracle.get_threads(), kind="oracle",
+               sample=(f"{decodes} decodes of the first {n_req} of {w.B} requests, all {w.L} "
+                       f"SID steps ({rows} beam rows): cross/self attention in fp64, CD+GTM "
+                       f"masks, log-softmax, top-k, reorder; index build excluded; "
+                       f"{spent:.1f} s on {cpu_model()}"),
+               seconds=spent)
+    if w.name in ("tiny_fp32", "main_b16_m1024"):
+        n1 = min(n_req, 2)
+        oracle.set_threads(1)
+        r1, s1, d1 = _oracle_decodes(b, ix, n1, min_seconds / 2, 4)
+        oracle.set_threads(threads)
+        res["single_thread"] = dict(
+            value=r1 / s1, unit="beam-rows/s", cores=1,
+            sample=(f"{d1} decodes of the first {n1} of {w.B} requests, all {w.L} SID steps "
+                    f"({r1} beam rows), one thread; {s1:.1f} s"))
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -432,8 +451,10 @@ def main():
         warm_elapsed = time.perf_counter() - t0w
 
         # The same decodes replayed as HIP graphs (one graph per input set,
-        # each capturing all L steps of gr_decode_step).
+        # each capturing all L steps of gr_decode_step).  A short spin kernel
+        # marks the start of the graph phase in a kernel trace.
         graphs = [b.gr.DecodeGraph(b.trie, b.args[s], stream) for s in range(args.sets)]
+        torch.cuda._sleep(1000)
         for i in range(args.warmup):
             graphs[i % args.sets].launch(stream)
         torch.cuda.synchronize()
@@ -442,6 +463,32 @@ def main():
             graphs[i % args.sets].launch(stream)
         torch.cuda.synchronize()
         graph_elapsed = time.perf_counter() - t0g
+        # Host cost of issuing one decode (queue far ahead of the GPU behind a
+        # spin kernel), and the latency of one decode issued alone and waited
+        # for, eager and as a graph.
+        def issue_cost(fn, n=40):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(100_000_000)
+            t0 = time.perf_counter()
+            for i in range(n):
+                fn(i)
+            dt = (time.perf_counter() - t0) / n
+            torch.cuda.synchronize()
+            return dt * 1e6
+        def sync_latency(fn, n=50):
+            lat = []
+            for i in range(n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn(i)
+                torch.cuda.synchronize()
+                lat.append((time.perf_counter() - t0) * 1e6)
+            return float(np.percentile(lat, 50))
+        eager_fn = lambda i: b.decode(i % args.sets)
+        graph_fn = lambda i: graphs[i % args.sets].launch(stream)
+        graph_host = dict(eager_issue_us=issue_cost(eager_fn), graph_issue_us=issue_cost(graph_fn),
+                          eager_sync_decode_p50_us=sync_latency(eager_fn),
+                          graph_sync_decode_p50_us=sync_latency(graph_fn))
         for g in graphs:
             g.close()
 
@@ -547,7 +594,7 @@ def main():
                             "decode_p99_us": float(np.percentile(dec_ms, 99)) * 1e3},
         "warm_value": rows_per_decode * args.steps / warm_elapsed,
         "graph": {"value": rows_per_decode * args.steps / graph_elapsed,
-                  "ms_per_step": graph_elapsed / args.steps * 1e3},
+                  "ms_per_step": graph_elapsed / args.steps * 1e3, **graph_host},
         "per_step": steps_tab,
         "roofline": roof,
         "cpu_baseline": None,

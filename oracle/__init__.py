@@ -90,8 +90,20 @@ def lib():
         L.orc_cross_attn.argtypes = [P, P, P, i32, i32, i32, i32, i32, P]
         L.orc_self_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, P]
         L.orc_joint_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
+        L.orc_get_threads.restype = i32
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops over rows (timing only)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
 
 
 def _p(a: np.ndarray):

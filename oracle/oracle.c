@@ -430,3 +430,18 @@ void orc_joint_attn(const double *q, const double *K, const double *Vv,
         free(s);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Threads of the loops over rows above (timing only: each row's arithmetic */
+/* is the same whatever the count).                                          */
+/* ------------------------------------------------------------------------ */
+#include <omp.h>
+void orc_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
+int orc_get_threads(void)
+{
+    return omp_get_max_threads();
+}

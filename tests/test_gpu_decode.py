@@ -1,20 +1,14 @@
 """Step-synced parity of the chained decode (gr_decode_step over all L steps)
-against the CPU oracle's walk of the same decode loop.
-
-Per step: masks, selected parents / tokens / scores and child nodes are
-bit-exact (top-k compared on the GPU's own fp32 scores), scores and attention
-outputs within tolerance, block table and KV pool checked structurally.  The
-oracle continues from the shared selection, so a near-tie cannot cascade.
+against the CPU oracle's walk of the same decode loop (tests/chain.py holds
+the per-step comparison).
 """
-import sys
 
 import numpy as np
 import pytest
 
-import oracle
-from oracle.decode import initial_state, step as oracle_step
 from synth import workload as W
-from tests.helpers import attn_close, to_dev, to_np64
+from tests.chain import ChainCheck
+from tests.helpers import to_dev
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -36,78 +30,20 @@ def run_chain(w, seed, sample_rows=None, mask_sample=None):
     req = W.make_requests(w, seed)
     kc, vc = W.make_context(w, seed)
     trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
-    view = trie.host_view()
-    ix = oracle.build_index(w, sids, ads)
-    npar, ntok, depth = view["node_parent"], view["node_token"], view["node_depth"]
+    chk = ChainCheck(w, seed, sids, ads, req, (kc, vc), trie.host_view(), sample_rows,
+                     mask_sample)
     probes = (gr.bloom_probes(req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
               if w.bloom_bits else np.zeros((1, 1), np.uint32))
     dec = Decoder(trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype, debug=True)
     ubm, upr = to_dev(req.user_bm), to_dev(probes)
     kct, vct = to_dev(kc, w.dtype), to_dev(vc, w.dtype)
-    st = initial_state(w)
-    rng = np.random.default_rng(seed)
-    as_f = lambda a: W.as_float(w, a)
     for t in range(w.L):
-        R = w.rows(t)
         inp = W.make_step(w, seed, t)
         dinp = {k: to_dev(v, w.dtype) for k, v in inp.items()}
         dec.step(t, ubm, upr if w.bloom_bits else None, w.n_loc, kct, vct, dinp)
         torch.cuda.synchronize()
-        scores = dec.dbg_scores[t].cpu().numpy()
-        rows = None
-        if sample_rows is not None and R > sample_rows:
-            rows = np.sort(rng.choice(R, size=sample_rows, replace=False))
-        gmask = dec.dbg_mask[t].cpu().numpy().view(np.uint64)
-        mrows = None
-        if mask_sample is not None and R > mask_sample:
-            mrows = np.sort(rng.choice(R, size=mask_sample, replace=False))
-        ref = oracle_step(w, ix, req, (kc, vc), t, st, inp, as_f, gpu_scores=scores,
-                          rows_subset=rows, mask_rows=mrows, given_mask=gmask)
-        # A3 mask (bit-exact on every row, or on the sampled rows), A4 scores
-        assert np.array_equal(gmask, ref.mask), f"mask t={t}"
-        fin = np.isfinite(ref.cand)
-        assert np.array_equal(np.isfinite(scores), fin), f"finite t={t}"
-        if fin.any():
-            err = np.abs(scores[fin] - ref.cand[fin])
-            assert (err <= 2e-5 + 2e-7 * np.abs(ref.cand[fin])).all(), f"scores t={t}: {err.max()}"
-        # A5 selection
-        parent = dec.parent[t].cpu().numpy()
-        token = dec.token[t].cpu().numpy()
-        assert np.array_equal(parent, ref.parent), f"parent t={t}"
-        assert np.array_equal(token, ref.token), f"token t={t}"
-        acc_out = dec.acc[t + 1].cpu().numpy()
-        k = w.schedule[t]
-        for b in range(w.B):
-            n = ref.sel_s[b].size
-            assert np.array_equal(acc_out[b * k:b * k + n].view(np.uint32), ref.sel_s[b].view(np.uint32))
-            assert np.isneginf(acc_out[b * k + n:(b + 1) * k]).all()
-        # A6 reorder: child nodes, token history, block table
-        live = parent >= 0
-        node_prev = dec.node[t].cpu().numpy()
-        node_out = dec.node[t + 1].cpu().numpy()
-        assert np.array_equal(npar[node_out[live]], node_prev[parent[live]])
-        assert np.array_equal(ntok[node_out[live]], token[live])
-        assert (depth[node_out[live]] == t + 1).all() and (node_out[~live] == -1).all()
-        tokens = dec.tokens[t + 1].cpu().numpy()
-        assert np.array_equal(tokens, ref.next_state.tokens), f"tokens t={t}"
-        tab_prev = dec.table[t].cpu().numpy()
-        tab = dec.table[t + 1].cpu().numpy()
-        assert np.array_equal(tab_prev[:, t], dec.fresh[t] + np.arange(R))
-        assert np.array_equal(tab[live, :t + 1], tab_prev[parent[live], :t + 1])
-        assert (tab[live, t + 1:] == -1).all() and (tab[~live] == -1).all()
-        # A2 pool write, A1/A2 outputs
-        kp = dec.k_pool[dec.fresh[t]:dec.fresh[t] + R].view(torch.int16 if w.dtype == "bf16" else torch.int32)
-        kin = inp["k"].view(np.int16) if w.dtype == "bf16" else inp["k"].view(np.int32)
-        assert np.array_equal(kp.cpu().numpy(), kin)
-        sel = slice(None) if rows is None else rows
-        attn_close(to_np64(dec.cross_out[t])[sel], ref.cross_out[sel], w.dtype, f"cross t={t}")
-        attn_close(to_np64(dec.self_out[t])[sel], ref.self_out[sel], w.dtype, f"self t={t}")
-        print(f"[chain] {w.name} t={t} R={R} live_out={int(live.sum())} ok", flush=True)
-        st = ref.next_state
-    final = dec.tokens[w.L].cpu().numpy()
-    live = dec.node[w.L].cpu().numpy() >= 0
-    catalog = {tuple(s) for s in sids.tolist()}
-    assert all(tuple(x) in catalog for x in final[live].tolist())
+        chk.check(dec, t, inp)
+    chk.check_final(dec)
     return dec
 
 

@@ -107,3 +107,55 @@ def test_decode_graph_replays_match_eager(name):
             torch.cuda.synchronize()
             print(f"[graph] {name} replay {rep} ok", flush=True)
         g.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "main_small", "long_split"])
+def test_decode_graph_replay_matches_oracle(name):
+    """The replayed graph itself against the CPU oracle, step by step (masks,
+    scores, selection, reorder, block table, pool, attention), on two
+    replays with eager work and scribbled outputs between them.  The split
+    case runs every step's cross-attention split over the 1024-token
+    context inside the graph."""
+    import wide_beam_sid_amd as gr
+    from wide_beam_sid_amd.runner import Decoder
+    from tests.chain import ChainCheck
+    w, seed = CASES[name]
+    print(f"[graph-oracle] {name} seed={seed} T_ctx={w.T_ctx}", flush=True)
+    sids = W.make_catalog(w, seed)
+    ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+    req = W.make_requests(w, seed)
+    kc, vc = W.make_context(w, seed)
+    trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
+    view = trie.host_view()
+    probes = (gr.bloom_probes(req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
+              if w.bloom_bits else np.zeros((1, 1), np.uint32))
+    ubm, upr = to_dev(req.user_bm), to_dev(probes)
+    kct, vct = to_dev(kc, w.dtype), to_dev(vc, w.dtype)
+    inp_np = [W.make_step(w, seed, t) for t in range(w.L)]
+    inputs = [{k: to_dev(v, w.dtype) for k, v in x.items()} for x in inp_np]
+    other = [{k: to_dev(v, w.dtype) for k, v in W.make_step(w, seed + 100, t).items()}
+             for t in range(w.L)]
+    args = (ubm, upr if w.bloom_bits else None, w.n_loc, kct, vct)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dec = Decoder(trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype, debug=True)
+        if name == "long_split":
+            assert dec.attn_ws is not None   # the split path is part of the graph
+        g = dec.graph(*args, inputs, stream)
+        eager = Decoder(trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype)
+        for rep in range(2):
+            _scribble(dec)
+            for t in range(dec.L):
+                dec.dbg_mask[t].fill_(-1)
+                dec.dbg_scores[t].fill_(5.0)
+            torch.cuda.synchronize()
+            g.launch(stream)
+            torch.cuda.synchronize()
+            chk = ChainCheck(w, seed, sids, ads, req, (kc, vc), view)
+            for t in range(w.L):
+                chk.check(dec, t, inp_np[t], later_steps_ran=True)
+            chk.check_final(dec)
+            eager.run(*args, other)
+            torch.cuda.synchronize()
+            print(f"[graph-oracle] {name} replay {rep} ok", flush=True)
+        g.close()
