@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "beam-rows/s per decode step at B16×M1024×L4; p99 step latency; % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+STREAM_SIDS = 4_000_000        # larger catalogs stream their ads into the index build
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
 
@@ -118,15 +119,24 @@ class Bench:
         dev = torch.device("cuda")
         t0 = time.time()
         sids = W.make_catalog(w, seed)
-        ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+        counts = W.ad_counts(w, seed)
         self.req = W.make_requests(w, seed)
-        log(f"[bench] workload {w.name}: {w.n_sids} SIDs, {ads.ad_sid.size} ads "
+        log(f"[bench] workload {w.name}: {w.n_sids} SIDs, {int(counts.sum())} ads "
             f"({time.time() - t0:.1f} s)")
         t0 = time.time()
-        self.trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads],
+        if w.n_sids > STREAM_SIDS:
+            # a large catalog's ads are streamed into the builder chunk by
+            # chunk (the stress catalog's geo lists alone are ~37 GB); the
+            # oracle's prefix tables, and so the CPU baseline, need them whole
+            ads = None
+            chunks = W.iter_ads(w, seed, counts, workers=8)
+        else:
+            ads = W.make_ads(w, seed, counts)
+            chunks = [ads]
+        self.trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, chunks,
                                   keep_host=True, bloom_slice_min=slice_min)
         self.slice_min = slice_min
-        self.view = self.trie.host_view()
+        self.view = self.trie.host_view(copy=False)
         log(f"[bench] trie {self.trie.info()} ({time.time() - t0:.1f} s)")
         self.sids, self.ads = sids, ads
         probes = (gr.bloom_probes(self.req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
@@ -335,6 +345,9 @@ def cpu_baseline(b: Bench, n_req: int, min_seconds: float = 10.0):
     reported beside it."""
     import oracle
     w = b.w
+    if b.ads is None:
+        raise SystemExit(f"cpu baseline: the {w.n_sids}-SID catalog is too large for the oracle's "
+                         "prefix tables; run with --cpu-requests 0")
     threads = min(16, len(os.sched_getaffinity(0)))
     os.environ["OMP_NUM_THREADS"] = str(threads)
     oracle.set_threads(threads)

@@ -26,6 +26,11 @@ Parity status per function (pins live in tests/test_oracle_*.py):
                     self-attention per row (dead slots included); final
                     scores = sum of per-step log-probs; finished SIDs in the
                     catalog (tests/test_oracle_pins.py)
+  SampledUnions     pinned: equals the prefix tables' rows (themselves pinned
+                    by brute force) on every sampled prefix of small catalogs
+  TrieAsData        pinned: masks equal mask_row's on every (prefix, request)
+                    of small catalogs, for a trie whose rows equal the prefix
+                    tables'; no false negatives by brute force
   joint_attn        pinned: no beam positions = cross_attn; the log-sum-exp
                     merge of the pinned cross_attn and self_attn results;
                     identical keys (mean of every value); q = 0
@@ -90,6 +95,18 @@ def lib():
         L.orc_cross_attn.argtypes = [P, P, P, i32, i32, i32, i32, i32, P]
         L.orc_self_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, P]
         L.orc_joint_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+        L.orc_usample_create.restype = P
+        L.orc_usample_create.argtypes = [i32, i32, i32, i32, i32, P, i64]
+        L.orc_usample_destroy.argtypes = [P]
+        L.orc_usample_destroy.restype = None
+        L.orc_usample_set_level.argtypes = [P, i32, P, i64]
+        L.orc_usample_set_level.restype = None
+        L.orc_usample_add_ads.argtypes = [P, i64, P, P, P, P]
+        L.orc_usample_add_ads.restype = None
+        L.orc_usample_rows.argtypes = [P, i32, P, P]
+        L.orc_usample_rows.restype = None
+        L.orc_mask_row_csr.restype = i32
+        L.orc_mask_row_csr.argtypes = [P, P, P, P, P, P, i32, P, i32, i32, P, i32, P, P, i32, P]
         L.orc_set_threads.argtypes = [i32]
         L.orc_set_threads.restype = None
         L.orc_get_threads.restype = i32
@@ -294,3 +311,94 @@ def joint_attn(q, K, Vv, hk, hv, valid, B: int, M: int) -> np.ndarray:
     out = np.empty_like(q)
     lib().orc_joint_attn(_p(q), _p(K), _p(Vv), _p(hk), _p(hv), _p(va), B, M, H, T, Tb, d, _p(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Large catalogs (too big for the prefix tables above): matcher unions of
+# sampled prefixes from the catalog and the ad stream, and the mask logic
+# applied to an Appendix A trie given as data.
+# ---------------------------------------------------------------------------
+
+def prefix_codes(sids: np.ndarray, level: int, V: int) -> np.ndarray:
+    """Base-V code t_1 V^(l-1) + ... + t_l of each SID's length-l prefix."""
+    code = np.zeros(sids.shape[0], np.int64)
+    for j in range(level):
+        code = code * V + sids[:, j].astype(np.int64)
+    return code
+
+
+class SampledUnions:
+    """bitmask(p) and bloom(p) (eqs 4 and 9) of chosen prefixes p, each the
+    OR over the ads of every catalog SID that starts with p."""
+
+    def __init__(self, w, sids: np.ndarray, samples: dict):
+        """samples: {level: sorted int64 prefix codes}."""
+        self._sids = _c(sids, np.int32)
+        self.w, self.samples = w, samples
+        self.h = lib().orc_usample_create(w.L, w.V, w.w_bm, w.bloom_bits, w.bloom_k,
+                                          _p(self._sids), self._sids.shape[0])
+        for level, codes in samples.items():
+            c = _c(codes, np.int64)
+            assert (np.diff(c) > 0).all()
+            lib().orc_usample_set_level(self.h, level, _p(c), c.size)
+
+    def add_ads(self, ad_sid, rules, geo_off, geo_ids):
+        a = _c(ad_sid, np.int64)
+        r = _c(rules, np.uint64)
+        go = _c(geo_off, np.int64)
+        gi = _c(geo_ids, np.int32) if len(geo_ids) else np.zeros(1, np.int32)
+        lib().orc_usample_add_ads(self.h, a.size, _p(a), _p(r), _p(go), _p(gi))
+
+    def rows(self, level: int):
+        n = self.samples[level].size
+        bm = np.zeros((max(n, 1), self.w.w_bm), np.uint64)
+        bl = np.zeros((max(n, 1), max(self.w.w_bl, 1)), np.uint64)
+        lib().orc_usample_rows(self.h, level, _p(bm), _p(bl))
+        return bm[:n], bl[:n, : self.w.w_bl]
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().orc_usample_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+
+class TrieAsData:
+    """The oracle's mask logic (Appendix A Lookup, eqs 5 and 8) over an
+    Appendix A trie given as arrays; the same mask_row / user_blooms
+    interface as Index, so the decode walk can use either."""
+
+    def __init__(self, w, arrays: dict):
+        self.w, self.V, self.L = w, w.V, w.L
+        self.w_bm, self.w_bl = w.w_bm, w.w_bl
+        self.bloom_bits, self.bloom_k = w.bloom_bits, w.bloom_k
+        self.a = {k: np.ascontiguousarray(arrays[k]) for k in
+                  ("node_offsets", "child_nodes", "tokens", "bitmask_index", "bitmask_table")}
+        if self.w_bl:
+            for k in ("bloom_index", "bloom_table"):
+                self.a[k] = np.ascontiguousarray(arrays[k])
+        assert self.a["tokens"].dtype == np.int16 and self.a["node_offsets"].dtype == np.int32
+
+    def user_blooms(self, user_locs) -> np.ndarray:
+        rows = np.zeros((max(len(user_locs), 1), max(self.w_bl, 1)), np.uint64)
+        if self.w_bl:
+            for j, g in enumerate(user_locs):
+                lib().orc_bloom_row(int(g), self.bloom_bits, self.bloom_k, _p(rows[j]))
+        return rows
+
+    def mask_row(self, prefix, t: int, user_bm, user_locs, blooms=None) -> np.ndarray:
+        a = self.a
+        out = np.zeros((self.V + 63) // 64, np.uint64)
+        p = _c(prefix if t > 0 else [0], np.int32)
+        ub = _c(user_bm, np.uint64)
+        bl = self.user_blooms(user_locs) if blooms is None else _c(blooms, np.uint64)
+        z = np.zeros(1, np.uint64)
+        lib().orc_mask_row_csr(_p(a["node_offsets"]), _p(a["child_nodes"]), _p(a["tokens"]),
+                               _p(a["bitmask_index"]),
+                               _p(a["bloom_index"]) if self.w_bl else None,
+                               _p(a["bitmask_table"]), self.w_bm,
+                               _p(a["bloom_table"]) if self.w_bl else _p(z), self.w_bl, self.V,
+                               _p(p), t, _p(ub), _p(bl), len(user_locs), _p(out))
+        return out

@@ -24,6 +24,7 @@
  * reading stated next to orc_bloom_positions.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -435,7 +436,6 @@ void orc_joint_attn(const double *q, const double *K, const double *Vv,
 /* Threads of the loops over rows above (timing only: each row's arithmetic */
 /* is the same whatever the count).                                          */
 /* ------------------------------------------------------------------------ */
-#include <omp.h>
 void orc_set_threads(int n)
 {
     if (n > 0) omp_set_num_threads(n);
@@ -444,4 +444,171 @@ void orc_set_threads(int n)
 int orc_get_threads(void)
 {
     return omp_get_max_threads();
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* Large catalogs: matcher unions of sampled prefixes (eqs 4 and 9), built  */
+/* from the catalog and the ad stream directly.  For each level l the       */
+/* caller names the prefixes to sample by their base-V code                 */
+/* (t_1 * V^(l-1) + ... + t_l), sorted; every ad whose SID starts with a     */
+/* sampled prefix ORs its rule words and the Bloom positions of its geo ids  */
+/* into that prefix's rows.  Ads can be added in any number of calls.        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int L, V, w_bm, w_bl, bloom_bits, bloom_k;
+    const int32_t *sids;     /* [n_sids, L], the caller's (kept alive by it) */
+    int64_t n_sids;
+    int64_t n[17];           /* sampled prefixes per level                   */
+    int64_t *code[17];       /* [n_l] sorted base-V codes                    */
+    uint64_t *bm[17];        /* [n_l, w_bm]                                  */
+    uint64_t *bl[17];        /* [n_l, w_bl]                                  */
+} orc_usample;
+
+orc_usample *orc_usample_create(int L, int V, int w_bm, int bloom_bits, int bloom_k,
+                                const int32_t *sids, int64_t n_sids)
+{
+    if (L < 1 || L > 16) return NULL;
+    orc_usample *u = (orc_usample *)calloc(1, sizeof(orc_usample));
+    u->L = L; u->V = V; u->w_bm = w_bm; u->bloom_bits = bloom_bits;
+    u->bloom_k = bloom_k; u->w_bl = bloom_bits / 64;
+    u->sids = sids; u->n_sids = n_sids;
+    return u;
+}
+
+void orc_usample_destroy(orc_usample *u)
+{
+    if (!u) return;
+    for (int l = 0; l <= 16; l++) { free(u->code[l]); free(u->bm[l]); free(u->bl[l]); }
+    free(u);
+}
+
+void orc_usample_set_level(orc_usample *u, int level, const int64_t *codes, int64_t n)
+{
+    free(u->code[level]); free(u->bm[level]); free(u->bl[level]);
+    u->n[level] = n;
+    u->code[level] = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n ? n : 1));
+    memcpy(u->code[level], codes, sizeof(int64_t) * (size_t)n);
+    u->bm[level] = (uint64_t *)calloc((size_t)(n ? n : 1) * u->w_bm, sizeof(uint64_t));
+    u->bl[level] = (uint64_t *)calloc((size_t)(n ? n : 1) * (u->w_bl ? u->w_bl : 1),
+                                      sizeof(uint64_t));
+}
+
+static int64_t find_code(const int64_t *a, int64_t n, int64_t key)
+{
+    int64_t lo = 0, hi = n;            /* plain binary search */
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if (a[mid] < key) lo = mid + 1;
+        else hi = mid;
+    }
+    return (lo < n && a[lo] == key) ? lo : -1;
+}
+
+void orc_usample_add_ads(orc_usample *u, int64_t n_ads, const int64_t *ad_sid,
+                         const uint64_t *rules, const int64_t *geo_off, const int32_t *geo_ids)
+{
+    const int L = u->L, wbm = u->w_bm, wbl = u->w_bl;
+    const int nt = omp_get_max_threads();
+    /* each thread ORs into rows of its own; the rows are merged at the end */
+    int64_t tot_bm = 0, tot_bl = 0, base_bm[17], base_bl[17];
+    for (int l = 1; l <= L; l++) {
+        base_bm[l] = tot_bm; base_bl[l] = tot_bl;
+        tot_bm += u->n[l] * wbm; tot_bl += u->n[l] * wbl;
+    }
+    uint64_t *pbm = (uint64_t *)calloc((size_t)nt * (tot_bm ? tot_bm : 1), sizeof(uint64_t));
+    uint64_t *pbl = (uint64_t *)calloc((size_t)nt * (tot_bl ? tot_bl : 1), sizeof(uint64_t));
+    #pragma omp parallel num_threads(nt)
+    {
+        const int th = omp_get_thread_num();
+        uint64_t *mbm = pbm + (size_t)th * tot_bm;
+        uint64_t *mbl = pbl + (size_t)th * tot_bl;
+        uint32_t pos[64];
+        int64_t hit[17];
+        #pragma omp for schedule(dynamic, 4096)
+        for (int64_t a = 0; a < n_ads; a++) {
+            const int32_t *sid = u->sids + (size_t)ad_sid[a] * L;
+            int64_t code = 0;
+            int any = 0;
+            for (int l = 1; l <= L; l++) {
+                code = code * u->V + sid[l - 1];
+                hit[l] = u->n[l] ? find_code(u->code[l], u->n[l], code) : -1;
+                if (hit[l] >= 0) any = 1;
+            }
+            if (!any) continue;
+            for (int l = 1; l <= L; l++) {
+                if (hit[l] < 0) continue;
+                uint64_t *r = mbm + base_bm[l] + hit[l] * wbm;
+                for (int q = 0; q < wbm; q++) r[q] |= rules[a * wbm + q];
+            }
+            if (!wbl) continue;
+            for (int64_t j = geo_off[a]; j < geo_off[a + 1]; j++) {
+                orc_bloom_positions(geo_ids[j], u->bloom_bits, u->bloom_k, pos);
+                for (int l = 1; l <= L; l++) {
+                    if (hit[l] < 0) continue;
+                    uint64_t *r = mbl + base_bl[l] + hit[l] * wbl;
+                    for (int i = 0; i < u->bloom_k; i++) r[pos[i] / 64] |= 1ULL << (pos[i] % 64);
+                }
+            }
+        }
+    }
+    for (int l = 1; l <= L; l++) {
+        const int64_t nbm = u->n[l] * wbm, nbl = u->n[l] * wbl;
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < nbm; i++)
+            for (int th = 0; th < nt; th++) u->bm[l][i] |= pbm[(size_t)th * tot_bm + base_bm[l] + i];
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < nbl; i++)
+            for (int th = 0; th < nt; th++) u->bl[l][i] |= pbl[(size_t)th * tot_bl + base_bl[l] + i];
+    }
+    free(pbm);
+    free(pbl);
+}
+
+void orc_usample_rows(const orc_usample *u, int level, uint64_t *bm, uint64_t *bl)
+{
+    memcpy(bm, u->bm[level], sizeof(uint64_t) * (size_t)u->n[level] * u->w_bm);
+    if (u->w_bl) memcpy(bl, u->bl[level], sizeof(uint64_t) * (size_t)u->n[level] * u->w_bl);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Appendix A Lookup over a trie given as data (the Appendix A arrays of an */
+/* index built elsewhere): follow the row's prefix from the root through    */
+/* the child entries of each node (a linear scan for the token), then keep  */
+/* token tok[e] of each child entry e of the reached node when eq 5 holds   */
+/* for its bitmask row and, with Bloom rows, eq 8 holds for one of the      */
+/* user's locations.  t < 0, or a prefix the trie does not hold, gives an   */
+/* all-zero mask (a dead row).  Returns the number of kept tokens.          */
+/* ------------------------------------------------------------------------ */
+int orc_mask_row_csr(const int32_t *off, const int32_t *child, const int16_t *tok,
+                     const int32_t *bmi, const int32_t *bli, const uint64_t *bm_tab, int w_bm,
+                     const uint64_t *bl_tab, int w_bl, int V, const int32_t *prefix, int t,
+                     const uint64_t *user_bm, const uint64_t *user_blooms, int n_loc,
+                     uint64_t *out)
+{
+    memset(out, 0, sizeof(uint64_t) * (size_t)((V + 63) / 64));
+    if (t < 0) return 0;
+    int64_t node = 0;
+    for (int j = 0; j < t; j++) {
+        int64_t next = -1;
+        for (int32_t e = off[node]; e < off[node + 1]; e++)
+            if (tok[e] == prefix[j]) { next = child[e]; break; }
+        if (next < 0) return 0;
+        node = next;
+    }
+    int kept = 0;
+    for (int32_t e = off[node]; e < off[node + 1]; e++) {
+        if (!orc_bitmask_match(bm_tab + (size_t)bmi[e] * w_bm, user_bm, w_bm)) continue;
+        int bl_ok = 1;
+        if (w_bl) {
+            bl_ok = 0;
+            const uint64_t *row = bl_tab + (size_t)bli[e] * w_bl;
+            for (int l = 0; l < n_loc && !bl_ok; l++)
+                bl_ok = orc_bloom_contains(row, user_blooms + (size_t)l * w_bl, w_bl);
+        }
+        if (!bl_ok) continue;
+        out[tok[e] / 64] |= 1ULL << (tok[e] % 64);
+        kept++;
+    }
+    return kept;
 }

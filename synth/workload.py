@@ -203,8 +203,10 @@ def ad_counts(w: Workload, seed: int) -> np.ndarray:
 
 def _rules(w: Workload, g: np.random.Generator, n: int) -> np.ndarray:
     """Per-ad rule words u64 [n, w_bm]: each attribute segment's bits are
-    Bernoulli(bm_p); an empty segment is redrawn so every ad is satisfiable."""
-    words = np.zeros((n, w.w_bm), dtype=np.uint64)
+    Bernoulli(bm_p); an empty segment is redrawn so every ad is satisfiable.
+    Bit b of the rule (segments laid out in order) is bit b % 64 of word
+    b // 64."""
+    bits = np.zeros((n, 64 * w.w_bm), dtype=bool)
     base = 0
     for width in w.bm_segments:
         seg = g.random((n, width)) < w.bm_p
@@ -212,11 +214,10 @@ def _rules(w: Workload, g: np.random.Generator, n: int) -> np.ndarray:
         while empty.any():
             seg[empty] = g.random((int(empty.sum()), width)) < w.bm_p
             empty = ~seg.any(axis=1)
-        for j in range(width):
-            bit = base + j
-            words[:, bit // 64] |= seg[:, j].astype(np.uint64) << np.uint64(bit % 64)
+        bits[:, base:base + width] = seg
         base += width
-    return words
+    packed = np.packbits(bits, axis=1, bitorder="little")      # byte j holds bits 8j..8j+7
+    return np.ascontiguousarray(packed).view("<u8").astype(np.uint64, copy=False)
 
 
 @dataclass
@@ -230,35 +231,61 @@ class AdChunk:
     geo_ids: np.ndarray       # int32 [geo_offsets[-1]]
 
 
+def _ad_chunk(w: Workload, seed: int, counts: np.ndarray, c: int, s0: int, s1: int,
+              first_ad: int) -> AdChunk:
+    cnt = counts[s0:s1]
+    n = int(cnt.sum())
+    ad_sid = np.repeat(np.arange(s0, s1, dtype=np.int64), cnt)
+    rules = _rules(w, rng(seed, S_AD_RULES, c), n)
+    if w.bloom_bits:
+        g = rng(seed, S_AD_GEO, c)
+        lo, hi = w.geo_per_ad
+        ng = g.integers(lo, hi + 1, size=n, dtype=np.int64)
+        offs = np.zeros(n + 1, dtype=np.int64)
+        np.cumsum(ng, out=offs[1:])
+        geo = g.integers(0, w.geo_pool, size=int(offs[-1]), dtype=np.int32)
+    else:
+        offs = np.zeros(n + 1, dtype=np.int64)
+        geo = np.zeros(0, dtype=np.int32)
+    return AdChunk(first_ad, ad_sid, rules, offs, geo)
+
+
 def iter_ads(w: Workload, seed: int, counts: np.ndarray,
-             sids_per_chunk: int = 1 << 18) -> Iterator[AdChunk]:
+             sids_per_chunk: int = 1 << 18, workers: int = 1) -> Iterator[AdChunk]:
     """Stream the ads of SIDs in catalog order, chunk by chunk.
 
     Chunk c covers SIDs [c*sids_per_chunk, (c+1)*sids_per_chunk); its rules and
-    geo lists come from sub-streams keyed by c, so it can be regenerated alone.
-    Geo ids are drawn with replacement from the pool (a list with a repeated id
-    is the same allow-set).
+    geo lists come from sub-streams keyed by c, so it can be regenerated alone
+    (and ``workers`` threads draw the next chunks while the caller consumes
+    one; the chunks and their order do not depend on it).  Geo ids are drawn
+    with replacement from the pool (a list with a repeated id is the same
+    allow-set).
     """
     n_sids = counts.size
-    first_ad = 0
-    for c, s0 in enumerate(range(0, n_sids, sids_per_chunk)):
-        s1 = min(n_sids, s0 + sids_per_chunk)
-        cnt = counts[s0:s1]
-        n = int(cnt.sum())
-        ad_sid = np.repeat(np.arange(s0, s1, dtype=np.int64), cnt)
-        rules = _rules(w, rng(seed, S_AD_RULES, c), n)
-        if w.bloom_bits:
-            g = rng(seed, S_AD_GEO, c)
-            lo, hi = w.geo_per_ad
-            ng = g.integers(lo, hi + 1, size=n, dtype=np.int64)
-            offs = np.zeros(n + 1, dtype=np.int64)
-            np.cumsum(ng, out=offs[1:])
-            geo = g.integers(0, w.geo_pool, size=int(offs[-1]), dtype=np.int32)
-        else:
-            offs = np.zeros(n + 1, dtype=np.int64)
-            geo = np.zeros(0, dtype=np.int32)
-        yield AdChunk(first_ad, ad_sid, rules, offs, geo)
-        first_ad += n
+    starts = list(range(0, n_sids, sids_per_chunk))
+    firsts = np.concatenate([[0], np.cumsum([int(counts[s0:s0 + sids_per_chunk].sum())
+                                              for s0 in starts])])
+    jobs = [(c, s0, min(n_sids, s0 + sids_per_chunk), int(firsts[c]))
+            for c, s0 in enumerate(starts)]
+    if workers <= 1:
+        for c, s0, s1, fa in jobs:
+            yield _ad_chunk(w, seed, counts, c, s0, s1, fa)
+        return
+    from collections import deque
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = deque()
+        it = iter(jobs)
+        for job in it:
+            pending.append(ex.submit(_ad_chunk, w, seed, counts, *job))
+            if len(pending) >= workers:
+                break
+        while pending:
+            ch = pending.popleft().result()
+            for job in it:
+                pending.append(ex.submit(_ad_chunk, w, seed, counts, *job))
+                break
+            yield ch
 
 
 def make_ads(w: Workload, seed: int, counts: np.ndarray) -> AdChunk:

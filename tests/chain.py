@@ -18,10 +18,14 @@ from tests.helpers import attn_close, to_np64
 class ChainCheck:
     """The oracle's side of one decode of workload ``w`` (seed ``seed``)."""
 
-    def __init__(self, w, seed, sids, ads, req, ctx, view, sample_rows=None, mask_sample=None):
+    def __init__(self, w, seed, sids, ads, req, ctx, view, sample_rows=None, mask_sample=None,
+                 ix=None):
+        """``ix``: the oracle's mask source (default: its prefix tables built
+        from ``sids`` and ``ads``; for large catalogs, ``oracle.TrieAsData``
+        over a trie whose rows were verified on sampled prefixes)."""
         self.w, self.seed, self.req, self.ctx = w, seed, req, ctx
         self.view = view
-        self.ix = oracle.build_index(w, sids, ads)
+        self.ix = oracle.build_index(w, sids, ads) if ix is None else ix
         self.sids = sids
         self.st = initial_state(w)
         self.rng = np.random.default_rng(seed)
@@ -93,11 +97,16 @@ class ChainCheck:
         sel = slice(None) if rows is None else rows
         attn_close(to_np64(dec.cross_out[t])[sel], ref.cross_out[sel], w.dtype, f"cross t={t}")
         attn_close(to_np64(dec.self_out[t])[sel], ref.self_out[sel], w.dtype, f"self t={t}")
-        print(f"[chain] {w.name} t={t} R={R} live_out={int(live.sum())} ok", flush=True)
+        from tests.large import progress
+        progress(f"[chain] {w.name} t={t} R={R} live_out={int(live.sum())} ok")
         self.st = ref.next_state
 
     def check_final(self, dec):
-        final = dec.tokens[self.w.L].cpu().numpy()
-        live = dec.node[self.w.L].cpu().numpy() >= 0
-        catalog = {tuple(s) for s in self.sids.tolist()}
-        assert all(tuple(x) in catalog for x in final[live].tolist())
+        """Every finished SID of a live beam is a catalog SID."""
+        w = self.w
+        final = dec.tokens[w.L].cpu().numpy()
+        live = dec.node[w.L].cpu().numpy() >= 0
+        cat = np.sort(oracle.prefix_codes(self.sids, w.L, w.V))
+        got = oracle.prefix_codes(final[live], w.L, w.V)
+        pos = np.minimum(np.searchsorted(cat, got), cat.size - 1)
+        assert (cat[pos] == got).all()

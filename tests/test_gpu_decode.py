@@ -21,17 +21,25 @@ def _gpu():
     yield
 
 
-def run_chain(w, seed, sample_rows=None, mask_sample=None):
+def run_chain(w, seed, sample_rows=None, mask_sample=None, prebuilt=None):
+    """``prebuilt``: the result of tests.large.build_verified_trie (the
+    library's trie, verified on sampled prefixes, read as data by the
+    oracle's mask logic) instead of a trie and prefix tables built here."""
     import wide_beam_sid_amd as gr
     from wide_beam_sid_amd.runner import Decoder
     print(f"[chain] {w.name} B={w.B} sched={w.schedule} n_sids={w.n_sids} seed={seed}", flush=True)
-    sids = W.make_catalog(w, seed)
-    ads = W.make_ads(w, seed, W.ad_counts(w, seed))
     req = W.make_requests(w, seed)
     kc, vc = W.make_context(w, seed)
-    trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
-    chk = ChainCheck(w, seed, sids, ads, req, (kc, vc), trie.host_view(), sample_rows,
-                     mask_sample)
+    if prebuilt is None:
+        sids = W.make_catalog(w, seed)
+        ads = W.make_ads(w, seed, W.ad_counts(w, seed))
+        trie = gr.Trie.build(sids, w.V, w.w_bm, w.bloom_bits, w.bloom_k, [ads], keep_host=True)
+        chk = ChainCheck(w, seed, sids, ads, req, (kc, vc), trie.host_view(), sample_rows,
+                         mask_sample)
+    else:
+        trie, sids = prebuilt["trie"], prebuilt["sids"]
+        chk = ChainCheck(w, seed, sids, None, req, (kc, vc), prebuilt["view"], sample_rows,
+                         mask_sample, ix=prebuilt["ix"])
     probes = (gr.bloom_probes(req.locs.reshape(-1), w.bloom_bits, w.bloom_k)
               if w.bloom_bits else np.zeros((1, 1), np.uint32))
     dec = Decoder(trie, w.B, w.V, w.schedule, w.H, w.d_h, w.T_ctx, w.dtype, debug=True)
@@ -97,12 +105,33 @@ def test_decode_chain_longctx_full_size():
 def test_decode_chain_stress_full_shape():
     """The stress shape (B = 64, M = 1024, V = 1024, T_ctx 512, 8 x 64 heads,
     8192-bit Bloom with k = 5, 64 user locations, geo lists of 1-256 ids from
-    1M, per-request eligibility ~10%) on a 2M-SID catalog (the 16M one is
-    exercised by the benchmark's index build, not by the oracle).  Masks are
-    compared bit for bit on 2048 sampled rows per step; scores, selection,
-    child nodes, token history and block table on every row."""
+    1M, per-request eligibility ~10%) on a 2M-SID catalog, small enough for
+    the oracle's own prefix tables.  Masks are compared bit for bit on 2048
+    sampled rows per step; scores, selection, child nodes, token history and
+    block table on every row."""
     run_chain(W.WORKLOADS["stress_b64"].scaled(n_sids=2_000_000), 4, sample_rows=256,
               mask_sample=2048)
+
+
+@pytest.mark.timeout(1800)
+def test_decode_chain_stress_full_size():
+    """The stress workload at its stated size: 16M SIDs with a Zipf(1.2)
+    first level, 1-8 ads per SID, geo lists of 1-256 ids from 1M in 8192-bit
+    Bloom filters (k = 5), B = 64, M = 1024, V = 1024.  The oracle's prefix
+    tables would not fit, so (as for any catalog of this size) the library's
+    index is verified on sampled prefixes -- all 1024 of the first level and
+    10,000 of each deeper level, rows equal to the unions the oracle
+    accumulates from the same ad stream, children equal to the catalog's
+    next tokens -- and the oracle's mask logic then reads that trie as data:
+    masks bit for bit on 2048 sampled rows per step; scores, selection,
+    child nodes, token history and block table on every row; attention on
+    256 sampled rows."""
+    from tests.large import build_verified_trie
+    w, seed = W.WORKLOADS["stress_b64"], 4
+    assert w.n_sids == 16_000_000
+    pre = build_verified_trie(w, seed, n_sample=10_000, workers=8)
+    assert pre["checked"] == 1024 + 3 * 10_000
+    run_chain(w, seed, sample_rows=256, mask_sample=2048, prebuilt=pre)
 
 
 def _decode_outputs(w, seed, trie, req, probes, kc, vc, debug):

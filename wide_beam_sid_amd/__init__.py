@@ -132,8 +132,10 @@ class Trie:
                                            "bloom_k", "num_nodes", "num_entries", "bm_rows",
                                            "bl_rows", "slice_words", "kway_rows")}
 
-    def host_view(self) -> dict:
-        """Copies of the host arrays (trie built with keep_host=True)."""
+    def host_view(self, copy: bool = True) -> dict:
+        """The host arrays (trie built with keep_host=True): copies, or with
+        copy=False read-only views of the trie's own arrays, valid while the
+        trie lives."""
         v = TrieView()
         check(_lib.lib().gr_trie_host_view(self.h, ctypes.byref(v)))
         n, e = v.num_nodes, v.num_entries
@@ -143,7 +145,11 @@ class Trie:
             if not ptr or count == 0:
                 return np.zeros(0, np_dtype)
             buf = (ctype * count).from_address(ptr)
-            return np.frombuffer(buf, dtype=np_dtype, count=count).copy()
+            a = np.frombuffer(buf, dtype=np_dtype, count=count)
+            if copy:
+                return a.copy()
+            a.flags.writeable = False
+            return a
 
         out = {
             "node_offsets": arr(v.node_offsets, ctypes.c_int32, n + 1, np.int32),
