@@ -283,7 +283,8 @@ def _trie_case(w, seed, slice_min=0, kway=None):
 
 
 def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mode="normal",
-             B=None, slice_min=0, staged=False, kway=None, trie=None):
+             B=None, slice_min=0, staged=False, kway=None, trie=None, between=None,
+             node_in=None, acc_in=None):
     """Run gr_constrain_topk on synthetic beam rows at depth t and check every
     output against the oracle.  ``trie`` replaces the built trie of the
     workload for the GPU call (the same index, made another way)."""
@@ -294,15 +295,20 @@ def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mo
     trie = built if trie is None else trie
     rng = np.random.default_rng(seed * 31 + M_in + t)
     R = B * M_in
-    depth_nodes = np.nonzero(view["node_depth"] == t)[0]
-    node_in = rng.choice(depth_nodes, size=R).astype(np.int32)
-    dead = rng.random(R) < dead_frac
-    node_in[dead] = -1
-    if acc_mode == "normal":
-        acc_in = (-rng.random(R) * 4).astype(np.float32)
-    else:
-        acc_in = np.full(R, -1.5, np.float32)
-    acc_in[dead] = -np.inf
+    if node_in is None:   # random rows at depth t (a few dead)
+        depth_nodes = np.nonzero(view["node_depth"] == t)[0]
+        node_in = rng.choice(depth_nodes, size=R).astype(np.int32)
+        dead = rng.random(R) < dead_frac
+        node_in[dead] = -1
+        if acc_mode == "normal":
+            acc_in = (-rng.random(R) * 4).astype(np.float32)
+        else:
+            acc_in = np.full(R, -1.5, np.float32)
+        acc_in[dead] = -np.inf
+    else:                 # the given beam rows (e.g. a previous step's outputs)
+        node_in = np.ascontiguousarray(node_in, np.int32)
+        acc_in = np.ascontiguousarray(acc_in, np.float32)
+        rng.random(R)
     if logit_mode == "normal":
         logits = _rand((R, w.V), w.dtype, rng)
     else:  # every logit equal: ties everywhere
@@ -336,6 +342,9 @@ def run_tail(w, seed, M_in, k_out, t, dead_frac=0.1, logit_mode="normal", acc_mo
                         ws_bytes=ws_bytes, **out)
     if staged:
         gr.constrain(trie, args)
+        if between is not None:   # sees the workspace between the two stages
+            torch.cuda.synchronize()
+            between(ws)
         gr.topk_reorder(trie, args)
     else:
         gr.constrain_topk(trie, args)
@@ -572,3 +581,28 @@ def test_trie_create_from_arrays_runs_the_same_tail(name, seed, M_in, k_out, t):
     b = run_tail(w, seed, M_in, k_out, t, 0.1, B=2)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_node_major_step_after_map_writes_of_other_batch_sizes():
+    """The step after the root takes the rows named by the inverse map that
+    the previous step's select leaves in the workspace.  Calls of different
+    batch sizes share the workspace here (B = 1 then 2 then 4 at the root, each
+    followed by the step after the root at another B): whatever the map and
+    the other calls left, every output matches the oracle."""
+    w = TAIL_WORKLOADS["stress_20k"]   # V = 1024: the node-major pass runs
+    seen = []
+
+    def back_counts(ws):
+        # the segments' back counts (node-major survivors) follow the
+        # 2048-bin histograms of up to 1024 requests in the workspace
+        off = 4 * 2048 * 1024
+        seen.append(int(ws[off:off + 4 * 1024 * 4].view(torch.int32).count_nonzero()))
+
+    for B1, B0 in ((2, 1), (3, 2), (4, 1), (4, 3)):
+        root = run_tail(w, 4, 1, 1024, 0, 0.0, B=B1)   # root step: writes the map
+        run_tail(w, 4, 1, 1024, 0, 0.0, B=B0)          # another B overwrites part of it
+        # the step after the root on the first call's outputs: rows of the
+        # requests b >= B0 are named by the map, the others are not
+        run_tail(w, 4, 1024, 1000, 1, B=B1, staged=True, between=back_counts,
+                 node_in=root["node_out"], acc_in=root["acc_out"])
+    assert all(n > 0 for n in seen), seen         # the pass took rows every time

@@ -95,6 +95,15 @@ struct TailParams {
     int vec_rows;             // token / block-table rows movable as 16-byte pieces
     const int32_t *kw_off, *kw_bmi, *kw_bli;   // k-way partitions (null: one union per entry)
     int lds_lg;         // the rows' bf16 logits are kept in LDS by the log-sum-exp pass
+    // Node-major pass at the step after the root (k_expand_nm): the rows of
+    // root children 1..n_nm that the inverse map names are tested there.
+    int n_nm;           // root children taken node-major this call (0: none)
+    int map_write;      // k_select records each output row's root child in inv
+    int n_root;         // the root's children are nodes 1..n_root
+    int32_t *inv;       // [B, V]: beam row of request b at root child v + 1
+    uint32_t *segback;  // [MAX_B, NM_MAX_GX]: node-major survivors at the back of each segment
+    int nm_wave_dw;     // LDS dwords per node-major wavefront
+    int nm_wgs;         // node-major workgroups at the front of k_expand's grid
 };
 
 // Bin of a candidate score below the request bound U (monotone
@@ -103,6 +112,15 @@ __device__ __forceinline__ int score_bin(float s, float U) {
     float d = (U - s) * BIN_SCALE;
     if (!(d > 0.0f)) return 0;
     return d >= (float)(NBINS - 1) ? NBINS - 1 : (int)d;
+}
+
+// Row m of request b at node `node` is the node-major pass's (k_expand_nm):
+// the node is a root child with a bit-sliced block and the inverse map names
+// row m for it.  k_expand and k_expand_nm both decide by this test.
+__device__ __forceinline__ bool nm_covered(const TailParams &p, int b, int m, int node,
+                                           int64_t blk) {
+    return p.n_nm && node >= 1 && node <= p.n_nm && blk >= 0 &&
+           p.inv[(size_t)b * p.V + node - 1] == m;
 }
 
 // 64-bit selection key: higher = better; score first, then lower flat index.
@@ -355,8 +373,284 @@ __device__ __forceinline__ void write_slot(const TailParams &p, int b, size_t sl
     }
 }
 
+// ---------------------------------------------------------------------------
+// Node-major pass at the step after the root.  There every live beam row of a
+// request sits at a different child of the root, so the rows of all requests
+// at one root child can be tested together against that node's bit-sliced
+// block: the workgroups of a node run on one XCD, so the block goes through
+// one L2 once instead of once per request.  One wavefront takes one
+// request's row.  The row of request b at root child n is the one the
+// inverse map names (recorded by the previous step's select); a row belongs
+// to this pass when the map names it, its node is n and n has a block, and
+// k_expand skips exactly those rows, so any map content gives the same
+// result and a map from the previous step covers every row.
+// ---------------------------------------------------------------------------
+constexpr int NM_WAVES = EXP_WAVES;   // the pass runs in k_expand's workgroups
+static_assert(NM_MAX_GX <= SEL_THREADS, "k_select takes one segment per thread with node-major parts");
+
+__device__ __forceinline__ int nth_set_bit(uint64_t x, int n) {
+    for (int i = 0; i < n; ++i) x &= x - 1;
+    return __builtin_ctzll(x);
+}
+
+// eqs 5 and 8 for every child of a bit-sliced block, for one request, by one
+// wavefront.  Column pos of the block is the wc words at blk + pos * wc (bit
+// j of word u: child 64 u + j).  A column is read as NP = wc / PW pieces of
+// PW words by LPC lanes (a power of two >= NP), so one load instruction
+// reads CPI = 64 / LPC whole columns -- a few cache lines -- rather than a
+// line per lane.  Lane (g, j) = (lane / LPC, lane % LPC) ANDs piece j of its
+// slot g's attribute columns (eq 5), and per location of its slot the
+// location's probe columns (eq 8), ORing over locations; then the slots are
+// combined across lanes.  Lanes j < NP of slot 0 return the pass bits of
+// words PW j .. PW j + PW - 1.  ubm: the request's attribute word; pr: this
+// lane's location's probe positions (lane l = location l < n_loc <= 64).
+template <int PW>
+__device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int bl_pos, uint64_t ubm,
+                                            const uint32_t pr[MAX_KP], int n_loc, int bloom_k,
+                                            bool bloom, int lane, uint64_t out[PW]) {
+    const int NP = wc / PW;
+    int lg = 0;
+    while ((1 << lg) < NP) ++lg;
+    const int LPC = 1 << lg, CPI = 64 >> lg;
+    const int g = lane >> lg, j = lane & (LPC - 1);
+    const bool jv = j < NP;
+    auto load = [&](int pos, uint64_t v[PW]) {
+        const uint64_t *c = blk + (size_t)pos * wc + PW * j;
+        if constexpr (PW == 2) {
+            const uint4 u = *(const uint4 *)c;
+            v[0] = (uint64_t)u.x | ((uint64_t)u.y << 32);
+            v[1] = (uint64_t)u.z | ((uint64_t)u.w << 32);
+        } else {
+            v[0] = *c;
+        }
+    };
+    uint64_t att[PW], acc[PW];
+#pragma unroll
+    for (int e = 0; e < PW; ++e) {
+        att[e] = ~0ull;
+        acc[e] = bloom ? 0ull : ~0ull;
+    }
+    const int nub = __popcll(ubm);
+    for (int u0 = 0; u0 < nub; u0 += CPI) {
+        const int u = u0 + g;
+        if (jv && u < nub) {
+            uint64_t v[PW];
+            load(bl_pos + nth_set_bit(ubm, u), v);
+#pragma unroll
+            for (int e = 0; e < PW; ++e) att[e] &= v[e];
+        }
+    }
+    if (bloom) {
+        for (int l0 = 0; l0 < n_loc; l0 += CPI) {   // uniform
+            const int l = l0 + g;
+            const bool lv = jv && l < n_loc;
+            uint32_t pos[MAX_KP];
+#pragma unroll
+            for (int k = 0; k < MAX_KP; ++k) pos[k] = __shfl(pr[k], l < 64 ? l : 0, 64);
+            uint64_t v[MAX_KP][PW];
+#pragma unroll
+            for (int k = 0; k < MAX_KP; ++k)   // every probe column first, then the ANDs
+                if (k < bloom_k && lv) load(pos[k], v[k]);
+            uint64_t a[PW];
+#pragma unroll
+            for (int e = 0; e < PW; ++e) a[e] = ~0ull;
+#pragma unroll
+            for (int k = 0; k < MAX_KP; ++k)
+                if (k < bloom_k && lv)
+#pragma unroll
+                    for (int e = 0; e < PW; ++e) a[e] &= v[k][e];
+            if (lv)
+#pragma unroll
+                for (int e = 0; e < PW; ++e) acc[e] |= a[e];
+        }
+    }
+    // the slots of a piece: lanes j, j + LPC, j + 2 LPC, ...
+    for (int o = LPC; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < PW; ++e) {
+            att[e] &= __shfl_xor(att[e], o, 64);
+            acc[e] |= __shfl_xor(acc[e], o, 64);
+        }
+#pragma unroll
+    for (int e = 0; e < PW; ++e) out[e] = att[e] & acc[e];
+}
+
+// Node-major workgroup k (at the front of k_expand's grid): request b at
+// NM_WAVES consecutive root children, one wavefront per child.  The
+// workgroups of one group of children, one per request, have the same k
+// mod 8, so they run on one XCD, one after another, and read the children's
+// blocks through one L2.  The workgroup shares the request's bound and a
+// histogram of its survivors' bins, added to the request's histogram one
+// atomic per bin in use (an atomic per survivor, many lanes of one
+// instruction on the same bin, cost more than the whole pass).
+template <bool BF16>
+__device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *s_dyn) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int xcd = k & 7, q = k >> 3;
+    const int ng = (q / p.B) * 8 + xcd, b = q % p.B;
+    if (ng * NM_WAVES >= p.n_nm) return;   // the whole workgroup
+    const int ni = ng * NM_WAVES + wave, node = ni + 1;   // this wavefront's root child
+    const int V = p.V, words = (V + 63) >> 6;
+    uint32_t *s_h = (uint32_t *)s_dyn;                                    // survivors' bins
+    float *s_ubw = (float *)(s_h + NBINS);                                // bound per wavefront
+    float *s_x = s_ubw + 4 + (size_t)wave * p.nm_wave_dw;                 // the row's logits
+    uint64_t *s_pw = (uint64_t *)(s_x + ((V + 3) & ~3));                   // pass words
+    uint64_t *s_tm = s_pw + ((words + 1) & ~1);                            // kept tokens (debug)
+
+    // The row the map names, the node's children and block, the request's
+    // attribute word and this lane's location's probes: one round of loads.
+    const bool has_node = ni < p.n_nm;
+    const int m = has_node ? p.inv[(size_t)b * V + ni] : -1;
+    const int32_t o0 = has_node ? p.off[node] : 0, o1 = has_node ? p.off[node + 1] : 0;
+    const int64_t blk = has_node && p.nslice ? p.nslice[node] : -1;
+    const uint64_t ubm = p.user_bm[(size_t)b * p.w_bm];
+    uint32_t pr[MAX_KP];
+#pragma unroll
+    for (int kk = 0; kk < MAX_KP; ++kk)
+        pr[kk] = (p.w_bl && lane < p.n_loc && kk < p.bloom_k)
+                     ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
+                           (uint32_t)(p.bloom_bits - 1)
+                     : 0u;
+    for (int i = tid; i < NBINS; i += EXP_THREADS) s_h[i] = 0u;
+    // the request's bound: the same live rows and the same max as k_select
+    {
+        const BoundLoads bl = bound_load(p, b);
+        const float ub = bound_finish(p, b, bl);
+        if (lane == 0) s_ubw[wave] = ub;
+    }
+    const bool active = m >= 0 && m < p.M_in && blk >= 0 &&
+                        p.node_in[(size_t)b * p.M_in + (m >= 0 && m < p.M_in ? m : 0)] == node;
+    __syncthreads();
+    const float U = fmaxf(fmaxf(s_ubw[0], s_ubw[1]), fmaxf(s_ubw[2], s_ubw[3]));
+    if (active) {   // wave-uniform: the wavefront's row is this pass's
+        const size_t r = (size_t)b * p.M_in + m;
+        const float acc = p.acc_in[r];
+        // log-sum-exp over all V logits; the logits stay in LDS for the scores
+        float mx = -INFINITY;
+        if (BF16 && p.vec_logits) {
+            const uint4 *x8 = (const uint4 *)((const uint16_t *)p.logits + r * V);
+            for (int c = lane; c < (V >> 3); c += 64) {
+                const uint4 u = x8[c];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float lo = __uint_as_float(w4[h] << 16), hi = __uint_as_float(w4[h] & 0xFFFF0000u);
+                    s_x[8 * c + 2 * h] = lo;
+                    s_x[8 * c + 2 * h + 1] = hi;
+                    mx = fmaxf(mx, fmaxf(lo, hi));
+                }
+            }
+        } else {
+            for (int v = lane; v < V; v += 64) {
+                const float x = logit_at<BF16>(p.logits, r * V + v);
+                s_x[v] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = wave_max(mx);
+        wave_lds_sync();
+        float se = 0.0f;
+        if (mx != -INFINITY)
+            for (int v = lane; v < V; v += 64) se += __expf(s_x[v] - mx);
+        se = wave_sum(se);
+        const float lse = mx + __logf(se);
+
+        // eqs 5 and 8 for every child
+        const int c = o1 - o0, wc = (c + 63) >> 6;
+        const uint64_t *bp = p.slice_tab + blk;
+        const int bl_pos = p.w_bl ? p.bloom_bits : 0;
+        if ((wc & 1) == 0) {
+            uint64_t pw[2];
+            sliced_pass<2>(bp, wc, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            if (lane < (wc >> 1)) {
+                s_pw[2 * lane] = pw[0];
+                s_pw[2 * lane + 1] = pw[1];
+            }
+        } else {
+            uint64_t pw[1];
+            sliced_pass<1>(bp, wc, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            if (lane < wc) s_pw[lane] = pw[0];
+        }
+        if (p.mask_words)
+            for (int w = lane; w < words; w += 64) s_tm[w] = 0ull;
+        wave_lds_sync();
+
+        // survivors: the passing children, reserved at the back of the
+        // segment of the row's row-major workgroup (m mod gx), a multiple of 8
+        uint32_t n = 0;
+        for (int u = lane; u < wc; u += 64) {
+            uint64_t w = s_pw[u];
+            const int rem = c - 64 * u;
+            if (rem < 64) w &= (1ull << rem) - 1ull;
+            n += (uint32_t)__popcll(w);
+        }
+        n = wave_incl_sum(n);
+        n = __builtin_amdgcn_readlane(n, 63);
+        const uint32_t n8 = (n + 7u) & ~7u;
+        const int xs = m % p.gx;
+        const uint64_t seg_cap = (uint64_t)p.seg_cap;
+        uint32_t old = 0;
+        if (lane == 0 && n8) old = atomicAdd(&p.segback[(size_t)b * NM_MAX_GX + xs], n8);
+        old = __builtin_amdgcn_readlane(old, 0);
+        const bool room = (uint64_t)old + n8 <= seg_cap;   // false only with a dirty workspace
+        const size_t base = ((size_t)b * p.gx + xs) * seg_cap + (seg_cap - old - n8);
+        uint32_t e = 0;   // survivors written (uniform)
+        for (int u0 = 0; u0 < wc; u0 += 8) {   // 8 words: every load of the chunk in flight
+            int tk[8], ch[8];
+            bool ok[8];
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2) {
+                const int u = u0 + q2, jj = 64 * u + lane;
+                ok[q2] = u < wc && jj < c && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
+                tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
+                ch[q2] = ok[q2] ? p.child[o0 + jj] : 0;
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < 8; ++q2) {
+                if (u0 + q2 >= wc) break;   // uniform
+                const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
+                if (ok[q2] && p.mask_words)
+                    atomicOr((unsigned long long *)&s_tm[tk[q2] >> 6], 1ull << (tk[q2] & 63));
+                const bool sel = ok[q2] && sc > -INFINITY;
+                const uint64_t bal = __ballot(sel);
+                if (sel && room) {
+                    const size_t idx = base + e + lanes_below(bal);
+                    const int bin = score_bin(sc, U);
+                    p.skey[idx] = make_key(sc, (uint32_t)(m * V + tk[q2]));
+                    p.schild[idx] = ch[q2];
+                    p.sbin[idx] = (uint16_t)bin;
+                    atomicAdd(&s_h[bin], 1u);
+                }
+                e += (uint32_t)__popcll(bal);
+            }
+        }
+        if (room)   // the reserved slots past the survivors are pads
+            for (uint32_t i = e + lane; i < n8; i += 64) {
+                p.skey[base + i] = 0ull;
+                p.sbin[base + i] = 0xFFFFu;
+            }
+        if (p.mask_words) {   // debug outputs of the row
+            wave_lds_sync();
+            if (p.dbg_mask)
+                for (int w = lane; w < words; w += 64) p.dbg_mask[r * words + w] = s_tm[w];
+            if (p.dbg_scores)
+                for (int v = lane; v < V; v += 64) {
+                    const bool kept = (s_tm[v >> 6] >> (v & 63)) & 1ull;
+                    p.dbg_scores[r * V + v] = kept ? acc + (s_x[v] - lse) : -INFINITY;
+                }
+        }
+    }
+    // the workgroup's bins into the request's histogram
+    __syncthreads();
+    uint32_t *gh = p.hist + (size_t)b * NBINS;
+    for (int i = tid; i < NBINS; i += EXP_THREADS) {
+        const uint32_t cnt = s_h[i];
+        if (cnt) atomicAdd(&gh[i], cnt);
+    }
+}
+
 // One workgroup = up to rows_wg beam rows of one request, taken with a stride
-// of gridDim.x (row m = blockIdx.x + i * gridDim.x) so that the live rows,
+// of gx (row m = x + i * gx) so that the live rows,
 // which sit at the front of a request after a top-k, spread over the grid.
 // The CSR child entries of those rows are flattened and processed 64 at a
 // time, one entry per lane: token, child, bitmask test (eq 5); then the Bloom
@@ -377,6 +671,7 @@ void k_expand(TailParams p) {
     __shared__ float s_lse[MAX_ROWS_WG];
     __shared__ float s_acc[MAX_ROWS_WG];
     __shared__ int64_t s_rblk[MAX_ROWS_WG];        // bit-sliced block of the row's node
+    __shared__ uint8_t s_skip[MAX_ROWS_WG];        // the row is the node-major pass's
     __shared__ uint32_t s_nsurv;                   // survivors written to the segment
     __shared__ int32_t s_slist[MAX_ROWS_WG];       // rows with a bit-sliced block
     __shared__ int s_nsl;
@@ -391,8 +686,16 @@ void k_expand(TailParams p) {
     __shared__ uint32_t s_kn;                      // k-way: partitions listed this sub-round
     __shared__ uint8_t s_kok[EXP_THREADS];         // k-way: entry kept (a partition passed)
 
-    const int b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int gx = gridDim.x, x = blockIdx.x;
+    // a flat grid: the node-major workgroups (p.nm_wgs, the longer ones)
+    // first, then gx * B row-major workgroups (x fastest)
+    const int gx = p.gx;
+    if ((int)blockIdx.x < p.nm_wgs) {
+        expand_nm<BF16>(p, (int)blockIdx.x, s_dyn);
+        return;
+    }
+    const int flat = (int)blockIdx.x - p.nm_wgs;
+    const int b = flat / gx, x = flat - b * gx;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nrows = x < p.M_in ? min(p.rows_wg, (p.M_in - x + gx - 1) / gx) : 0;
     const int V = p.V, words = (V + 63) >> 6;
     const int kp = (p.bloom_k + 3) & ~3;   // probes per location, padded
@@ -441,12 +744,19 @@ void k_expand(TailParams p) {
             int off0 = 0;
             float acc = -INFINITY;
             int64_t blk = -1;
+            bool skip = false;
             if (node >= 0 && node < p.num_nodes) {  // otherwise a dead row
                 off0 = p.off[node];
                 cnt = p.off[node + 1] - off0;
                 acc = p.acc_in[r];
                 if (p.nslice) blk = p.nslice[node];
+                if (nm_covered(p, b, m, node, blk)) {   // tested by k_expand_nm
+                    skip = true;
+                    cnt = 0;
+                    blk = -1;
+                }
             }
+            s_skip[lane] = skip;
             s_rblk[lane] = blk;
             s_roff[lane] = off0;
             s_rm[lane] = m;
@@ -487,6 +797,8 @@ void k_expand(TailParams p) {
             const int r = b * p.M_in + x + i * gx;
             const int nd = p.node_in[r];
             has = nd >= 0 && nd < p.num_nodes;
+            if (has && p.n_nm && nd >= 1 && nd <= p.n_nm)   // a node-major row needs no LSE here
+                has = !nm_covered(p, b, x + i * gx, nd, p.nslice ? p.nslice[nd] : -1);
             rowoff = (size_t)r * V;
         }
         if (has) {
@@ -1037,6 +1349,7 @@ void k_expand(TailParams p) {
     if (p.mask_words) {  // debug outputs: kept tokens and their scores, per row
         __syncthreads();
         for (int i = wave; i < nrows; i += EXP_WAVES) {
+            if (s_skip[i]) continue;   // written by the node-major pass
             const size_t r = (size_t)b * p.M_in + s_rm[i];
             const uint64_t *mk = s_mask + i * p.mask_words;
             if (p.dbg_mask)
@@ -1094,10 +1407,25 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     const uint64_t *keys = p.skey + (size_t)b * gx * seg_cap;
     uint32_t *gh = p.hist + (size_t)b * NBINS;
     // The segment counts and this thread's histogram bins are loaded before
-    // the bound's rows, so the three reads share one round trip.
+    // the bound's rows, so the three reads share one round trip.  The
+    // survivors are listed as sub-segments: with a node-major pass, segment
+    // x has a front part (its workgroup's survivors) and a back part (the
+    // node-major survivors of its rows, at the segment's end), thread tid
+    // taking both of segment tid; otherwise thread tid takes segments 2 tid
+    // and 2 tid + 1.  Every sub-segment holds a multiple of 8 entries.
     const uint32_t *cnt = p.segcnt + (size_t)b * gx;
-    const uint32_t c0 = 2 * tid < gx ? cnt[2 * tid] : 0u;       // gx <= 2 * SEL_THREADS
-    const uint32_t c1 = 2 * tid + 1 < gx ? cnt[2 * tid + 1] : 0u;
+    const bool two = p.n_nm != 0;                               // then gx <= NM_MAX_GX
+    const int nsub = two ? 2 * gx : gx;                         // <= 2 * SEL_THREADS
+    uint32_t c0, c1;
+    if (two) {
+        c0 = tid < gx ? min(cnt[tid], (uint32_t)seg_cap) & ~7u : 0u;
+        c1 = tid < gx ? p.segback[(size_t)b * NM_MAX_GX + tid] & ~7u : 0u;
+        if (c1 > (uint32_t)seg_cap - c0) c1 = 0u;   // only with a dirty workspace
+        if (tid < gx) p.segback[(size_t)b * NM_MAX_GX + tid] = 0u;   // zero for the next call
+    } else {
+        c0 = 2 * tid < gx ? cnt[2 * tid] : 0u;       // gx <= 2 * SEL_THREADS
+        c1 = 2 * tid + 1 < gx ? cnt[2 * tid + 1] : 0u;
+    }
     constexpr int PER = NBINS / SEL_THREADS;
     uint32_t c[PER];
 #pragma unroll
@@ -1114,11 +1442,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         uint32_t spre = 0;
         for (int w = 0; w < wave; ++w) spre += s_wsum2[w];
         const uint32_t ex = spre + sinc - c0 - c1;
-        // thread tid writes entries 2 tid and 2 tid + 1; entry gx (the total)
-        // lies past the last thread's pair when gx = 2 * SEL_THREADS
-        if (2 * tid <= gx) s_segpre[2 * tid] = ex;
-        if (2 * tid + 1 <= gx) s_segpre[2 * tid + 1] = ex + c0;
-        if (gx == 2 * SEL_THREADS && tid == SEL_THREADS - 1) s_segpre[gx] = ex + c0 + c1;
+        // thread tid writes entries 2 tid and 2 tid + 1; entry nsub (the
+        // total) lies past the last thread's pair when nsub = 2 * SEL_THREADS
+        if (2 * tid <= nsub) s_segpre[2 * tid] = ex;
+        if (2 * tid + 1 <= nsub) s_segpre[2 * tid + 1] = ex + c0;
+        if (nsub == 2 * SEL_THREADS && tid == SEL_THREADS - 1) s_segpre[nsub] = ex + c0 + c1;
     }
     float U = s_ub[0];
     for (int w = 1; w < SEL_THREADS / 64; ++w) U = fmaxf(U, s_ub[w]);
@@ -1165,15 +1493,19 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     const int thr = s_thr, below = s_below;
     uint32_t n_surv = 0;   // the total of the segment counts
     for (int w = 0; w < SEL_THREADS / 64; ++w) n_surv += s_wsum2[w];
-    // offset of the f-th survivor (segments concatenated) in the request's keys
+    // offset of the f-th survivor (sub-segments concatenated) in the
+    // request's keys
     auto surv = [&](uint32_t f) -> uint32_t {
-        int lo = 0, hi = gx;
+        int lo = 0, hi = nsub;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (s_segpre[mid] <= f) lo = mid;
             else hi = mid;
         }
-        return (uint32_t)(lo * seg_cap) + (f - s_segpre[lo]);
+        if (!two) return (uint32_t)(lo * seg_cap) + (f - s_segpre[lo]);
+        const uint32_t seg = (uint32_t)lo >> 1;
+        if (!(lo & 1)) return (uint32_t)(seg * seg_cap) + (f - s_segpre[lo]);
+        return (uint32_t)((seg + 1) * seg_cap) - (s_segpre[lo + 1] - f);   // a back part
     };
 
     // 2. Survivors of bins below the threshold go to their bin's slots;
@@ -1385,6 +1717,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         // survivor's), so it goes out with the parent's rows
         const int32_t ch = p.schild[(size_t)b * gx * seg_cap + (live ? srcp : 0u)];
         write_slot(p, b, (size_t)b * k + slot, live, keyp, live ? ch : -1);
+        // the next step's node-major pass finds the row at each root child
+        if (p.map_write && live && ch >= 1 && ch <= p.n_root) p.inv[(size_t)b * p.V + ch - 1] = slot;
     }
 }
 
@@ -1462,6 +1796,27 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
                  al16(a.table_out);
     const int nprobe = tr.w_bl ? p.n_loc * ((tr.bloom_k + 3) & ~3) : 0;
     p.lds_lg = p.vec_logits && (size_t)p.rows_wg * a.V * 2 <= (size_t)LG_BYTES;
+    // Node-major pass at the step after the root (rows at root children).
+    // It pays when a column of a node's block spans whole cache lines and
+    // the blocks are large (V >= 512: 1 MB per node at V = 1024, 8192-bit
+    // Bloom; stress workload t = 1: 1337 -> 751 us) and when the step's rows
+    // cover most root children; at V = 256 (32-byte columns) it measured
+    // even with the row-major pass, which is kept there.
+    p.inv = (int32_t *)(ws + ly.inv);
+    p.segback = (uint32_t *)(ws + ly.segback);
+    p.n_root = tr.n_root;
+    const bool nm_ok = tr.n_root > 0 && tr.node_slice && !tr.kway_offsets && tr.w_bm == 1 &&
+                       (!tr.w_bl || (p.n_loc <= 64 && tr.bloom_k <= MAX_KP)) && a.V >= 512;
+    p.n_nm = (nm_ok && a.t == 1 && gx <= NM_MAX_GX && 2 * (int64_t)a.M_in >= tr.n_root)
+                 ? tr.n_root : 0;
+    p.map_write = nm_ok && a.t == 0;
+    {   // per node-major wavefront: its row's logits, pass words and kept
+        // tokens; workgroups: 8 * ceil(groups / 8) * B (see expand_nm)
+        const int words = (a.V + 63) / 64;
+        p.nm_wave_dw = ((a.V + 3) & ~3) + 4 * ((words + 1) & ~1);
+        const int ngroups = (p.n_nm + NM_WAVES - 1) / NM_WAVES;
+        p.nm_wgs = p.n_nm ? 8 * ((ngroups + 7) / 8) * a.B : 0;
+    }
     const size_t shm = sizeof(uint64_t) * (((size_t)p.rows_wg * p.mask_words + 1) & ~(size_t)1) +
                        sizeof(uint64_t) * (((size_t)p.rows_wg * p.wmax + 1) & ~(size_t)1) +
                        (p.lds_lg ? sizeof(uint16_t) * (size_t)p.rows_wg * a.V : 0) +
@@ -1485,7 +1840,9 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
 hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
     size_t shm = 0;
     const TailParams p = tail_params(tr, a, &shm);
-    dim3 g1(p.gx, a.B);
+    if (p.n_nm)   // the histogram, the bounds, then the wavefronts' areas
+        shm = std::max(shm, sizeof(uint32_t) * ((size_t)NBINS + 4 + (size_t)NM_WAVES * p.nm_wave_dw));
+    const dim3 g1((unsigned)p.nm_wgs + (unsigned)p.gx * (unsigned)a.B);
     const bool wide = tr.w_bl >= 64;
     if (a.dtype == GR_BF16) {
         if (wide) k_expand<true, true><<<g1, EXP_THREADS, shm, s>>>(p);
@@ -1545,9 +1902,14 @@ hipError_t tail_scratch(void **out) {
 }
 
 hipError_t launch_clear_hist(void *ws, int B, hipStream_t s) {
-    // the histogram region sits at offset 0 of the tail workspace layout
+    // the histograms sit at offset 0 of the tail workspace layout, the
+    // segments' back counts right after the histogram region
+    const TailWsLayout ly = tail_ws_layout(B, 1, 1);
     const size_t n = (size_t)B * NBINS * sizeof(uint32_t) / sizeof(uint4);
     k_clear_u32x4<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((uint4 *)ws, n);
+    const size_t n2 = (size_t)B * NM_MAX_GX * sizeof(uint32_t) / sizeof(uint4);
+    k_clear_u32x4<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+        (uint4 *)((char *)ws + ly.segback), n2);
     return hipGetLastError();
 }
 

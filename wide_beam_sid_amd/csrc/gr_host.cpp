@@ -653,6 +653,12 @@ static gr_status upload_trie(gr_trie *t, const int32_t *off, const int32_t *chil
         d.kway_rows = kw_rows;
         slice_min = -1;   // the bit-sliced blocks hold one-union rows only
     }
+    {   // are the root's children nodes 1..n1 (token order)?
+        const int32_t n1 = d.num_nodes > 0 ? off[1] - off[0] : 0;
+        bool dense = n1 > 0;
+        for (int32_t j = 0; j < n1 && dense; ++j) dense = child[off[0] + j] == j + 1;
+        d.n_root = dense ? n1 : 0;
+    }
     if (slice_min >= 0) {
         std::vector<int64_t> ns;
         std::vector<uint64_t> tab;
@@ -1119,10 +1125,15 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     const size_t nseg = (size_t)B * l.shape.gx;
     const size_t nsurv = nseg * (size_t)l.shape.seg_cap;
     size_t o = 0;
-    // the histograms first, at a fixed size: the region is only ever used as
-    // histograms and stays zero between calls of any shape
-    l.hist = o;   o = al(o + sizeof(uint32_t) * (size_t)NBINS * MAX_B);
-    l.segcnt = o; o = al(o + sizeof(uint32_t) * nseg);
+    // the histograms and the segments' back counts first, at fixed places
+    // and sizes: each region is only ever used as what it is and stays zero
+    // between calls of any shape; then the inverse map of root children at a
+    // fixed place, so that a decode's steps (several M_in) find it where the
+    // previous step left it (its content is checked before use)
+    l.hist = o;    o = al(o + sizeof(uint32_t) * (size_t)NBINS * MAX_B);
+    l.segback = o; o = al(o + sizeof(uint32_t) * (size_t)MAX_B * NM_MAX_GX);
+    l.inv = o;     o = al(o + sizeof(int32_t) * (size_t)B * V);
+    l.segcnt = o;  o = al(o + sizeof(uint32_t) * nseg);
     l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);
     l.schild = o; o = al(o + sizeof(int32_t) * nsurv);
     l.sbin = o;   o = al(o + sizeof(uint16_t) * nsurv);

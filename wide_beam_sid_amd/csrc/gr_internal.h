@@ -39,6 +39,9 @@ struct TrieDev {
     const int32_t *kway_bmi;
     const int32_t *kway_bli;
     int64_t kway_rows;
+    // The root's children are nodes 1..n_root in token order (0 otherwise):
+    // then a step after the root can take its rows node-major.
+    int32_t n_root;
 };
 constexpr int ENTRY_BM_MAX_W = 2;
 
@@ -65,6 +68,7 @@ struct TailShape {
 constexpr int MAX_M_IN = 65536;      // beam rows per request entering the tail
 constexpr int MAX_B = 1024;          // requests per tail call (histogram region)
 constexpr int MAX_GX = 2048;         // expand workgroups per request
+constexpr int NM_MAX_GX = 1024;      // expand workgroups per request with a node-major pass
 inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
     const int64_t R = (int64_t)B * M_in;
     int64_t rw = R / 1024;
@@ -74,13 +78,15 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
     TailShape t;
     t.rows_wg = (int)rw;
     t.gx = (int)((M_in + rw - 1) / rw);
-    t.seg_cap = (rw * V + 7) & ~(int64_t)7;   // segments are read 8 bins / 2 keys at a time
+    // segments are read 8 bins / 2 keys at a time; a segment also holds up
+    // to rows_wg rows' node-major survivors, each padded to a multiple of 8
+    t.seg_cap = rw * (((int64_t)V + 7) & ~(int64_t)7);
     return t;
 }
 
 // Workspace carving of gr_constrain_topk (byte offsets).
 struct TailWsLayout {
-    size_t segcnt, hist, skey, schild, sbin, total;
+    size_t hist, segback, inv, segcnt, skey, schild, sbin, total;
     TailShape shape;
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
@@ -121,7 +127,7 @@ hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_
 // that zero-fills the score histograms of B requests in a workspace.
 constexpr size_t TAIL_SCRATCH_BYTES = (size_t)128 << 20;
 hipError_t tail_scratch(void **out);
-hipError_t launch_clear_hist(void *ws, int B, hipStream_t s);
+hipError_t launch_clear_hist(void *ws, int B, hipStream_t s);   // also the back counts
 
 // Records msg as the message gr_last_error returns and returns st.
 gr_status report(gr_status st, const char *msg);
