@@ -598,6 +598,9 @@ def test_node_major_step_after_map_writes_of_other_batch_sizes():
         off = 4 * 2048 * 1024
         seen.append(int(ws[off:off + 4 * 1024 * 4].view(torch.int32).count_nonzero()))
 
+    # the workspace sized for the largest call first: a workspace that grows
+    # between the root step and the next would start the next with no map
+    _workspace(_gr().constrain_topk_workspace(4, 1024, w.V, 1024))
     for B1, B0 in ((2, 1), (3, 2), (4, 1), (4, 3)):
         root = run_tail(w, 4, 1, 1024, 0, 0.0, B=B1)   # root step: writes the map
         run_tail(w, 4, 1, 1024, 0, 0.0, B=B0)          # another B overwrites part of it
@@ -606,3 +609,24 @@ def test_node_major_step_after_map_writes_of_other_batch_sizes():
         run_tail(w, 4, 1024, 1000, 1, B=B1, staged=True, between=back_counts,
                  node_in=root["node_out"], acc_in=root["acc_out"])
     assert all(n > 0 for n in seen), seen         # the pass took rows every time
+
+
+@pytest.mark.parametrize("geo", [(1, 64), (200, 256)])
+def test_node_major_pass_sparse_and_dense_bloom_rows(geo):
+    """The node-major pass stops testing a row's locations once every child
+    that passes eq 5 has a location with all its probe bits.  With long geo
+    lists (dense Bloom rows) that happens after the first group of
+    locations; with shorter ones most rows test every location.  Both
+    against the oracle, on the step after the root."""
+    w = TAIL_WORKLOADS["stress_20k"].scaled(geo_per_ad=geo)
+    seen = []
+
+    def back_counts(ws):
+        off = 4 * 2048 * 1024
+        seen.append(int(ws[off:off + 4 * 1024 * 4].view(torch.int32).count_nonzero()))
+
+    _workspace(_gr().constrain_topk_workspace(2, 1024, w.V, 1024))   # kept by both calls
+    root = run_tail(w, 4, 1, 1024, 0, 0.0, B=2)
+    run_tail(w, 4, 1024, 1000, 1, B=2, staged=True, between=back_counts,
+             node_in=root["node_out"], acc_in=root["acc_out"])
+    assert seen and seen[0] > 0, seen

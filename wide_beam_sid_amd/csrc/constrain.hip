@@ -43,6 +43,8 @@ constexpr int EXP_THREADS = 64 * EXP_WAVES;
 constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 4096 bits)
 constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
 constexpr int MAX_KP = 8;             // probes per location held in registers (more: LDS)
+constexpr int NM_KP = 6;              // probes per location of the node-major pass (registers only)
+constexpr int NM_SW = 4;              // node-major survivor words whose loads are in flight together
 constexpr int LG_BYTES = 8192;        // bf16 logit rows an expand workgroup keeps in LDS
 constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
@@ -395,19 +397,25 @@ __device__ __forceinline__ int nth_set_bit(uint64_t x, int n) {
 
 // eqs 5 and 8 for every child of a bit-sliced block, for one request, by one
 // wavefront.  Column pos of the block is the wc words at blk + pos * wc (bit
-// j of word u: child 64 u + j).  A column is read as NP = wc / PW pieces of
-// PW words by LPC lanes (a power of two >= NP), so one load instruction
-// reads CPI = 64 / LPC whole columns -- a few cache lines -- rather than a
-// line per lane.  Lane (g, j) = (lane / LPC, lane % LPC) ANDs piece j of its
-// slot g's attribute columns (eq 5), and per location of its slot the
-// location's probe columns (eq 8), ORing over locations; then the slots are
-// combined across lanes.  Lanes j < NP of slot 0 return the pass bits of
-// words PW j .. PW j + PW - 1.  ubm: the request's attribute word; pr: this
-// lane's location's probe positions (lane l = location l < n_loc <= 64).
+// j of word u: child 64 u + j); the block has c children.  A column is read
+// as NP = wc / PW pieces of PW words by LPC lanes (a power of two >= NP), so
+// one load instruction reads CPI = 64 / LPC whole columns -- a few cache
+// lines -- rather than a line per lane.  Lane (g, j) = (lane / LPC, lane %
+// LPC) ANDs piece j of its slot g's attribute columns (eq 5), which the
+// slots then combine; eq 8 takes the user's locations CPI at a time, lane
+// (g, j) ANDing the probe columns of location g of the group, and the slots
+// OR their results into the running ANY.  The groups stop as soon as every
+// child that passes eq 5 has a location with all its probe bits: further
+// locations cannot change the result (the OR only grows), and the Bloom rows
+// of shallow nodes -- unions over many ads -- are dense enough that the
+// first group usually covers every child.  Lanes j < NP of slot 0 return the
+// pass bits of words PW j .. PW j + PW - 1.  ubm: the request's attribute
+// word; pr: this lane's location's probe positions (lane l = location l <
+// n_loc <= 64).
 template <int PW>
-__device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int bl_pos, uint64_t ubm,
-                                            const uint32_t pr[MAX_KP], int n_loc, int bloom_k,
-                                            bool bloom, int lane, uint64_t out[PW]) {
+__device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int c, int bl_pos,
+                                            uint64_t ubm, const uint32_t pr[NM_KP], int n_loc,
+                                            int bloom_k, bool bloom, int lane, uint64_t out[PW]) {
     const int NP = wc / PW;
     int lg = 0;
     while ((1 << lg) < NP) ++lg;
@@ -415,20 +423,20 @@ __device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int bl_
     const int g = lane >> lg, j = lane & (LPC - 1);
     const bool jv = j < NP;
     auto load = [&](int pos, uint64_t v[PW]) {
-        const uint64_t *c = blk + (size_t)pos * wc + PW * j;
+        const uint64_t *col = blk + (size_t)pos * wc + PW * j;
         if constexpr (PW == 2) {
-            const uint4 u = *(const uint4 *)c;
+            const uint4 u = *(const uint4 *)col;
             v[0] = (uint64_t)u.x | ((uint64_t)u.y << 32);
             v[1] = (uint64_t)u.z | ((uint64_t)u.w << 32);
         } else {
-            v[0] = *c;
+            v[0] = *col;
         }
     };
     uint64_t att[PW], acc[PW];
 #pragma unroll
     for (int e = 0; e < PW; ++e) {
         att[e] = ~0ull;
-        acc[e] = bloom ? 0ull : ~0ull;
+        acc[e] = 0ull;
     }
     const int nub = __popcll(ubm);
     for (int u0 = 0; u0 < nub; u0 += CPI) {
@@ -440,37 +448,54 @@ __device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int bl_
             for (int e = 0; e < PW; ++e) att[e] &= v[e];
         }
     }
-    if (bloom) {
-        for (int l0 = 0; l0 < n_loc; l0 += CPI) {   // uniform
-            const int l = l0 + g;
-            const bool lv = jv && l < n_loc;
-            uint32_t pos[MAX_KP];
-#pragma unroll
-            for (int k = 0; k < MAX_KP; ++k) pos[k] = __shfl(pr[k], l < 64 ? l : 0, 64);
-            uint64_t v[MAX_KP][PW];
-#pragma unroll
-            for (int k = 0; k < MAX_KP; ++k)   // every probe column first, then the ANDs
-                if (k < bloom_k && lv) load(pos[k], v[k]);
-            uint64_t a[PW];
-#pragma unroll
-            for (int e = 0; e < PW; ++e) a[e] = ~0ull;
-#pragma unroll
-            for (int k = 0; k < MAX_KP; ++k)
-                if (k < bloom_k && lv)
-#pragma unroll
-                    for (int e = 0; e < PW; ++e) a[e] &= v[k][e];
-            if (lv)
-#pragma unroll
-                for (int e = 0; e < PW; ++e) acc[e] |= a[e];
-        }
-    }
     // the slots of a piece: lanes j, j + LPC, j + 2 LPC, ...
     for (int o = LPC; o < 64; o <<= 1)
 #pragma unroll
-        for (int e = 0; e < PW; ++e) {
-            att[e] &= __shfl_xor(att[e], o, 64);
-            acc[e] |= __shfl_xor(acc[e], o, 64);
-        }
+        for (int e = 0; e < PW; ++e) att[e] &= __shfl_xor(att[e], o, 64);
+    if (!bloom) {
+#pragma unroll
+        for (int e = 0; e < PW; ++e) out[e] = att[e];
+        return;
+    }
+    // children of this lane's piece that pass eq 5 and that no location
+    // has covered yet
+    uint64_t need[PW];
+#pragma unroll
+    for (int e = 0; e < PW; ++e) {
+        const int rem = c - 64 * (PW * j + e);
+        const uint64_t vm = rem >= 64 ? ~0ull : (rem > 0 ? (1ull << rem) - 1ull : 0ull);
+        need[e] = jv ? att[e] & vm : 0ull;
+    }
+    for (int l0 = 0; l0 < n_loc; l0 += CPI) {   // uniform
+        uint64_t any_need = 0ull;
+#pragma unroll
+        for (int e = 0; e < PW; ++e) any_need |= need[e];
+        if (__ballot(any_need != 0ull) == 0ull) break;
+        const int l = l0 + g;
+        const bool lv = jv && l < n_loc;
+        uint32_t pos[NM_KP];
+#pragma unroll
+        for (int k = 0; k < NM_KP; ++k) pos[k] = __shfl(pr[k], l < 64 ? l : 0, 64);
+        uint64_t v[NM_KP][PW];
+#pragma unroll
+        for (int k = 0; k < NM_KP; ++k)   // every probe column first, then the ANDs
+            if (k < bloom_k && lv) load(pos[k], v[k]);
+        uint64_t a[PW];
+#pragma unroll
+        for (int e = 0; e < PW; ++e) a[e] = lv ? ~0ull : 0ull;
+#pragma unroll
+        for (int k = 0; k < NM_KP; ++k)
+            if (k < bloom_k && lv)
+#pragma unroll
+                for (int e = 0; e < PW; ++e) a[e] &= v[k][e];
+#pragma unroll
+        for (int e = 0; e < PW; ++e) acc[e] |= a[e];
+        for (int o = LPC; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < PW; ++e) acc[e] |= __shfl_xor(acc[e], o, 64);
+#pragma unroll
+        for (int e = 0; e < PW; ++e) need[e] &= ~acc[e];
+    }
 #pragma unroll
     for (int e = 0; e < PW; ++e) out[e] = att[e] & acc[e];
 }
@@ -504,9 +529,9 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     const int32_t o0 = has_node ? p.off[node] : 0, o1 = has_node ? p.off[node + 1] : 0;
     const int64_t blk = has_node && p.nslice ? p.nslice[node] : -1;
     const uint64_t ubm = p.user_bm[(size_t)b * p.w_bm];
-    uint32_t pr[MAX_KP];
+    uint32_t pr[NM_KP];
 #pragma unroll
-    for (int kk = 0; kk < MAX_KP; ++kk)
+    for (int kk = 0; kk < NM_KP; ++kk)
         pr[kk] = (p.w_bl && lane < p.n_loc && kk < p.bloom_k)
                      ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
                            (uint32_t)(p.bloom_bits - 1)
@@ -561,14 +586,14 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
         if ((wc & 1) == 0) {
             uint64_t pw[2];
-            sliced_pass<2>(bp, wc, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<2>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < (wc >> 1)) {
                 s_pw[2 * lane] = pw[0];
                 s_pw[2 * lane + 1] = pw[1];
             }
         } else {
             uint64_t pw[1];
-            sliced_pass<1>(bp, wc, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<1>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < wc) s_pw[lane] = pw[0];
         }
         if (p.mask_words)
@@ -595,18 +620,18 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const bool room = (uint64_t)old + n8 <= seg_cap;   // false only with a dirty workspace
         const size_t base = ((size_t)b * p.gx + xs) * seg_cap + (seg_cap - old - n8);
         uint32_t e = 0;   // survivors written (uniform)
-        for (int u0 = 0; u0 < wc; u0 += 8) {   // 8 words: every load of the chunk in flight
-            int tk[8], ch[8];
-            bool ok[8];
+        for (int u0 = 0; u0 < wc; u0 += NM_SW) {   // NM_SW words: every load of the chunk in flight
+            int tk[NM_SW], ch[NM_SW];
+            bool ok[NM_SW];
 #pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) {
+            for (int q2 = 0; q2 < NM_SW; ++q2) {
                 const int u = u0 + q2, jj = 64 * u + lane;
                 ok[q2] = u < wc && jj < c && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
                 tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
                 ch[q2] = ok[q2] ? p.child[o0 + jj] : 0;
             }
 #pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) {
+            for (int q2 = 0; q2 < NM_SW; ++q2) {
                 if (u0 + q2 >= wc) break;   // uniform
                 const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
                 if (ok[q2] && p.mask_words)
@@ -647,6 +672,16 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const uint32_t cnt = s_h[i];
         if (cnt) atomicAdd(&gh[i], cnt);
     }
+}
+
+// The node-major pass as its own launch: no row-major state, so it holds
+// fewer registers and less LDS and more of its (latency-bound) workgroups
+// share a CU.
+template <bool BF16>
+__global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
+void k_expand_nm(TailParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];
+    expand_nm<BF16>(p, (int)blockIdx.x, s_dyn);
 }
 
 // One workgroup = up to rows_wg beam rows of one request, taken with a stride
@@ -1806,7 +1841,7 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     p.segback = (uint32_t *)(ws + ly.segback);
     p.n_root = tr.n_root;
     const bool nm_ok = tr.n_root > 0 && tr.node_slice && !tr.kway_offsets && tr.w_bm == 1 &&
-                       (!tr.w_bl || (p.n_loc <= 64 && tr.bloom_k <= MAX_KP)) && a.V >= 512;
+                       (!tr.w_bl || (p.n_loc <= 64 && tr.bloom_k <= NM_KP)) && a.V >= 512;
     p.n_nm = (nm_ok && a.t == 1 && gx <= NM_MAX_GX && 2 * (int64_t)a.M_in >= tr.n_root)
                  ? tr.n_root : 0;
     p.map_write = nm_ok && a.t == 0;
@@ -1839,10 +1874,15 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
 
 hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
     size_t shm = 0;
-    const TailParams p = tail_params(tr, a, &shm);
-    if (p.n_nm)   // the histogram, the bounds, then the wavefronts' areas
-        shm = std::max(shm, sizeof(uint32_t) * ((size_t)NBINS + 4 + (size_t)NM_WAVES * p.nm_wave_dw));
-    const dim3 g1((unsigned)p.nm_wgs + (unsigned)p.gx * (unsigned)a.B);
+    TailParams p = tail_params(tr, a, &shm);
+    if (p.n_nm) {   // the node-major pass first, as its own launch
+        // LDS: the histogram, the bounds, then the wavefronts' areas
+        const size_t shm_nm = sizeof(uint32_t) * ((size_t)NBINS + 4 + (size_t)NM_WAVES * p.nm_wave_dw);
+        if (a.dtype == GR_BF16) k_expand_nm<true><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
+        else k_expand_nm<false><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
+        p.nm_wgs = 0;   // k_expand: row-major workgroups only (n_nm still names the pass's rows)
+    }
+    const dim3 g1((unsigned)p.gx * (unsigned)a.B);
     const bool wide = tr.w_bl >= 64;
     if (a.dtype == GR_BF16) {
         if (wide) k_expand<true, true><<<g1, EXP_THREADS, shm, s>>>(p);
