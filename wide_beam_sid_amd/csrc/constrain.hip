@@ -44,7 +44,8 @@ constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 40
 constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
 constexpr int MAX_KP = 8;             // probes per location held in registers (more: LDS)
 constexpr int NM_KP = 6;              // probes per location of the node-major pass (registers only)
-constexpr int NM_SW = 4;              // node-major survivor words whose loads are in flight together
+constexpr int NM_SW = 8;              // node-major survivor words whose loads are in flight together
+constexpr int NM_LG = 2;              // node-major 16-byte logit pieces per lane loaded up front
 constexpr int LG_BYTES = 8192;        // bf16 logit rows an expand workgroup keeps in LDS
 constexpr int BUF_DWORD3 = 0x00020000;  // buffer descriptor word 3 for gfx9 raw loads
 constexpr int SEL_THREADS = 1024;
@@ -537,34 +538,48 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
                            (uint32_t)(p.bloom_bits - 1)
                      : 0u;
     for (int i = tid; i < NBINS; i += EXP_THREADS) s_h[i] = 0u;
+    // The row's node (whether the row is this pass's), its score and its
+    // first logits need only m, so they are loaded together; a row that
+    // turns out not to be the pass's drops them.
+    const bool in_range = m >= 0 && m < p.M_in && blk >= 0;
+    const size_t r = (size_t)b * p.M_in + (in_range ? m : 0);
+    const int32_t nd = in_range ? p.node_in[r] : -1;
+    const float acc = in_range ? p.acc_in[r] : 0.0f;
+    const bool vec = BF16 && p.vec_logits;
+    const uint4 *x8 = (const uint4 *)((const uint16_t *)p.logits + r * V);
+    uint4 lgv[NM_LG];   // 8 logits per piece, NM_LG pieces per lane up front
+#pragma unroll
+    for (int q = 0; q < NM_LG; ++q) {
+        const int cc = lane + 64 * q;
+        lgv[q] = vec && in_range && cc < (V >> 3) ? x8[cc] : make_uint4(0u, 0u, 0u, 0u);
+    }
     // the request's bound: the same live rows and the same max as k_select
     {
         const BoundLoads bl = bound_load(p, b);
         const float ub = bound_finish(p, b, bl);
         if (lane == 0) s_ubw[wave] = ub;
     }
-    const bool active = m >= 0 && m < p.M_in && blk >= 0 &&
-                        p.node_in[(size_t)b * p.M_in + (m >= 0 && m < p.M_in ? m : 0)] == node;
-    __syncthreads();
-    const float U = fmaxf(fmaxf(s_ubw[0], s_ubw[1]), fmaxf(s_ubw[2], s_ubw[3]));
-    if (active) {   // wave-uniform: the wavefront's row is this pass's
-        const size_t r = (size_t)b * p.M_in + m;
-        const float acc = p.acc_in[r];
+    const bool active = in_range && nd == node;   // wave-uniform
+    const int c = o1 - o0, wc = (c + 63) >> 6;
+    float lse = 0.0f;
+    if (active) {
         // log-sum-exp over all V logits; the logits stay in LDS for the scores
         float mx = -INFINITY;
-        if (BF16 && p.vec_logits) {
-            const uint4 *x8 = (const uint4 *)((const uint16_t *)p.logits + r * V);
-            for (int c = lane; c < (V >> 3); c += 64) {
-                const uint4 u = x8[c];
+        if (vec) {
+            auto take8 = [&](int cc, const uint4 &u) {
                 const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     const float lo = __uint_as_float(w4[h] << 16), hi = __uint_as_float(w4[h] & 0xFFFF0000u);
-                    s_x[8 * c + 2 * h] = lo;
-                    s_x[8 * c + 2 * h + 1] = hi;
+                    s_x[8 * cc + 2 * h] = lo;
+                    s_x[8 * cc + 2 * h + 1] = hi;
                     mx = fmaxf(mx, fmaxf(lo, hi));
                 }
-            }
+            };
+#pragma unroll
+            for (int q = 0; q < NM_LG; ++q)
+                if (lane + 64 * q < (V >> 3)) take8(lane + 64 * q, lgv[q]);
+            for (int cc = lane + 64 * NM_LG; cc < (V >> 3); cc += 64) take8(cc, x8[cc]);
         } else {
             for (int v = lane; v < V; v += 64) {
                 const float x = logit_at<BF16>(p.logits, r * V + v);
@@ -578,10 +593,9 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         if (mx != -INFINITY)
             for (int v = lane; v < V; v += 64) se += __expf(s_x[v] - mx);
         se = wave_sum(se);
-        const float lse = mx + __logf(se);
+        lse = mx + __logf(se);
 
         // eqs 5 and 8 for every child
-        const int c = o1 - o0, wc = (c + 63) >> 6;
         const uint64_t *bp = p.slice_tab + blk;
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
         if ((wc & 1) == 0) {
@@ -598,8 +612,11 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         }
         if (p.mask_words)
             for (int w = lane; w < words; w += 64) s_tm[w] = 0ull;
-        wave_lds_sync();
-
+    }
+    // the wavefronts' bounds and the cleared histogram, needed from here on
+    __syncthreads();
+    const float U = fmaxf(fmaxf(s_ubw[0], s_ubw[1]), fmaxf(s_ubw[2], s_ubw[3]));
+    if (active) {
         // survivors: the passing children, reserved at the back of the
         // segment of the row's row-major workgroup (m mod gx), a multiple of 8
         uint32_t n = 0;
