@@ -54,6 +54,9 @@ CROSS_CASES = [
     (1, 20, 16, 1, 128, "bf16"),     # T_ctx = 1: output = V
     (2, 200, 2, 333, 64, "bf16"),    # 128-row workgroups, ragged last key tile
     (1, 150, 2, 200, 32, "bf16"),    # 128-row workgroups at d_h = 32
+    (2, 300, 2, 333, 64, "bf16"),    # 256-row workgroups, ragged rows and last key tile
+    (1, 512, 2, 256, 32, "bf16"),    # 256-row workgroups at d_h = 32
+    (2, 1024, 2, 512, 64, "bf16"),   # the stress shape's per-request rows and context
 ]
 
 
@@ -73,6 +76,28 @@ def test_cross_attn_parity(B, M, H, T, d, dt):
     if T == 1:
         got = to_np64(out)
         assert np.array_equal(got, np.repeat(_as_f(Vv, dt)[:, :, 0], M, axis=0))
+
+
+@pytest.mark.parametrize("B,M,H,T,d", [(2, 300, 2, 512, 64), (1, 100, 2, 384, 64),
+                                       (1, 70, 2, 640, 32)])
+def test_cross_attn_growing_scores(B, M, H, T, d):
+    """Keys whose scale grows along the context, so that every key tile's
+    max lies far above the running max of the tiles before it: the path
+    that rescales the output and normaliser after the first tile."""
+    gr = _gr()
+    rng = np.random.default_rng(7 * T + M)
+    q = _rand((B * M, H, d), "bf16", rng)
+    K = _rand((B, H, T, d), "bf16", rng)
+    Vv = _rand((B, H, T, d), "bf16", rng)
+    # the tile maxima climb by well over 8 (log2 units) from one 64-key
+    # tile to the next
+    grow = np.linspace(0.05, 30.0, T).astype(np.float32)[None, None, :, None]
+    K = W.f32_to_bf16_bits((_as_f(K, "bf16") * grow).astype(np.float32))
+    out = torch.empty((B * M, H, d), dtype=torch.bfloat16, device="cuda")
+    gr.cross_attn(to_dev(q, "bf16"), to_dev(K, "bf16"), to_dev(Vv, "bf16"), out, B, M)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attn(_as_f(q, "bf16"), _as_f(K, "bf16"), _as_f(Vv, "bf16"), B, M)
+    attn_close(to_np64(out), ref, "bf16", f"growing {B}x{M}x{H}x{T}x{d}")
 
 
 # Few tiles over a long context: the split path (key ranges over several

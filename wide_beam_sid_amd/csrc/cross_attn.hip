@@ -35,9 +35,6 @@ union V8 {
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
-// bf16 pair (1, 1): a dot2 with it sums both halves of a packed pair.
-constexpr bf16x2v kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-
 // Two fp32 values to a bf16 pair (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
@@ -203,11 +200,16 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         }
     }
     f32x4 o[RB][NDB];
+    // osum: the product of an all-ones V^T block with P^T, i.e. the row's
+    // running normaliser (the sum of the weights the product uses), in every
+    // element of each lane of the row
+    f32x4 osum[RB];
     float mrow[RB], lpart[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         mrow[rb] = -INFINITY;
         lpart[rb] = 0.0f;
+        osum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -226,20 +228,26 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
         const int cb = NBUF == 1 ? 0 : cur;   // the buffer holding this tile
         if (first) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
         if (more) load_tile(t0 + TT);
+        // S^T block kb of row block rb: lane holds S[row a][key t0 + kb*16 +
+        // g*4 + i].  Each K fragment read from LDS serves every row block.
+        f32x4 s[RB][4];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) {
+                V8 ka;
+                ka.u = *(const uint4 *)&sK[cb][kb * 16 + a][c * 32 + g * 8];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[rb][kb], 0, 0, 0);
+            }
+        uint32_t pk[RB][4][2];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            // S^T block kb: lane holds S[row a][key t0 + kb*16 + g*4 + i].
-            f32x4 s[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < NDC; ++c) {
-                    V8 ka;
-                    ka.u = *(const uint4 *)&sK[cb][kb * 16 + a][c * 32 + g * 8];
-                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[kb], 0, 0, 0);
-                }
-            }
             // The max runs over the raw dot products (the scale is positive);
             // the running max m is kept in scaled log2 units, and each weight
             // is exp2(s * scale_log2 - m) with the scale folded into one FMA.
@@ -249,49 +257,61 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (RAG && t0 + kb * 16 + g * 4 + i >= T) s[kb][i] = -INFINITY;
-                    tmax = fmaxf(tmax, s[kb][i]);
+                    if (RAG && t0 + kb * 16 + g * 4 + i >= T) s[rb][kb][i] = -INFINITY;
+                    tmax = fmaxf(tmax, s[rb][kb][i]);
                 }
             tmax = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
-            const float mnew = fmaxf(mrow[rb], tmax);
-            const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
-            mrow[rb] = mnew;
-            float lsum = 0.0f;
-            uint32_t pk[4][2];
+            // The running max moves only when a row's tile max exceeds it by
+            // more than 8 (log2 units): the weights then stay below 2^8, and
+            // the rescale of the output and normaliser is skipped on most
+            // tiles.  Any max gives the same normalised output.
+            if (__ballot(tmax > mrow[rb] + 8.0f)) {   // uniform
+                const float mnew = fmaxf(mrow[rb], tmax);
+                const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
+                mrow[rb] = mnew;
+                osum[rb] *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                for (int hp = 0; hp < 2; ++hp) {
-                    const uint32_t w = cvt_bf16x2(
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * hp], scale_log2, -mnew)),
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * hp + 1], scale_log2, -mnew)));
-                    // the normaliser sums the weights the product uses (both
-                    // bf16 halves of w times 1 on one dot2)
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), kOnes2,
-                                                          lsum, false);
-                    pk[kb][hp] = w;
-                }
+                for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
             }
-            lpart[rb] = lpart[rb] * alpha + lsum;
+            const float mcur = mrow[rb];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
-            // O^T += V^T P^T, k step over keys of sub-blocks (2pc, 2pc+1):
-            // slot g*8+i <-> key (2pc)*16 + g*4 + i (i < 4),
-            //                    (2pc+1)*16 + g*4 + i-4 (i >= 4).
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc) {
-                V8 pb;
-                pb.u = make_uint4(pk[2 * pc][0], pk[2 * pc][1], pk[2 * pc + 1][0], pk[2 * pc + 1][1]);
+                for (int hp = 0; hp < 2; ++hp)
+                    pk[rb][kb][hp] = cvt_bf16x2(
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb][2 * hp], scale_log2, -mcur)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb][2 * hp + 1], scale_log2, -mcur)));
+        }
+        // O^T += V^T P^T, k step over keys of sub-blocks (2pc, 2pc+1):
+        // slot g*8+i <-> key (2pc)*16 + g*4 + i (i < 4),
+        //                    (2pc+1)*16 + g*4 + i-4 (i >= 4).
+        // Each V^T fragment read from LDS serves every row block.
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    // A row a <-> d = (a/4)*4*NDB + db*4 + a%4
-                    const int d = (a >> 2) * (4 * NDB) + db * 4 + (a & 3);
-                    const uint2 lo = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16)];
-                    const uint2 hi = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16 + 8)];
-                    V8 va;
-                    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int pc = 0; pc < 2; ++pc) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                // A row a <-> d = (a/4)*4*NDB + db*4 + a%4
+                const int d = (a >> 2) * (4 * NDB) + db * 4 + (a & 3);
+                const uint2 lo = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16)];
+                const uint2 hi = *(const uint2 *)&sVt[cb][d][vc0 ^ (pc * 16 + 8)];
+                V8 va;
+                va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    V8 pb;
+                    pb.u = make_uint4(pk[rb][2 * pc][0], pk[rb][2 * pc][1], pk[rb][2 * pc + 1][0],
+                                      pk[rb][2 * pc + 1][1]);
                     o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.b, pb.b, o[rb][db], 0, 0, 0);
                 }
+            }
+            V8 ones;   // bf16 1.0 in every slot
+            ones.u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                V8 pb;
+                pb.u = make_uint4(pk[rb][2 * pc][0], pk[rb][2 * pc][1], pk[rb][2 * pc + 1][0],
+                                  pk[rb][2 * pc + 1][1]);
+                osum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.b, pb.b, osum[rb], 0, 0, 0);
             }
         }
         if (more) {
@@ -302,6 +322,9 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     };
     key_tile(k0, 0, true);
     for (int t0 = k0 + TT, cur = 1; t0 < k1; t0 += TT, cur ^= 1) key_tile(t0, cur, false);
+    // the normaliser as a partial per lane, summed over the row's 4 lanes below
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lpart[rb] = g == 0 ? osum[rb][0] : 0.0f;
 
     if constexpr (JOINT) {
 #pragma unroll
@@ -589,12 +612,12 @@ __global__ __launch_bounds__(256) void k_joint_f32(const float *__restrict__ q,
     if (act) out[((size_t)r * H + h) * D + lane] = o / l;
 }
 
-// The bf16 tile kernel for head size d, one or two row blocks per
-// wavefront (big) and a ragged last key tile or none (rag).
+// The bf16 tile kernel for head size d, rb = 1, 2 or 4 row blocks per
+// wavefront (4: d_h <= 64 only) and a ragged last key tile or none (rag).
 template <bool JOINT>
 hipError_t launch_cross_tiles(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               uint16_t *out, int M, int H, int T, int d, float sl2, int gxc,
-                              int n, bool big, bool rag, const JointArgs &jn, hipStream_t s) {
+                              int n, int rb, bool rag, const JointArgs &jn, hipStream_t s) {
 #define GR_TILES(DD, RBB, RG) \
     k_cross_bf16<DD, RBB, JOINT, RG><<<n, 256, 0, s>>>(q, k, v, out, M, H, T, sl2, gxc, n, jn)
 #define GR_TILES_R(DD, RBB)        \
@@ -603,9 +626,9 @@ hipError_t launch_cross_tiles(const uint16_t *q, const uint16_t *k, const uint16
         else GR_TILES(DD, RBB, false);    \
     }
     if (d == 32) {
-        if (big) GR_TILES_R(32, 2) else GR_TILES_R(32, 1)
+        if (rb == 4) GR_TILES_R(32, 4) else if (rb == 2) GR_TILES_R(32, 2) else GR_TILES_R(32, 1)
     } else if (d == 64) {
-        if (big) GR_TILES_R(64, 2) else GR_TILES_R(64, 1)
+        if (rb == 4) GR_TILES_R(64, 4) else if (rb == 2) GR_TILES_R(64, 2) else GR_TILES_R(64, 1)
     } else {
         GR_TILES_R(128, 1)
     }
@@ -674,14 +697,16 @@ hipError_t launch_cross_attn(const void *q, const void *k, const void *v, void *
     const float sl2 = 1.4426950408889634f / sqrtf((float)d);
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *oo = (uint16_t *)out;
-    // long key loops amortise the per-workgroup tile loads over 128 rows;
-    // short ones take 64 rows per workgroup for more workgroups in flight
-    // (d_h = 128 always: 128 rows would not fit the registers of two waves
-    // per SIMD)
-    const bool big = T > 2 * TT && d <= 64;
-    const int gxc = (M + (big ? 127 : 63)) / (big ? 128 : 64);
+    // Long key loops amortise each tile's LDS stores and the softmax's
+    // per-tile work over 4 row blocks (256 rows) per workgroup when a request
+    // has that many rows; short ones take 64 rows per workgroup for more
+    // workgroups in flight (d_h = 128 always: more rows would not fit the
+    // registers of two waves per SIMD).
+    const int rb = T > 2 * TT && d <= 64 ? (M >= 256 ? 4 : 2) : 1;
+    const int rows = 64 * rb;
+    const int gxc = (M + rows - 1) / rows;
     const int n = gxc * H * B;
-    return launch_cross_tiles<false>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, big, T % TT != 0,
+    return launch_cross_tiles<false>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, rb, T % TT != 0,
                                      JointArgs{}, s);
 }
 
@@ -710,11 +735,13 @@ hipError_t launch_joint_attn(const void *q, const void *k, const void *v, const 
     jn.fresh_base = fresh_base;
     jn.t = t;
     jn.L = L;
+    // two row blocks per wavefront on long key loops (four cost the beam
+    // positions' loop more than they save)
     const bool big = T > 2 * TT && d <= 64;
     const int gxc = (M + (big ? 127 : 63)) / (big ? 128 : 64);
     const int n = gxc * H * B;
-    return launch_cross_tiles<true>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, big, T % TT != 0,
-                                    jn, s);
+    return launch_cross_tiles<true>(qq, kk, vv, oo, M, H, T, d, sl2, gxc, n, big ? 2 : 1,
+                                    T % TT != 0, jn, s);
 }
 
 hipError_t launch_attn_pair(const void *qx, const void *k_ctx, const void *v_ctx, void *cross_out,
