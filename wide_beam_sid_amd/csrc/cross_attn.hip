@@ -245,13 +245,14 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                 for (int rb = 0; rb < RB; ++rb)
                     s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, qf[rb][c], s[rb][kb], 0, 0, 0);
             }
-        uint32_t pk[RB][4][2];
+        // The max runs over the raw dot products (the scale is positive); the
+        // running max m is kept in scaled log2 units, and each weight is
+        // exp2(s * scale_log2 - m) with the scale folded into one FMA.  Keys
+        // past T exist only in a ragged last tile (RAG).
+        float tm[RB];
+        bool grow = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            // The max runs over the raw dot products (the scale is positive);
-            // the running max m is kept in scaled log2 units, and each weight
-            // is exp2(s * scale_log2 - m) with the scale folded into one FMA.
-            // Keys past T exist only in a ragged last tile (RAG).
             float tmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -260,19 +261,28 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                     if (RAG && t0 + kb * 16 + g * 4 + i >= T) s[rb][kb][i] = -INFINITY;
                     tmax = fmaxf(tmax, s[rb][kb][i]);
                 }
-            tmax = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
-            // The running max moves only when a row's tile max exceeds it by
-            // more than 8 (log2 units): the weights then stay below 2^8, and
-            // the rescale of the output and normaliser is skipped on most
-            // tiles.  Any max gives the same normalised output.
-            if (__ballot(tmax > mrow[rb] + 8.0f)) {   // uniform
-                const float mnew = fmaxf(mrow[rb], tmax);
+            tm[rb] = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
+            grow = grow || tm[rb] > mrow[rb] + 8.0f;
+        }
+        // The running maxima move only when a row's tile max exceeds its
+        // running max by more than 8 (log2 units): the weights then stay
+        // below 2^8, and the rescale of the outputs and normalisers is
+        // skipped on most tiles (one uniform branch for the wavefront's row
+        // blocks).  Any max gives the same normalised output.
+        if (__ballot(grow)) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float mnew = fmaxf(mrow[rb], tm[rb]);
                 const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
                 mrow[rb] = mnew;
                 osum[rb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
             }
+        }
+        uint32_t pk[RB][4][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
             const float mcur = mrow[rb];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
