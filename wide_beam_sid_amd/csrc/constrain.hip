@@ -109,6 +109,13 @@ struct TailParams {
     int nm_wgs;         // node-major workgroups at the front of k_expand's grid
 };
 
+// Lane-wise minimum of two pairs of unsigned 16-bit values.
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
 // Bin of a candidate score below the request bound U (monotone
 // non-increasing in the score: a better score never lands in a later bin).
 __device__ __forceinline__ int score_bin(float s, float U) {
@@ -1545,20 +1552,25 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     const int thr = s_thr, below = s_below;
     uint32_t n_surv = 0;   // the total of the segment counts
     for (int w = 0; w < SEL_THREADS / 64; ++w) n_surv += s_wsum2[w];
-    // offset of the f-th survivor (sub-segments concatenated) in the
-    // request's keys
-    auto surv = [&](uint32_t f) -> uint32_t {
+    // the sub-segment holding the f-th survivor (sub-segments concatenated)
+    auto sub_of = [&](uint32_t f) -> int {
         int lo = 0, hi = nsub;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (s_segpre[mid] <= f) lo = mid;
             else hi = mid;
         }
+        return lo;
+    };
+    // offset in the request's keys of the f-th survivor, in sub-segment lo
+    // (survivors s_segpre[lo] .. s_segpre[lo + 1] - 1)
+    auto off_in = [&](int lo, uint32_t f) -> uint32_t {
         if (!two) return (uint32_t)(lo * seg_cap) + (f - s_segpre[lo]);
         const uint32_t seg = (uint32_t)lo >> 1;
         if (!(lo & 1)) return (uint32_t)(seg * seg_cap) + (f - s_segpre[lo]);
         return (uint32_t)((seg + 1) * seg_cap) - (s_segpre[lo + 1] - f);   // a back part
     };
+    auto surv = [&](uint32_t f) -> uint32_t { return off_in(sub_of(f), f); };
 
     // 2. Survivors of bins below the threshold go to their bin's slots;
     //    members of the threshold bin are buffered.  Zero keys are the
@@ -1588,25 +1600,45 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
         const uint16_t *bins = p.sbin + (size_t)b * gx * seg_cap;
         const uint32_t n_oct = n_surv >> 3;
         for (uint32_t o0 = 0; o0 < n_oct; o0 += 4 * SEL_THREADS) {
+            // wavefront w takes 256 consecutive groups, lane l groups l,
+            // l + 64, l + 128, l + 192 of them (each load instruction reads
+            // 1 KB in one piece); a lane searches for its sub-segment once
+            // and again only when a later group lies past it
             uint32_t src[4];
             uint4 bv[4];
+            int lo = -1;
+            uint32_t end = 0;   // first survivor past sub-segment lo
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t oo = o0 + u * SEL_THREADS + tid;
-                src[u] = oo < n_oct ? surv(8 * oo) : 0xFFFFFFFFu;
-                bv[u] = oo < n_oct ? *(const uint4 *)(bins + src[u])
-                                   : make_uint4(~0u, ~0u, ~0u, ~0u);
+                const uint32_t oo = o0 + (uint32_t)wave * 256u + (uint32_t)u * 64u + (uint32_t)lane;
+                src[u] = 0xFFFFFFFFu;
+                if (oo < n_oct) {
+                    const uint32_t f = 8 * oo;
+                    if (lo < 0 || f >= end) {
+                        lo = sub_of(f);
+                        end = s_segpre[lo + 1];
+                    }
+                    src[u] = off_in(lo, f);
+                }
+                bv[u] = src[u] != 0xFFFFFFFFu ? *(const uint4 *)(bins + src[u])
+                                              : make_uint4(~0u, ~0u, ~0u, ~0u);
             }
             // bit 8u + e: survivor src[u] + e is a candidate; one LDS atomic
-            // per wavefront reserves the wavefront's list positions
+            // per wavefront reserves the wavefront's list positions.  Few
+            // groups hold a candidate: the smallest of a group's 8 bins
+            // (packed 16-bit minima) decides whether its bits are looked at.
             uint32_t msk = 0u;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t wv[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+                const uint32_t m2 = pk_min_u16(pk_min_u16(bv[u].x, bv[u].y), pk_min_u16(bv[u].z, bv[u].w));
+                const uint32_t mn = min(m2 & 0xFFFFu, m2 >> 16);
+                if (src[u] != 0xFFFFFFFFu && mn <= (uint32_t)thr) {
+                    const uint32_t wv[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int bn = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                    if (src[u] != 0xFFFFFFFFu && bn <= thr) msk |= 1u << (8 * u + e);
+                    for (int e = 0; e < 8; ++e) {
+                        const int bn = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        if (bn <= thr) msk |= 1u << (8 * u + e);
+                    }
                 }
             }
             const uint32_t nmine = (uint32_t)__popc(msk);
