@@ -1806,6 +1806,176 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The whole tail in one launch when every request enters with one beam row
+// (the root step: M_0 = 1).  A row has at most V <= 1024 children, so one
+// 1024-thread workgroup per request holds all of its candidates: the row's
+// log-sum-exp over its V logits, eqs 5 and 8 for every child (the bit-sliced
+// block through one wavefront, as in the node-major pass, or a plain test
+// per child when the node has no block), the candidates placed in order in
+// LDS (score descending, then token ascending, as the histogram select
+// orders them: a histogram of score bins below the row's own score, its
+// prefix sums, then a rank by counting inside each bin) and the reorder
+// writes -- no global histogram, no segments and no second launch.  The same
+// masks, scores and selection as k_expand + k_select.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(SEL_THREADS) void k_root(TailParams p) {
+    __shared__ uint64_t s_key[SEL_THREADS];
+    __shared__ int32_t s_ch[SEL_THREADS];
+    __shared__ float s_x[SEL_THREADS];          // the row's logits (V <= 1024)
+    __shared__ uint64_t s_pw[SEL_THREADS / 64];  // pass words of a bit-sliced block
+    __shared__ uint64_t s_tm[SEL_THREADS / 64];  // kept tokens (debug outputs)
+    __shared__ float s_red[SEL_THREADS / 64];
+    __shared__ uint32_t s_bin[NBINS];            // bin counts, then bin starts, then ends
+    __shared__ uint32_t s_wsum[SEL_THREADS / 64];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int V = p.V, k = p.k_out, words = (V + 63) >> 6;
+    const size_t r = (size_t)b;   // one row per request
+    const int node = p.node_in[r];
+    const bool live = node >= 0 && node < p.num_nodes;
+    int32_t o0 = 0, c = 0;
+    int64_t blk = -1;
+    if (live) {
+        o0 = p.off[node];
+        c = p.off[node + 1] - o0;
+        if (p.nslice) blk = p.nslice[node];
+    }
+    const float acc = live ? p.acc_in[r] : 0.0f;
+    const uint64_t ubm = p.user_bm[(size_t)b * p.w_bm];   // one attribute word
+    // thread v: logit v; thread j: child entry j (both loaded up front)
+    const float x = live && tid < V ? logit_at<BF16>(p.logits, r * V + tid) : -INFINITY;
+    const int32_t tk = tid < c ? (int32_t)p.tok[o0 + tid] : 0;
+    const int32_t chv = tid < c ? p.child[o0 + tid] : -1;
+    if (tid < V) s_x[tid] = x;
+    if (tid < words) s_tm[tid] = 0ull;
+    for (int i = tid; i < NBINS; i += SEL_THREADS) s_bin[i] = 0u;
+
+    // eqs 5 and 8 for every child of a bit-sliced block: wavefront 0
+    if (live && blk >= 0 && c > 0 && wave == 0) {
+        uint32_t pr[NM_KP];
+#pragma unroll
+        for (int kk = 0; kk < NM_KP; ++kk)
+            pr[kk] = (p.w_bl && lane < p.n_loc && kk < p.bloom_k)
+                         ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
+                               (uint32_t)(p.bloom_bits - 1)
+                         : 0u;
+        const int wc = (c + 63) >> 6;
+        const uint64_t *bp = p.slice_tab + blk;
+        const int bl_pos = p.w_bl ? p.bloom_bits : 0;
+        if ((wc & 1) == 0) {
+            uint64_t pw[2];
+            sliced_pass<2>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            if (lane < (wc >> 1)) {
+                s_pw[2 * lane] = pw[0];
+                s_pw[2 * lane + 1] = pw[1];
+            }
+        } else {
+            uint64_t pw[1];
+            sliced_pass<1>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            if (lane < wc) s_pw[lane] = pw[0];
+        }
+    }
+    // the row's log-sum-exp over all V logits
+    float mx = wave_max(x);
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    mx = s_red[0];
+    for (int w = 1; w < SEL_THREADS / 64; ++w) mx = fmaxf(mx, s_red[w]);
+    float se = wave_sum(tid < V && mx != -INFINITY ? __expf(x - mx) : 0.0f);
+    __syncthreads();   // every wavefront has read the maxima
+    if (lane == 0) s_red[wave] = se;
+    __syncthreads();
+    se = 0.0f;
+    for (int w = 0; w < SEL_THREADS / 64; ++w) se += s_red[w];
+    const float lse = mx + __logf(se);
+
+    // child tid: kept (CD + GTM) and its key
+    bool kept = false;
+    if (tid < c) {
+        if (blk >= 0) {
+            kept = (s_pw[tid >> 6] >> (tid & 63)) & 1ull;
+        } else {   // no block: the child's own rows (eq 5, then eq 8)
+            const int64_t e = (int64_t)o0 + tid;
+            const uint64_t row_bm = p.ent_bm ? p.ent_bm[e] : p.bm_tab[p.bmi[e]];
+            kept = (row_bm & ubm) == ubm;
+            if (kept && p.w_bl) {
+                const uint64_t *row = p.bl_tab + (size_t)p.bli[e] * p.w_bl;
+                bool any = false;
+                for (int l = 0; l < p.n_loc && !any; ++l) {
+                    bool all = true;
+                    for (int q = 0; q < p.bloom_k && all; ++q) {
+                        const uint32_t pos = p.user_probes[((size_t)b * p.n_loc + l) * p.bloom_k + q] &
+                                             (uint32_t)(p.bloom_bits - 1);
+                        all = (row[pos >> 6] >> (pos & 63)) & 1ull;
+                    }
+                    any = all;
+                }
+                kept = any;
+            }
+        }
+    }
+    const float sc = kept ? acc + (s_x[tk] - lse) : -INFINITY;
+    if (kept && p.mask_words) atomicOr((unsigned long long *)&s_tm[tk >> 6], 1ull << (tk & 63));
+    const uint64_t key = kept && sc > -INFINITY ? make_key(sc, (uint32_t)tk) : 0ull;   // flat index = token
+    // the candidate's bin below the row's own score (every candidate's
+    // score is at most it), counted in LDS
+    const int bin = key ? score_bin(sc, acc) : 0;
+    if (key) atomicAdd(&s_bin[bin], 1u);
+    __syncthreads();
+    if (p.mask_words) {   // debug outputs of the row
+        if (p.dbg_mask)
+            for (int w = tid; w < words; w += SEL_THREADS) p.dbg_mask[r * words + w] = s_tm[w];
+        if (p.dbg_scores && tid < V) {
+            const bool kv = (s_tm[tid >> 6] >> (tid & 63)) & 1ull;
+            p.dbg_scores[r * V + tid] = kv ? acc + (x - lse) : -INFINITY;
+        }
+    }
+    // exclusive prefix of the bins (thread tid: bins 2 tid and 2 tid + 1)
+    static_assert(NBINS == 2 * SEL_THREADS, "two bins per thread");
+    const uint32_t b0 = s_bin[2 * tid], b1 = s_bin[2 * tid + 1];
+    const uint32_t inc = wave_incl_sum(b0 + b1);   // inclusive prefix over the lanes
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    uint32_t pre = 0, n = 0;
+    for (int w = 0; w < SEL_THREADS / 64; ++w) {
+        pre += w < wave ? s_wsum[w] : 0u;
+        n += s_wsum[w];
+    }
+    pre += inc - b0 - b1;
+    s_bin[2 * tid] = pre;             // bin starts: each thread writes its own two bins
+    s_bin[2 * tid + 1] = pre + b0;
+    __syncthreads();
+    // each candidate into its bin's run (the bins' starts become their ends),
+    // then its rank inside the run by counting
+    if (key) {
+        const uint32_t pos = atomicAdd(&s_bin[bin], 1u);
+        s_key[pos] = key;
+    }
+    __syncthreads();
+    int slot = -1;
+    if (key) {
+        const int end = (int)s_bin[bin], start = bin ? (int)s_bin[bin - 1] : 0;
+        slot = start + count_above(s_key, start, end, key);
+    }
+    __syncthreads();   // every rank is counted before the keys move
+    if (key) {
+        s_key[slot] = key;   // slots 0 .. n - 1, in order
+        s_ch[slot] = chv;
+    }
+    __syncthreads();
+
+    // slot i: the i-th best candidate, dead past the last one
+    for (int i = tid; i < k; i += SEL_THREADS) {
+        const bool lv = (uint32_t)i < n;
+        const uint64_t ki = lv ? s_key[i] : 0ull;
+        const int32_t ch = lv ? s_ch[i] : -1;
+        write_slot(p, b, (size_t)b * k + i, lv, ki, ch);
+        // the next step's node-major pass finds the row at each root child
+        if (p.map_write && lv && ch >= 1 && ch <= p.n_root) p.inv[(size_t)b * V + ch - 1] = i;
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -1948,6 +2118,24 @@ hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStre
     const TailParams p = tail_params(tr, a, &shm);
     k_select<<<a.B, SEL_THREADS, 0, s>>>(p);
     return hipGetLastError();
+}
+
+hipError_t launch_tail(const TrieDev &tr, const gr_tail_args &a, hipStream_t s) {
+    // one row per request: the whole tail in one workgroup per request
+    // (one attribute word, the node-major pass's probe registers)
+    const bool one = a.M_in == 1 && a.V <= SEL_THREADS && a.k_out <= SEL_THREADS &&
+                     !tr.kway_offsets && tr.w_bm == 1 &&
+                     (!tr.w_bl || (a.n_loc <= 64 && tr.bloom_k <= NM_KP));
+    if (one) {
+        size_t shm = 0;
+        const TailParams p = tail_params(tr, a, &shm);
+        if (a.dtype == GR_BF16) k_root<true><<<a.B, SEL_THREADS, 0, s>>>(p);
+        else k_root<false><<<a.B, SEL_THREADS, 0, s>>>(p);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_constrain(tr, a, s);
+    if (e == hipSuccess) e = launch_topk_reorder(tr, a, s);
+    return e;
 }
 
 // ---------------------------------------------------------------------------

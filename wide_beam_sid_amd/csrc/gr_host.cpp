@@ -1217,8 +1217,7 @@ gr_status gr_topk_reorder(const gr_trie *trie, const gr_tail_args *a, void *stre
 gr_status gr_constrain_topk(const gr_trie *trie, const gr_tail_args *a, void *stream) {
     gr_status st = check_tail(trie, a, "gr_constrain_topk");
     if (st) return st;
-    hipError_t e = launch_constrain(trie->d, *a, (hipStream_t)stream);
-    if (e == hipSuccess) e = launch_topk_reorder(trie->d, *a, (hipStream_t)stream);
+    hipError_t e = launch_tail(trie->d, *a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk launch");
     return GR_OK;
 }
@@ -1246,8 +1245,7 @@ gr_status gr_constrain_topk_noalloc(const gr_trie *trie, const gr_tail_args *a, 
     // the scratch keeps the last call's contents: clear the histograms this
     // call accumulates into (the rest is written before it is read)
     e = launch_clear_hist(ws, b.B, hs);
-    if (e == hipSuccess) e = launch_constrain(trie->d, b, hs);
-    if (e == hipSuccess) e = launch_topk_reorder(trie->d, b, hs);
+    if (e == hipSuccess) e = launch_tail(trie->d, b, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_constrain_topk_noalloc launch");
     return GR_OK;
 }
@@ -1310,8 +1308,7 @@ static gr_status launch_step(const gr_trie *trie, const gr_step_args *s, void *s
                              a.t, a.L, a.dtype, s->self_out, hs);
         if (e != hipSuccess) return hip_fail(e, "gr_decode_step attention launch");
     }
-    e = launch_constrain(trie->d, a, hs);
-    if (e == hipSuccess) e = launch_topk_reorder(trie->d, a, hs);
+    e = launch_tail(trie->d, a, hs);
     if (e != hipSuccess) return hip_fail(e, "gr_decode_step constrain/top-k launch");
     return GR_OK;
 }

@@ -132,5 +132,8 @@ hipError_t launch_clear_hist(void *ws, int B, hipStream_t s);   // also the back
 // Records msg as the message gr_last_error returns and returns st.
 gr_status report(gr_status st, const char *msg);
 hipError_t launch_topk_reorder(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
+// Both halves, or, when every request enters with one row, one launch that
+// does the whole tail.
+hipError_t launch_tail(const TrieDev &tr, const gr_tail_args &a, hipStream_t s);
 
 }  // namespace gr
