@@ -503,6 +503,29 @@ def test_constrain_topk_parity(name, seed, B, M_in, k_out, t, dead, lmode, amode
     run_tail(w, seed, M_in, k_out, t, dead, lmode, amode, B=B)
 
 
+ROOT_CASES = [
+    # workload, seed, B, k_out, t, dead, logits, acc -- one beam row per request
+    ("main_50k", 1, 4, 37, 0, 0.0, "normal", "normal"),       # fewer slots than candidates
+    ("main_50k", 2, 6, 1024, 1, 0.3, "normal", "normal"),     # rows at depth-1 nodes, some dead
+    ("main_50k", 3, 4, 200, 2, 0.0, "normal", "normal"),      # deeper nodes, most without a block
+    ("main_50k", 1, 3, 1000, 0, 0.0, "equal", "normal"),      # every candidate in one score bin
+    ("stress_20k", 4, 3, 1024, 0, 0.0, "normal", "normal"),   # V = 1024 at the root
+    ("stress_20k", 5, 4, 300, 1, 0.25, "normal", "normal"),
+    ("long_50k", 3, 2, 900, 0, 0.0, "normal", "normal"),      # bitmask-only matcher
+    ("tiny", 1, 2, 8, 1, 0.0, "normal", "normal"),            # fp32, nodes without blocks
+    ("wide_attr", 5, 2, 64, 0, 0.0, "normal", "normal"),      # three attribute words: two launches
+]
+
+
+@pytest.mark.parametrize("name,seed,B,k_out,t,dead,lmode,amode", ROOT_CASES)
+def test_one_row_per_request_tail(name, seed, B, k_out, t, dead, lmode, amode):
+    """One beam row per request, as at the root: the tail runs as one launch
+    that places the candidates in order in LDS.  Checked against the oracle
+    as the two-launch tail is, with dead rows, nodes with and without a
+    bit-sliced block, ties in one score bin and more candidates than slots."""
+    run_tail(TAIL_WORKLOADS[name], seed, 1, k_out, t, dead, lmode, amode, B=B)
+
+
 def test_constrain_topk_workspace_error():
     gr = _gr()
     w = TAIL_WORKLOADS["tiny"]
