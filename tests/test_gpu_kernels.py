@@ -678,3 +678,35 @@ def test_node_major_pass_sparse_and_dense_bloom_rows(geo):
     run_tail(w, 4, 1024, 1000, 1, B=2, staged=True, between=back_counts,
              node_in=root["node_out"], acc_in=root["acc_out"])
     assert seen and seen[0] > 0, seen
+
+
+def test_node_major_pass_drops_candidates_past_a_full_cutoff():
+    """A node-major wavefront drops the candidates past the first cutoff bin
+    that already holds k counted survivors of its request (on large launches
+    the workgroups that run later see such counts).  Here the counters are
+    preset to the final counts of an identical run -- the most any
+    wavefront could see -- and every output still matches the oracle."""
+    w = TAIL_WORKLOADS["stress_20k"]
+    gr = _gr()
+    ws = _workspace(gr.constrain_topk_workspace(2, 1024, w.V, 1024))
+    root = run_tail(w, 4, 1, 1024, 0, 0.0, B=2)
+    hists = []
+
+    def grab(wsv):   # after gr_constrain: the requests' histograms
+        hists.append(wsv[:2 * 2048 * 4].view(torch.int32).cpu().numpy().reshape(2, 2048).copy())
+
+    # a narrow top-k (5 of a few hundred survivors per request), so that a
+    # tight cutoff holds k
+    kw = dict(B=2, staged=True, node_in=root["node_out"], acc_in=root["acc_out"])
+    first = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
+    cuts = np.stack([hists[0][:, :16 << j].sum(axis=1) for j in range(7)], axis=1)
+    assert ((cuts >= 5) & (cuts < cuts[:, -1:])).any(), cuts   # some are past it somewhere
+    # the counters sit after the histograms (8 MiB) and the back counts (4 MiB)
+    off = 4 * 2048 * 1024 + 4 * 1024 * 1024
+    cnt = torch.zeros(2 * 8, dtype=torch.int32)
+    cnt.view(2, 8)[:, :7] = torch.from_numpy(cuts.astype(np.int32))
+    ws[off:off + 2 * 8 * 4].copy_(cnt.view(torch.uint8).to("cuda"))
+    second = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
+    assert hists[1].sum() < hists[0].sum()   # candidates were dropped
+    for k in ("parent_out", "token_out", "node_out", "acc_out"):
+        assert np.array_equal(first[k], second[k]), k

@@ -105,6 +105,7 @@ struct TailParams {
     int n_root;         // the root's children are nodes 1..n_root
     int32_t *inv;       // [B, V]: beam row of request b at root child v + 1
     uint32_t *segback;  // [MAX_B, NM_MAX_GX]: node-major survivors at the back of each segment
+    uint32_t *cut;      // [MAX_B, NCUT]: survivors counted at or below the cutoff bins
     int nm_wave_dw;     // LDS dwords per node-major wavefront
     int nm_wgs;         // node-major workgroups at the front of k_expand's grid
 };
@@ -526,7 +527,8 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     const int V = p.V, words = (V + 63) >> 6;
     uint32_t *s_h = (uint32_t *)s_dyn;                                    // survivors' bins
     float *s_ubw = (float *)(s_h + NBINS);                                // bound per wavefront
-    float *s_x = s_ubw + 4 + (size_t)wave * p.nm_wave_dw;                 // the row's logits
+    uint32_t *s_cp = (uint32_t *)(s_ubw + 4);                             // cutoff counts per wavefront
+    float *s_x = s_ubw + 4 + 4 * NCUT + (size_t)wave * p.nm_wave_dw;      // the row's logits
     uint64_t *s_pw = (uint64_t *)(s_x + ((V + 3) & ~3));                   // pass words
     uint64_t *s_tm = s_pw + ((words + 1) & ~1);                            // kept tokens (debug)
 
@@ -569,6 +571,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     const bool active = in_range && nd == node;   // wave-uniform
     const int c = o1 - o0, wc = (c + 63) >> 6;
     float lse = 0.0f;
+    uint32_t cutv = 0u;
     if (active) {
         // log-sum-exp over all V logits; the logits stay in LDS for the scores
         float mx = -INFINITY;
@@ -605,6 +608,8 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         // eqs 5 and 8 for every child
         const uint64_t *bp = p.slice_tab + blk;
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
+        // the request's cutoff counters, read now, used at the survivors
+        cutv = lane < NCUT_USED ? p.cut[(size_t)b * NCUT + lane] : 0u;
         if ((wc & 1) == 0) {
             uint64_t pw[2];
             sliced_pass<2>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
@@ -624,17 +629,39 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     __syncthreads();
     const float U = fmaxf(fmaxf(s_ubw[0], s_ubw[1]), fmaxf(s_ubw[2], s_ubw[3]));
     if (active) {
-        // survivors: the passing children, reserved at the back of the
-        // segment of the row's row-major workgroup (m mod gx), a multiple of 8
+        // Candidates past the first cutoff bin that already holds k counted
+        // survivors of the request cannot be selected (the threshold bin lies
+        // at or below that cutoff, and the counts only grow), so they are
+        // dropped: written nowhere, counted nowhere.
+        const uint64_t full = __ballot(lane < NCUT_USED && cutv >= (uint32_t)p.k_out);
+        const int bmax = full ? (16 << __builtin_ctzll(full)) - 1 : NBINS;
+        // pass 1: the kept children of each word (their mask replaces the
+        // word's pass bits) and their number
         uint32_t n = 0;
-        for (int u = lane; u < wc; u += 64) {
-            uint64_t w = s_pw[u];
-            const int rem = c - 64 * u;
-            if (rem < 64) w &= (1ull << rem) - 1ull;
-            n += (uint32_t)__popcll(w);
+        for (int u0 = 0; u0 < wc; u0 += NM_SW) {   // NM_SW words: every load of the chunk in flight
+            int tk[NM_SW];
+            bool ok[NM_SW];
+#pragma unroll
+            for (int q2 = 0; q2 < NM_SW; ++q2) {
+                const int u = u0 + q2, jj = 64 * u + lane;
+                ok[q2] = u < wc && jj < c && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
+                tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < NM_SW; ++q2) {
+                if (u0 + q2 >= wc) break;   // uniform
+                const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
+                if (ok[q2] && p.mask_words)
+                    atomicOr((unsigned long long *)&s_tm[tk[q2] >> 6], 1ull << (tk[q2] & 63));
+                const bool keep = ok[q2] && sc > -INFINITY && score_bin(sc, U) <= bmax;
+                const uint64_t bal = __ballot(keep);
+                if (lane == 0) s_pw[u0 + q2] = bal;
+                n += (uint32_t)__popcll(bal);
+            }
         }
-        n = wave_incl_sum(n);
-        n = __builtin_amdgcn_readlane(n, 63);
+        wave_lds_sync();
+        // pass 2: the kept children reserved at the back of the segment of
+        // the row's row-major workgroup (m mod gx), a multiple of 8
         const uint32_t n8 = (n + 7u) & ~7u;
         const int xs = m % p.gx;
         const uint64_t seg_cap = (uint64_t)p.seg_cap;
@@ -644,13 +671,13 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const bool room = (uint64_t)old + n8 <= seg_cap;   // false only with a dirty workspace
         const size_t base = ((size_t)b * p.gx + xs) * seg_cap + (seg_cap - old - n8);
         uint32_t e = 0;   // survivors written (uniform)
-        for (int u0 = 0; u0 < wc; u0 += NM_SW) {   // NM_SW words: every load of the chunk in flight
+        for (int u0 = 0; u0 < wc && e < n; u0 += NM_SW) {
             int tk[NM_SW], ch[NM_SW];
             bool ok[NM_SW];
 #pragma unroll
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 const int u = u0 + q2, jj = 64 * u + lane;
-                ok[q2] = u < wc && jj < c && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
+                ok[q2] = u < wc && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
                 tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
                 ch[q2] = ok[q2] ? p.child[o0 + jj] : 0;
             }
@@ -658,11 +685,8 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 if (u0 + q2 >= wc) break;   // uniform
                 const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
-                if (ok[q2] && p.mask_words)
-                    atomicOr((unsigned long long *)&s_tm[tk[q2] >> 6], 1ull << (tk[q2] & 63));
-                const bool sel = ok[q2] && sc > -INFINITY;
-                const uint64_t bal = __ballot(sel);
-                if (sel && room) {
+                const uint64_t bal = __ballot(ok[q2]);
+                if (ok[q2] && room) {
                     const size_t idx = base + e + lanes_below(bal);
                     const int bin = score_bin(sc, U);
                     p.skey[idx] = make_key(sc, (uint32_t)(m * V + tk[q2]));
@@ -689,12 +713,26 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
                 }
         }
     }
-    // the workgroup's bins into the request's histogram
+    // the workgroup's bins into the request's histogram, and its counts at
+    // or below each cutoff bin into the request's counters
     __syncthreads();
     uint32_t *gh = p.hist + (size_t)b * NBINS;
+    uint32_t cp[NCUT_USED] = {};
     for (int i = tid; i < NBINS; i += EXP_THREADS) {
         const uint32_t cnt = s_h[i];
         if (cnt) atomicAdd(&gh[i], cnt);
+#pragma unroll
+        for (int j = 0; j < NCUT_USED; ++j) cp[j] += i <= (16 << j) - 1 ? cnt : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < NCUT_USED; ++j) {
+        const uint32_t t = wave_incl_sum(cp[j]);   // the wavefront's total in lane 63
+        if (lane == 63) s_cp[wave * NCUT + j] = t;
+    }
+    __syncthreads();
+    if (tid < NCUT_USED) {
+        const uint32_t t = s_cp[tid] + s_cp[NCUT + tid] + s_cp[2 * NCUT + tid] + s_cp[3 * NCUT + tid];
+        if (t) atomicAdd(&p.cut[(size_t)b * NCUT + tid], t);
     }
 }
 
@@ -1518,6 +1556,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(TailParams p) {
     for (int i = 0; i < PER; ++i) part += c[i];
 #pragma unroll
     for (int i = 0; i < PER; ++i) gh[tid * PER + i] = 0u;
+    if (tid < NCUT) p.cut[(size_t)b * NCUT + tid] = 0u;   // zero for the next call too
     for (int i = tid; i < MAX_K; i += SEL_THREADS) s_key[i] = 0ull;
     uint32_t inc = part;
     inc = wave_incl_sum(inc);   // inclusive prefix over the lanes
@@ -2058,6 +2097,7 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     // even with the row-major pass, which is kept there.
     p.inv = (int32_t *)(ws + ly.inv);
     p.segback = (uint32_t *)(ws + ly.segback);
+    p.cut = (uint32_t *)(ws + ly.cut);
     p.n_root = tr.n_root;
     const bool nm_ok = tr.n_root > 0 && tr.node_slice && !tr.kway_offsets && tr.w_bm == 1 &&
                        (!tr.w_bl || (p.n_loc <= 64 && tr.bloom_k <= NM_KP)) && a.V >= 512;
@@ -2096,7 +2136,7 @@ hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_
     TailParams p = tail_params(tr, a, &shm);
     if (p.n_nm) {   // the node-major pass first, as its own launch
         // LDS: the histogram, the bounds, then the wavefronts' areas
-        const size_t shm_nm = sizeof(uint32_t) * ((size_t)NBINS + 4 + (size_t)NM_WAVES * p.nm_wave_dw);
+        const size_t shm_nm = sizeof(uint32_t) * ((size_t)NBINS + 4 + 4 * NCUT + (size_t)NM_WAVES * p.nm_wave_dw);
         if (a.dtype == GR_BF16) k_expand_nm<true><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
         else k_expand_nm<false><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
         p.nm_wgs = 0;   // k_expand: row-major workgroups only (n_nm still names the pass's rows)
@@ -2187,6 +2227,9 @@ hipError_t launch_clear_hist(void *ws, int B, hipStream_t s) {
     const size_t n2 = (size_t)B * NM_MAX_GX * sizeof(uint32_t) / sizeof(uint4);
     k_clear_u32x4<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
         (uint4 *)((char *)ws + ly.segback), n2);
+    const size_t n3 = (size_t)B * NCUT * sizeof(uint32_t) / sizeof(uint4);
+    k_clear_u32x4<<<(unsigned)((n3 + 255) / 256), 256, 0, s>>>(
+        (uint4 *)((char *)ws + ly.cut), n3);
     return hipGetLastError();
 }
 

@@ -1125,13 +1125,14 @@ TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V) {
     const size_t nseg = (size_t)B * l.shape.gx;
     const size_t nsurv = nseg * (size_t)l.shape.seg_cap;
     size_t o = 0;
-    // the histograms and the segments' back counts first, at fixed places
-    // and sizes: each region is only ever used as what it is and stays zero
-    // between calls of any shape; then the inverse map of root children at a
+    // the histograms, the segments' back counts and the cutoff counters
+    // first, at fixed places and sizes: each region is only ever used as what
+    // it is and stays zero between calls of any shape; then the inverse map of root children at a
     // fixed place, so that a decode's steps (several M_in) find it where the
     // previous step left it (its content is checked before use)
     l.hist = o;    o = al(o + sizeof(uint32_t) * (size_t)NBINS * MAX_B);
     l.segback = o; o = al(o + sizeof(uint32_t) * (size_t)MAX_B * NM_MAX_GX);
+    l.cut = o;     o = al(o + sizeof(uint32_t) * (size_t)MAX_B * NCUT);
     l.inv = o;     o = al(o + sizeof(int32_t) * (size_t)B * V);
     l.segcnt = o;  o = al(o + sizeof(uint32_t) * nseg);
     l.skey = o;   o = al(o + sizeof(uint64_t) * nsurv);

@@ -85,8 +85,13 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
 }
 
 // Workspace carving of gr_constrain_topk (byte offsets).
+// Per request, NCUT counters of survivors already counted in the histogram
+// at or below cutoff bins (16 << j) - 1, j < NCUT_USED (the node-major pass
+// drops candidates past the first cutoff that already holds k survivors).
+constexpr int NCUT = 8;
+constexpr int NCUT_USED = 7;
 struct TailWsLayout {
-    size_t hist, segback, inv, segcnt, skey, schild, sbin, total;
+    size_t hist, segback, cut, inv, segcnt, skey, schild, sbin, total;
     TailShape shape;
 };
 TailWsLayout tail_ws_layout(int32_t B, int32_t M_in, int32_t V);
