@@ -636,7 +636,10 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const uint64_t full = __ballot(lane < NCUT_USED && cutv >= (uint32_t)p.k_out);
         const int bmax = full ? (16 << __builtin_ctzll(full)) - 1 : NBINS;
         // pass 1: the kept children of each word (their mask replaces the
-        // word's pass bits) and their number
+        // word's pass bits) and their number.  A node with all V children has
+        // tokens 0 .. V - 1 in entry order (sorted and distinct), so its
+        // tokens need no loads.
+        const bool dense = c == V;
         uint32_t n = 0;
         for (int u0 = 0; u0 < wc; u0 += NM_SW) {   // NM_SW words: every load of the chunk in flight
             int tk[NM_SW];
@@ -645,7 +648,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 const int u = u0 + q2, jj = 64 * u + lane;
                 ok[q2] = u < wc && jj < c && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
-                tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
+                tk[q2] = ok[q2] ? (dense ? jj : p.tok[o0 + jj]) : 0;
             }
 #pragma unroll
             for (int q2 = 0; q2 < NM_SW; ++q2) {
@@ -678,7 +681,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 const int u = u0 + q2, jj = 64 * u + lane;
                 ok[q2] = u < wc && ((s_pw[u < wc ? u : 0] >> lane) & 1ull);
-                tk[q2] = ok[q2] ? p.tok[o0 + jj] : 0;
+                tk[q2] = ok[q2] ? (dense ? jj : p.tok[o0 + jj]) : 0;
                 ch[q2] = ok[q2] ? p.child[o0 + jj] : 0;
             }
 #pragma unroll
