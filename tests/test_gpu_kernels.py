@@ -100,6 +100,28 @@ def test_cross_attn_growing_scores(B, M, H, T, d):
     attn_close(to_np64(out), ref, "bf16", f"growing {B}x{M}x{H}x{T}x{d}")
 
 
+@pytest.mark.parametrize("B,M,H,T,d", [(2, 300, 2, 512, 64), (1, 100, 2, 384, 64)])
+def test_cross_attn_single_key_spikes(B, M, H, T, d):
+    """One key per 64-key tile scaled up, at a random place in the tile,
+    with the scale climbing from tile to tile: a row's tile max then sits
+    in one of the four lanes that hold the row's scores, and only that
+    lane's own max passes the running max by more than 8 (log2 units)."""
+    gr = _gr()
+    rng = np.random.default_rng(11 * T + M)
+    q = _rand((B * M, H, d), "bf16", rng)
+    K = _as_f(_rand((B, H, T, d), "bf16", rng), "bf16")
+    Vv = _rand((B, H, T, d), "bf16", rng)
+    for t0 in range(0, T, 64):
+        j = t0 + int(rng.integers(0, min(64, T - t0)))
+        K[:, :, j, :] *= 2.0 + 6.0 * t0 / 64
+    K = W.f32_to_bf16_bits(K.astype(np.float32))
+    out = torch.empty((B * M, H, d), dtype=torch.bfloat16, device="cuda")
+    gr.cross_attn(to_dev(q, "bf16"), to_dev(K, "bf16"), to_dev(Vv, "bf16"), out, B, M)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attn(_as_f(q, "bf16"), _as_f(K, "bf16"), _as_f(Vv, "bf16"), B, M)
+    attn_close(to_np64(out), ref, "bf16", f"spiky {B}x{M}x{H}x{T}x{d}")
+
+
 # Few tiles over a long context: the split path (key ranges over several
 # workgroups, merged with a log-sum-exp) against the oracle, and the same
 # inputs without a workspace.

@@ -204,10 +204,19 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     // running normaliser (the sum of the weights the product uses), in every
     // element of each lane of the row
     f32x4 osum[RB];
-    float mrow[RB], lpart[RB];
+    // VOTE (four row blocks per wavefront, where the vector work of the
+    // tile bounds the kernel): the growth test on each lane's own maximum;
+    // with fewer row blocks the test on the row's maximum measured faster.
+    constexpr bool VOTE = RB >= 4;
+    // thr: the raw dot product above which a row's weights would pass 2^8
+    // (mrow + 8 in scaled log2 units; a rounding either way only moves a
+    // rescale by a tile, and any running max gives the same output)
+    float mrow[RB], lpart[RB], thr[RB];
+    const float inv_scale = 1.0f / scale_log2;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         mrow[rb] = -INFINITY;
+        thr[rb] = -INFINITY;
         lpart[rb] = 0.0f;
         osum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -261,18 +270,31 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
                     if (RAG && t0 + kb * 16 + g * 4 + i >= T) s[rb][kb][i] = -INFINITY;
                     tmax = fmaxf(tmax, s[rb][kb][i]);
                 }
-            tm[rb] = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
-            grow = grow || tm[rb] > mrow[rb] + 8.0f;
+            if constexpr (VOTE) {
+                tm[rb] = tmax;   // this lane's part of the row (raw dot products)
+                grow = grow || tmax > thr[rb];
+            } else {
+                tm[rb] = pair32_max(pair16_max(tmax)) * scale_log2;   // over the row's 4 lanes g
+                grow = grow || tm[rb] > mrow[rb] + 8.0f;
+            }
         }
         // The running maxima move only when a row's tile max exceeds its
         // running max by more than 8 (log2 units): the weights then stay
         // below 2^8, and the rescale of the outputs and normalisers is
         // skipped on most tiles (one uniform branch for the wavefront's row
-        // blocks).  Any max gives the same normalised output.
+        // blocks).  Any max gives the same normalised output.  VOTE: a row's
+        // tile max exceeds the bound exactly when one of its four lanes'
+        // maxima does, so the test votes on the lanes' own maxima and the
+        // maxima over the row's lanes are taken only on the (rare) rescale.
         if (__ballot(grow)) {
+            if constexpr (VOTE)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)   // over the row's 4 lanes g
+                    tm[rb] = pair32_max(pair16_max(tm[rb])) * scale_log2;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const float mnew = fmaxf(mrow[rb], tm[rb]);
+                thr[rb] = (mnew + 8.0f) * inv_scale;
                 const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - mnew);
                 mrow[rb] = mnew;
                 osum[rb] *= alpha;
