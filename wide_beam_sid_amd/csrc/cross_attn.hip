@@ -94,24 +94,22 @@ __device__ __forceinline__ void cross_rows(const uint16_t *__restrict__ q,
     // barrier per tile guards the buffer before they are stored.
     static_assert(NBUF == 1 || NBUF == 2, "tile buffers");
     __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TT][D + PAD];
-    // V^T as key pairs, row d of TT / 2 dwords.  SWZ (one row block, short
-    // key loops): the dword column is XORed with vsw(d), so the 16 rows a
-    // 16-lane pass of the P.V product reads (d & 3 and d / (D / 4) varying)
-    // fall on distinct banks.  Otherwise rows are padded by 4 dwords, which
-    // leaves 4-way conflicts but measured faster with two row blocks over
-    // long key loops.
-    constexpr bool SWZ = RB == 1;
-    constexpr int VP = TT / 2 + (SWZ ? 0 : PAD / 2);   // dwords per V^T row
+    // V^T as key pairs, row d of TT / 2 dwords, the dword column XORed with
+    // vsw(d), so the 16 rows a 16-lane pass of the P.V product reads (d & 3
+    // and d / (D / 4) varying) fall on distinct banks (padded rows instead
+    // leave 4-way conflicts: rows d and d + 16 of a 36-dword pitch share a
+    // bank; the joint kernel at two row blocks ran 2-3% faster swizzled).
+    constexpr int VP = TT / 2;   // dwords per V^T row
     __shared__ __attribute__((aligned(16))) uint32_t sVt[NBUF][D][VP];
     static_assert(D == 32 || D == 64 || D == 128, "head size");
     constexpr int SHV = D == 32 ? 3 : (D == 64 ? 4 : 5);   // log2(D / 4)
-    auto vsw = [](int d) { return SWZ ? 2 * ((d & 3) | (((d >> SHV) & 3) << 2)) : 0; };
+    auto vsw = [](int d) { return 2 * ((d & 3) | (((d >> SHV) & 3) << 2)); };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, a = lane & 15;
-    // every row d this lane reads in the P.V product has vsw(d) = 2a (SWZ)
-    // or 0, so its four V^T dword columns are vc0 ^ {0, 8, 16, 24}
-    const int vc0 = (2 * g) ^ (RB == 1 ? 2 * a : 0);
+    // every row d this lane reads in the P.V product has vsw(d) = 2a, so
+    // its four V^T dword columns are vc0 ^ {0, 8, 16, 24}
+    const int vc0 = (2 * g) ^ (2 * a);
     const int mbase = bx * ROWS + wave * RB * 16;
     const size_t kvbase = ((size_t)b * H + h) * (size_t)T * D;
 
