@@ -43,7 +43,7 @@ constexpr int EXP_THREADS = 64 * EXP_WAVES;
 constexpr int STAGE_BYTES = 4352;     // Bloom rows staged per wavefront (8 x 4096 bits)
 constexpr int NQ = 16;                // 8-byte staging registers per lane (wide rows)
 constexpr int MAX_KP = 8;             // probes per location held in registers (more: LDS)
-constexpr int NM_KP = 6;              // probes per location of the node-major pass (registers only)
+constexpr int NM_KP = 5;              // probes per location of the node-major pass (registers only)
 constexpr int NM_SW = 8;              // node-major survivor words whose loads are in flight together
 constexpr int NM_LG = 2;              // node-major 16-byte logit pieces per lane loaded up front
 constexpr int LG_BYTES = 8192;        // bf16 logit rows an expand workgroup keeps in LDS
@@ -419,11 +419,12 @@ __device__ __forceinline__ int nth_set_bit(uint64_t x, int n) {
 // of shallow nodes -- unions over many ads -- are dense enough that the
 // first group usually covers every child.  Lanes j < NP of slot 0 return the
 // pass bits of words PW j .. PW j + PW - 1.  ubm: the request's attribute
-// word; pr: this lane's location's probe positions (lane l = location l <
-// n_loc <= 64).
+// word; spr: the wavefront's copy in LDS of the user's probe positions,
+// location l's at spr[l * NM_KP ..] (l < n_loc <= 64; written by the
+// wavefront and ordered before the call).
 template <int PW>
 __device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int c, int bl_pos,
-                                            uint64_t ubm, const uint32_t pr[NM_KP], int n_loc,
+                                            uint64_t ubm, const uint16_t *spr, int n_loc,
                                             int bloom_k, bool bloom, int lane, uint64_t out[PW]) {
     const int NP = wc / PW;
     int lg = 0;
@@ -484,7 +485,7 @@ __device__ __forceinline__ void sliced_pass(const uint64_t *blk, int wc, int c, 
         const bool lv = jv && l < n_loc;
         uint32_t pos[NM_KP];
 #pragma unroll
-        for (int k = 0; k < NM_KP; ++k) pos[k] = __shfl(pr[k], l < 64 ? l : 0, 64);
+        for (int k = 0; k < NM_KP; ++k) pos[k] = spr[(lv ? l : 0) * NM_KP + k];
         uint64_t v[NM_KP][PW];
 #pragma unroll
         for (int k = 0; k < NM_KP; ++k)   // every probe column first, then the ANDs
@@ -528,9 +529,18 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     uint32_t *s_h = (uint32_t *)s_dyn;                                    // survivors' bins
     float *s_ubw = (float *)(s_h + NBINS);                                // bound per wavefront
     uint32_t *s_cp = (uint32_t *)(s_ubw + 4);                             // cutoff counts per wavefront
-    float *s_x = s_ubw + 4 + 4 * NCUT + (size_t)wave * p.nm_wave_dw;      // the row's logits
-    uint64_t *s_pw = (uint64_t *)(s_x + ((V + 3) & ~3));                   // pass words
+    // the row's logits, as they are in memory (bf16 bits or fp32), then
+    // the pass words
+    float *s_xw = s_ubw + 4 + 4 * NCUT + (size_t)wave * p.nm_wave_dw;
+    float *s_x = s_xw;
+    uint16_t *s_xh = (uint16_t *)s_xw;
+    uint64_t *s_pw = (uint64_t *)(s_xw + (BF16 ? ((V + 7) & ~7) / 2 : (V + 3) & ~3));
+    auto xat = [&](int v) -> float {   // logit v of the row
+        if constexpr (BF16) return bf16_to_f32(s_xh[v]);
+        else return s_x[v];
+    };
     uint64_t *s_tm = s_pw + ((words + 1) & ~1);                            // kept tokens (debug)
+    uint16_t *s_pr = (uint16_t *)(s_tm + ((words + 1) & ~1));              // the user's probes
 
     // The row the map names, the node's children and block, the request's
     // attribute word and this lane's location's probes: one round of loads.
@@ -539,13 +549,14 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     const int32_t o0 = has_node ? p.off[node] : 0, o1 = has_node ? p.off[node + 1] : 0;
     const int64_t blk = has_node && p.nslice ? p.nslice[node] : -1;
     const uint64_t ubm = p.user_bm[(size_t)b * p.w_bm];
-    uint32_t pr[NM_KP];
+    // lane l: location l's probe positions, into the wavefront's LDS copy
+    // (below 2^16: bloom_bits <= 65536), where the block test reads them
 #pragma unroll
     for (int kk = 0; kk < NM_KP; ++kk)
-        pr[kk] = (p.w_bl && lane < p.n_loc && kk < p.bloom_k)
-                     ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
-                           (uint32_t)(p.bloom_bits - 1)
-                     : 0u;
+        s_pr[lane * NM_KP + kk] = (uint16_t)((p.w_bl && lane < p.n_loc && kk < p.bloom_k)
+                                                 ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
+                                                       (uint32_t)(p.bloom_bits - 1)
+                                                 : 0u);
     for (int i = tid; i < NBINS; i += EXP_THREADS) s_h[i] = 0u;
     // The row's node (whether the row is this pass's), its score and its
     // first logits need only m, so they are loaded together; a row that
@@ -577,14 +588,11 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         float mx = -INFINITY;
         if (vec) {
             auto take8 = [&](int cc, const uint4 &u) {
+                *(uint4 *)(s_xh + 8 * cc) = u;
                 const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float lo = __uint_as_float(w4[h] << 16), hi = __uint_as_float(w4[h] & 0xFFFF0000u);
-                    s_x[8 * cc + 2 * h] = lo;
-                    s_x[8 * cc + 2 * h + 1] = hi;
-                    mx = fmaxf(mx, fmaxf(lo, hi));
-                }
+                for (int h = 0; h < 4; ++h)
+                    mx = fmaxf(mx, fmaxf(__uint_as_float(w4[h] << 16), __uint_as_float(w4[h] & 0xFFFF0000u)));
             };
 #pragma unroll
             for (int q = 0; q < NM_LG; ++q)
@@ -592,16 +600,22 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
             for (int cc = lane + 64 * NM_LG; cc < (V >> 3); cc += 64) take8(cc, x8[cc]);
         } else {
             for (int v = lane; v < V; v += 64) {
-                const float x = logit_at<BF16>(p.logits, r * V + v);
-                s_x[v] = x;
-                mx = fmaxf(mx, x);
+                if constexpr (BF16) {
+                    const uint16_t u = ((const uint16_t *)p.logits)[r * V + v];
+                    s_xh[v] = u;
+                    mx = fmaxf(mx, bf16_to_f32(u));
+                } else {
+                    const float x = logit_at<BF16>(p.logits, r * V + v);
+                    s_x[v] = x;
+                    mx = fmaxf(mx, x);
+                }
             }
         }
         mx = wave_max(mx);
         wave_lds_sync();
         float se = 0.0f;
         if (mx != -INFINITY)
-            for (int v = lane; v < V; v += 64) se += __expf(s_x[v] - mx);
+            for (int v = lane; v < V; v += 64) se += __expf(xat(v) - mx);
         se = wave_sum(se);
         lse = mx + __logf(se);
 
@@ -610,16 +624,17 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
         // the request's cutoff counters, read now, used at the survivors
         cutv = lane < NCUT_USED ? p.cut[(size_t)b * NCUT + lane] : 0u;
+        wave_lds_sync();   // the probes' LDS copy
         if ((wc & 1) == 0) {
             uint64_t pw[2];
-            sliced_pass<2>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<2>(bp, wc, c, bl_pos, ubm, s_pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < (wc >> 1)) {
                 s_pw[2 * lane] = pw[0];
                 s_pw[2 * lane + 1] = pw[1];
             }
         } else {
             uint64_t pw[1];
-            sliced_pass<1>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<1>(bp, wc, c, bl_pos, ubm, s_pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < wc) s_pw[lane] = pw[0];
         }
         if (p.mask_words)
@@ -653,7 +668,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
 #pragma unroll
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 if (u0 + q2 >= wc) break;   // uniform
-                const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
+                const float sc = ok[q2] ? acc + (xat(tk[q2]) - lse) : -INFINITY;
                 if (ok[q2] && p.mask_words)
                     atomicOr((unsigned long long *)&s_tm[tk[q2] >> 6], 1ull << (tk[q2] & 63));
                 const bool keep = ok[q2] && sc > -INFINITY && score_bin(sc, U) <= bmax;
@@ -687,7 +702,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
 #pragma unroll
             for (int q2 = 0; q2 < NM_SW; ++q2) {
                 if (u0 + q2 >= wc) break;   // uniform
-                const float sc = ok[q2] ? acc + (s_x[tk[q2]] - lse) : -INFINITY;
+                const float sc = ok[q2] ? acc + (xat(tk[q2]) - lse) : -INFINITY;
                 const uint64_t bal = __ballot(ok[q2]);
                 if (ok[q2] && room) {
                     const size_t idx = base + e + lanes_below(bal);
@@ -712,7 +727,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
             if (p.dbg_scores)
                 for (int v = lane; v < V; v += 64) {
                     const bool kept = (s_tm[v >> 6] >> (v & 63)) & 1ull;
-                    p.dbg_scores[r * V + v] = kept ? acc + (s_x[v] - lse) : -INFINITY;
+                    p.dbg_scores[r * V + v] = kept ? acc + (xat(v) - lse) : -INFINITY;
                 }
         }
     }
@@ -743,7 +758,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
 // fewer registers and less LDS and more of its (latency-bound) workgroups
 // share a CU.
 template <bool BF16>
-__global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(7)))
 void k_expand_nm(TailParams p) {
     extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];
     expand_nm<BF16>(p, (int)blockIdx.x, s_dyn);
@@ -1866,6 +1881,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_root(TailParams p) {
     __shared__ uint64_t s_key[SEL_THREADS];
     __shared__ int32_t s_ch[SEL_THREADS];
     __shared__ float s_x[SEL_THREADS];          // the row's logits (V <= 1024)
+    __shared__ uint16_t s_pr[64 * NM_KP];       // the user's probe positions (block test)
     __shared__ uint64_t s_pw[SEL_THREADS / 64];  // pass words of a bit-sliced block
     __shared__ uint64_t s_tm[SEL_THREADS / 64];  // kept tokens (debug outputs)
     __shared__ float s_red[SEL_THREADS / 64];
@@ -1895,26 +1911,26 @@ __global__ __launch_bounds__(SEL_THREADS) void k_root(TailParams p) {
 
     // eqs 5 and 8 for every child of a bit-sliced block: wavefront 0
     if (live && blk >= 0 && c > 0 && wave == 0) {
-        uint32_t pr[NM_KP];
 #pragma unroll
         for (int kk = 0; kk < NM_KP; ++kk)
-            pr[kk] = (p.w_bl && lane < p.n_loc && kk < p.bloom_k)
-                         ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
-                               (uint32_t)(p.bloom_bits - 1)
-                         : 0u;
+            s_pr[lane * NM_KP + kk] = (uint16_t)((p.w_bl && lane < p.n_loc && kk < p.bloom_k)
+                                                     ? p.user_probes[((size_t)b * p.n_loc + lane) * p.bloom_k + kk] &
+                                                           (uint32_t)(p.bloom_bits - 1)
+                                                     : 0u);
+        wave_lds_sync();
         const int wc = (c + 63) >> 6;
         const uint64_t *bp = p.slice_tab + blk;
         const int bl_pos = p.w_bl ? p.bloom_bits : 0;
         if ((wc & 1) == 0) {
             uint64_t pw[2];
-            sliced_pass<2>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<2>(bp, wc, c, bl_pos, ubm, s_pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < (wc >> 1)) {
                 s_pw[2 * lane] = pw[0];
                 s_pw[2 * lane + 1] = pw[1];
             }
         } else {
             uint64_t pw[1];
-            sliced_pass<1>(bp, wc, c, bl_pos, ubm, pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
+            sliced_pass<1>(bp, wc, c, bl_pos, ubm, s_pr, p.n_loc, p.bloom_k, p.w_bl != 0, lane, pw);
             if (lane < wc) s_pw[lane] = pw[0];
         }
     }
@@ -2110,7 +2126,10 @@ TailParams tail_params(const TrieDev &tr, const gr_tail_args &a, size_t *shm_out
     {   // per node-major wavefront: its row's logits, pass words and kept
         // tokens; workgroups: 8 * ceil(groups / 8) * B (see expand_nm)
         const int words = (a.V + 63) / 64;
-        p.nm_wave_dw = ((a.V + 3) & ~3) + 4 * ((words + 1) & ~1);
+        // the row's logits as stored (bf16 or fp32), then the pass words and
+        // kept tokens
+        const int xdw = a.dtype == GR_BF16 ? ((a.V + 7) & ~7) / 2 : (a.V + 3) & ~3;
+        p.nm_wave_dw = xdw + 4 * ((words + 1) & ~1) + 32 * NM_KP;
         const int ngroups = (p.n_nm + NM_WAVES - 1) / NM_WAVES;
         p.nm_wgs = p.n_nm ? 8 * ((ngroups + 7) / 8) * a.B : 0;
     }
