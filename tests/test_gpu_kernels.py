@@ -721,13 +721,16 @@ def test_node_major_pass_drops_candidates_past_a_full_cutoff():
     # tight cutoff holds k
     kw = dict(B=2, staged=True, node_in=root["node_out"], acc_in=root["acc_out"])
     first = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
-    cuts = np.stack([hists[0][:, :16 << j].sum(axis=1) for j in range(7)], axis=1)
+    # the cutoff bins: 15, 22, 31, 45, 63, ..., 735, 1023 (about sqrt(2) apart)
+    bins = [((23 << (j >> 1)) if j & 1 else (16 << (j >> 1))) - 1 for j in range(13)]
+    cuts = np.stack([hists[0][:, :b + 1].sum(axis=1) for b in bins], axis=1)
     assert ((cuts >= 5) & (cuts < cuts[:, -1:])).any(), cuts   # some are past it somewhere
-    # the counters sit after the histograms (8 MiB) and the back counts (4 MiB)
+    # the 16 counters of each request sit after the histograms (8 MiB) and
+    # the back counts (4 MiB)
     off = 4 * 2048 * 1024 + 4 * 1024 * 1024
-    cnt = torch.zeros(2 * 8, dtype=torch.int32)
-    cnt.view(2, 8)[:, :7] = torch.from_numpy(cuts.astype(np.int32))
-    ws[off:off + 2 * 8 * 4].copy_(cnt.view(torch.uint8).to("cuda"))
+    cnt = torch.zeros(2 * 16, dtype=torch.int32)
+    cnt.view(2, 16)[:, :13] = torch.from_numpy(cuts.astype(np.int32))
+    ws[off:off + 2 * 16 * 4].copy_(cnt.view(torch.uint8).to("cuda"))
     second = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
     assert hists[1].sum() < hists[0].sum()   # candidates were dropped
     for k in ("parent_out", "token_out", "node_out", "acc_out"):

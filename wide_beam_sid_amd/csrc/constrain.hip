@@ -649,7 +649,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         // at or below that cutoff, and the counts only grow), so they are
         // dropped: written nowhere, counted nowhere.
         const uint64_t full = __ballot(lane < NCUT_USED && cutv >= (uint32_t)p.k_out);
-        const int bmax = full ? (16 << __builtin_ctzll(full)) - 1 : NBINS;
+        const int bmax = full ? cut_bin(__builtin_ctzll(full)) : NBINS;
         // pass 1: the kept children of each word (their mask replaces the
         // word's pass bits) and their number.  A node with all V children has
         // tokens 0 .. V - 1 in entry order (sorted and distinct), so its
@@ -740,7 +740,7 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         const uint32_t cnt = s_h[i];
         if (cnt) atomicAdd(&gh[i], cnt);
 #pragma unroll
-        for (int j = 0; j < NCUT_USED; ++j) cp[j] += i <= (16 << j) - 1 ? cnt : 0u;
+        for (int j = 0; j < NCUT_USED; ++j) cp[j] += i <= cut_bin(j) ? cnt : 0u;
     }
 #pragma unroll
     for (int j = 0; j < NCUT_USED; ++j) {

@@ -86,10 +86,14 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
 
 // Workspace carving of gr_constrain_topk (byte offsets).
 // Per request, NCUT counters of survivors already counted in the histogram
-// at or below cutoff bins (16 << j) - 1, j < NCUT_USED (the node-major pass
+// at or below cutoff bins cut_bin(j), j < NCUT_USED (the node-major pass
 // drops candidates past the first cutoff that already holds k survivors).
-constexpr int NCUT = 8;
-constexpr int NCUT_USED = 7;
+// The cutoffs grow by about sqrt(2): 15, 22, 31, 45, 63, 91, ..., 735, 1023.
+constexpr int NCUT = 16;
+constexpr int NCUT_USED = 13;
+__host__ __device__ constexpr int cut_bin(int j) {
+    return ((j & 1) ? (23 << (j >> 1)) : (16 << (j >> 1))) - 1;
+}
 struct TailWsLayout {
     size_t hist, segback, cut, inv, segcnt, skey, schild, sbin, total;
     TailShape shape;
