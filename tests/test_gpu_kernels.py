@@ -702,12 +702,25 @@ def test_node_major_pass_sparse_and_dense_bloom_rows(geo):
     assert seen and seen[0] > 0, seen
 
 
+def _cutoff_preset(cuts, k_out):
+    """The 16 cutoff counters of each request (bytes): k_out at the first of
+    the 13 cutoffs whose count in cuts reaches k_out, zero elsewhere."""
+    cnt = torch.zeros((cuts.shape[0], 16), dtype=torch.int32)
+    for b in range(cuts.shape[0]):
+        full = np.nonzero(cuts[b] >= k_out)[0]
+        if full.size:
+            cnt[b, int(full[0])] = k_out
+    return cnt.reshape(-1).view(torch.uint8)
+
+
 def test_node_major_pass_drops_candidates_past_a_full_cutoff():
     """A node-major wavefront drops the candidates past the first cutoff bin
     that already holds k counted survivors of its request (on large launches
-    the workgroups that run later see such counts).  Here the counters are
-    preset to the final counts of an identical run -- the most any
-    wavefront could see -- and every output still matches the oracle."""
+    the workgroups that run later see such counts).  Here the counter of the
+    first cutoff that an identical run's histogram fills to k is preset to k
+    (those survivors exist, so k of them will be counted there; presetting
+    every final count would count them twice), so every wavefront drops
+    past it, and every output still matches the oracle."""
     w = TAIL_WORKLOADS["stress_20k"]
     gr = _gr()
     ws = _workspace(gr.constrain_topk_workspace(2, 1024, w.V, 1024))
@@ -728,9 +741,7 @@ def test_node_major_pass_drops_candidates_past_a_full_cutoff():
     # the 16 counters of each request sit after the histograms (8 MiB) and
     # the back counts (4 MiB)
     off = 4 * 2048 * 1024 + 4 * 1024 * 1024
-    cnt = torch.zeros(2 * 16, dtype=torch.int32)
-    cnt.view(2, 16)[:, :13] = torch.from_numpy(cuts.astype(np.int32))
-    ws[off:off + 2 * 16 * 4].copy_(cnt.view(torch.uint8).to("cuda"))
+    ws[off:off + 2 * 16 * 4].copy_(_cutoff_preset(cuts, 5).to("cuda"))
     second = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
     assert hists[1].sum() < hists[0].sum()   # candidates were dropped
     for k in ("parent_out", "token_out", "node_out", "acc_out"):
