@@ -681,6 +681,26 @@ def test_node_major_step_after_map_writes_of_other_batch_sizes():
     assert all(n > 0 for n in seen), seen         # the pass took rows every time
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_node_major_pass_logit_dtypes(dtype):
+    """The node-major pass keeps its row's logits in LDS as they are in
+    memory: bf16 bits (16-byte pieces) or fp32 values, at different LDS
+    pitches.  The step after the root with fp32 and with bf16 logits,
+    against the oracle; the back counts show the pass took rows."""
+    w = TAIL_WORKLOADS["stress_20k"].scaled(dtype=dtype)
+    seen = []
+
+    def back_counts(ws):
+        off = 4 * 2048 * 1024
+        seen.append(int(ws[off:off + 4 * 1024 * 4].view(torch.int32).count_nonzero()))
+
+    _workspace(_gr().constrain_topk_workspace(2, 1024, w.V, 1024))   # kept by both calls
+    root = run_tail(w, 5, 1, 1024, 0, 0.0, B=2)
+    run_tail(w, 5, 1024, 1000, 1, B=2, staged=True, between=back_counts,
+             node_in=root["node_out"], acc_in=root["acc_out"])
+    assert seen and seen[0] > 0, seen
+
+
 @pytest.mark.parametrize("geo", [(1, 64), (200, 256)])
 def test_node_major_pass_sparse_and_dense_bloom_rows(geo):
     """The node-major pass stops testing a row's locations once every child
