@@ -755,8 +755,10 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
 }
 
 // The node-major pass as its own launch: no row-major state, so it holds
-// fewer registers and less LDS and more of its (latency-bound) workgroups
-// share a CU.
+// fewer registers and less LDS and more of its workgroups share a CU:
+// seven wavefronts per SIMD (72 registers, about 20 KB of LDS per
+// workgroup at V = 1024); at eight the spills cost more than the pass
+// gains, the memory system being what then bounds it.
 template <bool BF16>
 __global__ __launch_bounds__(EXP_THREADS) __attribute__((amdgpu_waves_per_eu(7)))
 void k_expand_nm(TailParams p) {
