@@ -732,24 +732,35 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
         }
     }
     // the workgroup's bins into the request's histogram, and its counts at
-    // or below each cutoff bin into the request's counters
+    // or below each cutoff bin into the request's counters: an inclusive
+    // prefix sum over bins 0 .. 1023 (4 consecutive bins per thread), left
+    // in place of those bins and read at the cutoffs
+    static_assert(4 * EXP_THREADS == 1024 && NBINS >= 1024, "cutoff bins");
     __syncthreads();
     uint32_t *gh = p.hist + (size_t)b * NBINS;
-    uint32_t cp[NCUT_USED] = {};
     for (int i = tid; i < NBINS; i += EXP_THREADS) {
         const uint32_t cnt = s_h[i];
         if (cnt) atomicAdd(&gh[i], cnt);
-#pragma unroll
-        for (int j = 0; j < NCUT_USED; ++j) cp[j] += i <= cut_bin(j) ? cnt : 0u;
     }
+    uint32_t c4[4], t4 = 0;
 #pragma unroll
-    for (int j = 0; j < NCUT_USED; ++j) {
-        const uint32_t t = wave_incl_sum(cp[j]);   // the wavefront's total in lane 63
-        if (lane == 63) s_cp[wave * NCUT + j] = t;
+    for (int q = 0; q < 4; ++q) {
+        c4[q] = s_h[4 * tid + q];
+        t4 += c4[q];
+    }
+    const uint32_t inc = wave_incl_sum(t4);   // inclusive prefix over the lanes
+    if (lane == 63) s_cp[wave] = inc;
+    __syncthreads();   // every bin read (above and by the merge), the wave totals written
+    uint32_t run = inc - t4;
+    for (int w = 0; w < wave; ++w) run += s_cp[w];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        run += c4[q];
+        s_h[4 * tid + q] = run;
     }
     __syncthreads();
     if (tid < NCUT_USED) {
-        const uint32_t t = s_cp[tid] + s_cp[NCUT + tid] + s_cp[2 * NCUT + tid] + s_cp[3 * NCUT + tid];
+        const uint32_t t = s_h[cut_bin(tid)];
         if (t) atomicAdd(&p.cut[(size_t)b * NCUT + tid], t);
     }
 }
