@@ -723,9 +723,9 @@ def test_node_major_pass_sparse_and_dense_bloom_rows(geo):
 
 
 def _cutoff_preset(cuts, k_out):
-    """The 16 cutoff counters of each request (bytes): k_out at the first of
-    the 13 cutoffs whose count in cuts reaches k_out, zero elsewhere."""
-    cnt = torch.zeros((cuts.shape[0], 16), dtype=torch.int32)
+    """The 32 cutoff counters of each request (bytes): k_out at the first of
+    the 25 cutoffs whose count in cuts reaches k_out, zero elsewhere."""
+    cnt = torch.zeros((cuts.shape[0], 32), dtype=torch.int32)
     for b in range(cuts.shape[0]):
         full = np.nonzero(cuts[b] >= k_out)[0]
         if full.size:
@@ -754,14 +754,14 @@ def test_node_major_pass_drops_candidates_past_a_full_cutoff():
     # tight cutoff holds k
     kw = dict(B=2, staged=True, node_in=root["node_out"], acc_in=root["acc_out"])
     first = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
-    # the cutoff bins: 15, 22, 31, 45, 63, ..., 735, 1023 (about sqrt(2) apart)
-    bins = [((23 << (j >> 1)) if j & 1 else (16 << (j >> 1))) - 1 for j in range(13)]
+    # the cutoff bins: 15, 18, 21, 26, 31, ..., 863, 1023 (about 2^(1/4) apart)
+    bins = [(16 << (j >> 2)) * (64, 76, 91, 108)[j & 3] // 64 - 1 for j in range(25)]
     cuts = np.stack([hists[0][:, :b + 1].sum(axis=1) for b in bins], axis=1)
     assert ((cuts >= 5) & (cuts < cuts[:, -1:])).any(), cuts   # some are past it somewhere
-    # the 16 counters of each request sit after the histograms (8 MiB) and
+    # the 32 counters of each request sit after the histograms (8 MiB) and
     # the back counts (4 MiB)
     off = 4 * 2048 * 1024 + 4 * 1024 * 1024
-    ws[off:off + 2 * 16 * 4].copy_(_cutoff_preset(cuts, 5).to("cuda"))
+    ws[off:off + 2 * 32 * 4].copy_(_cutoff_preset(cuts, 5).to("cuda"))
     second = run_tail(w, 4, 1024, 5, 1, between=grab, **kw)
     assert hists[1].sum() < hists[0].sum()   # candidates were dropped
     for k in ("parent_out", "token_out", "node_out", "acc_out"):

@@ -528,10 +528,10 @@ __device__ __forceinline__ void expand_nm(const TailParams &p, int k, uint64_t *
     const int V = p.V, words = (V + 63) >> 6;
     uint32_t *s_h = (uint32_t *)s_dyn;                                    // survivors' bins
     float *s_ubw = (float *)(s_h + NBINS);                                // bound per wavefront
-    uint32_t *s_cp = (uint32_t *)(s_ubw + 4);                             // cutoff counts per wavefront
+    uint32_t *s_cp = (uint32_t *)(s_ubw + 4);                             // histogram sum per wavefront
     // the row's logits, as they are in memory (bf16 bits or fp32), then
     // the pass words
-    float *s_xw = s_ubw + 4 + 4 * NCUT + (size_t)wave * p.nm_wave_dw;
+    float *s_xw = s_ubw + 8 + (size_t)wave * p.nm_wave_dw;
     float *s_x = s_xw;
     uint16_t *s_xh = (uint16_t *)s_xw;
     uint64_t *s_pw = (uint64_t *)(s_xw + (BF16 ? ((V + 7) & ~7) / 2 : (V + 3) & ~3));
@@ -2170,8 +2170,9 @@ hipError_t launch_constrain(const TrieDev &tr, const gr_tail_args &a, hipStream_
     size_t shm = 0;
     TailParams p = tail_params(tr, a, &shm);
     if (p.n_nm) {   // the node-major pass first, as its own launch
-        // LDS: the histogram, the bounds, then the wavefronts' areas
-        const size_t shm_nm = sizeof(uint32_t) * ((size_t)NBINS + 4 + 4 * NCUT + (size_t)NM_WAVES * p.nm_wave_dw);
+        // LDS: the histogram, the bounds, the wavefronts' histogram sums,
+        // then the wavefronts' areas
+        const size_t shm_nm = sizeof(uint32_t) * ((size_t)NBINS + 8 + (size_t)NM_WAVES * p.nm_wave_dw);
         if (a.dtype == GR_BF16) k_expand_nm<true><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
         else k_expand_nm<false><<<p.nm_wgs, EXP_THREADS, shm_nm, s>>>(p);
         p.nm_wgs = 0;   // k_expand: row-major workgroups only (n_nm still names the pass's rows)

@@ -88,11 +88,12 @@ inline TailShape tail_shape(int32_t B, int32_t M_in, int32_t V) {
 // Per request, NCUT counters of survivors already counted in the histogram
 // at or below cutoff bins cut_bin(j), j < NCUT_USED (the node-major pass
 // drops candidates past the first cutoff that already holds k survivors).
-// The cutoffs grow by about sqrt(2): 15, 22, 31, 45, 63, 91, ..., 735, 1023.
-constexpr int NCUT = 16;
-constexpr int NCUT_USED = 13;
+// The cutoffs grow by about 2^(1/4): 15, 18, 21, 26, 31, 37, ..., 863, 1023
+// (16 * 2^(j/4) with the quarter steps rounded to 76/64, 91/64, 108/64).
+constexpr int NCUT = 32;
+constexpr int NCUT_USED = 25;
 __host__ __device__ constexpr int cut_bin(int j) {
-    return ((j & 1) ? (23 << (j >> 1)) : (16 << (j >> 1))) - 1;
+    return ((16 << (j >> 2)) * ((j & 3) == 0 ? 64 : (j & 3) == 1 ? 76 : (j & 3) == 2 ? 91 : 108)) / 64 - 1;
 }
 struct TailWsLayout {
     size_t hist, segback, cut, inv, segcnt, skey, schild, sbin, total;
