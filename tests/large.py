@@ -16,13 +16,15 @@ from synth import workload as W
 
 def progress(msg: str) -> None:
     """A progress line on stdout and, since test output is captured, also
-    appended to gpurun_out/test_progress.log at the repository root (a long
-    test then shows that it is alive)."""
+    appended to the file that GR_PROGRESS_LOG names, when it is set (a long
+    test then shows that it is alive while pytest holds its output)."""
     print(msg, flush=True)
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.environ.get("GR_PROGRESS_LOG")
+    if not path:
+        return
     try:
-        os.makedirs(os.path.join(root, "gpurun_out"), exist_ok=True)
-        with open(os.path.join(root, "gpurun_out", "test_progress.log"), "a") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
             f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
     except OSError:
         pass
